@@ -1,0 +1,220 @@
+"""CPU fp64 oracle for the few-row quantized verify GEMM.
+
+TEST INFRASTRUCTURE.  Only the tests, the package's smoke check and the benchmark's
+CPU-baseline leg may import or run this module.  The HIP library never calls it, and
+the two share no code: no kernels, helpers, tables or pre/post-processing.
+
+What the method computes.  Speculative decoding checks a block of M drafted rows in
+one pass; the verify kernel decodes each packed weight once and multiplies it
+against every drafted row ("Ishizuki" README, "Kernels written for the verify";
+"dflash-mlx-bonsai2" README, "Why").  Up to summation order the result is the plain
+product  y[m, n] = sum_k x[m, k] * w[n, k]  of the activations with the dequantized
+weights, so this oracle is that definition written out in float64 numpy: unpack,
+dequantize, (rotate,) multiply.  Every fp16, bf16 and fp32 input is exactly
+representable in float64, so the only rounding is numpy's fp64 summation.
+
+Formats:
+  sign1  -- one sign bit per weight, bit 0 -> -scale, bit 1 -> +scale, one fp16
+            scale per 128 consecutive weights of an output row ("Bonsai-27B-mlx-1bit"
+            model card, the paragraph on the binary weight format).
+  affine2 -- 2-bit code q in {0,1,2,3}, w = q*s + b with one fp16 scale s and one
+            fp16 bias b per 64 consecutive weights (MLX's grouped affine format,
+            which stores a scale and a bias per group: same model card, MLX paragraph;
+            "Ishizuki" README, MLX affine codes).
+  had2   -- the 2-bit affine format applied to activations first multiplied by a
+            block-diagonal normalized Sylvester Hadamard matrix with block 128
+            ("dflash-mlx-bonsai2" README, "What this fork adds": Hadamard-rotated 2-bit
+            pack, verify prep with a fused Hadamard; "Ishizuki" README: the rotation
+            is declared by the pack).
+
+Readings taken where the pages are silent:
+  * bit order: LSB-first within little-endian uint32 words.  Weight k of a 1-bit row
+    is bit k%32 of word k//32; code k of a 2-bit row sits at bits 2*(k%16)..+1 of
+    word k//16.  Groups start at k = 0.
+  * scales and biases are separate fp16 arrays of shape [N, K/G], row-major.
+  * the output is fp32 [M, N] on the GPU; the oracle returns fp64.
+  * the Hadamard step is x' = x @ H_bd with H_bd block-diagonal, each block
+    H_128 / sqrt(128) built by the Sylvester recursion; no random sign diagonal.
+  * argmax ties go to the lowest column index.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+N_CHUNK = 16384  # output columns dequantized at a time (bounds the dense fp64 block)
+
+
+# ----------------------------------------------------------------------------- decoding
+def decode_f16(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns -> float64 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 (exact): bf16 is the upper half of an fp32."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u32.view(np.float32).astype(np.float64)
+
+
+def activations(x: np.ndarray, x_dtype: str) -> np.ndarray:
+    """Raw activation rows (uint16 bits for f16/bf16, float32 for f32) -> float64."""
+    if x_dtype == "f16":
+        return decode_f16(x)
+    if x_dtype == "bf16":
+        return decode_bf16(x)
+    if x_dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown activation dtype {x_dtype!r}")
+
+
+# ----------------------------------------------------------------------------- unpacking
+def unpack_sign1(words: np.ndarray, K: int) -> np.ndarray:
+    """uint32 [N, K/32] -> bits uint8 [N, K]; bit k is (word[k // 32] >> (k % 32)) & 1."""
+    w = np.asarray(words, dtype=np.uint32)
+    k = np.arange(K)
+    return ((w[:, k // 32] >> (k % 32).astype(np.uint32)) & 1).astype(np.uint8)
+
+
+def unpack_affine2(words: np.ndarray, K: int) -> np.ndarray:
+    """uint32 [N, K/16] -> codes uint8 [N, K]; code k is (word[k // 16] >> 2*(k % 16)) & 3."""
+    w = np.asarray(words, dtype=np.uint32)
+    k = np.arange(K)
+    return ((w[:, k // 16] >> (2 * (k % 16)).astype(np.uint32)) & 3).astype(np.uint8)
+
+
+def pack_sign1(bits: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_sign1 (used to build hand-made cases and round-trip checks)."""
+    b = np.asarray(bits, dtype=np.uint64)
+    N, K = b.shape
+    out = np.zeros((N, K // 32), dtype=np.uint64)
+    for j in range(32):
+        out |= b[:, j::32] << np.uint64(j)
+    return out.astype(np.uint32)
+
+
+def pack_affine2(codes: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_affine2."""
+    q = np.asarray(codes, dtype=np.uint64)
+    N, K = q.shape
+    out = np.zeros((N, K // 16), dtype=np.uint64)
+    for j in range(16):
+        out |= (q[:, j::16] & np.uint64(3)) << np.uint64(2 * j)
+    return out.astype(np.uint32)
+
+
+# ----------------------------------------------------------------------------- dequant
+def dequant_sign1(bits: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """w[n, k] = +s[n, k // 128] if bit else -s[n, k // 128]   (fp64)."""
+    s = decode_f16(scales)
+    K = bits.shape[1]
+    s_full = s[:, np.arange(K) // 128]
+    return np.where(bits.astype(bool), s_full, -s_full)
+
+
+def dequant_affine2(codes: np.ndarray, scales: np.ndarray, biases: np.ndarray) -> np.ndarray:
+    """w[n, k] = q[n, k] * s[n, k // 64] + b[n, k // 64]   (fp64, exact for fp16 s, b)."""
+    K = codes.shape[1]
+    g = np.arange(K) // 64
+    return codes.astype(np.float64) * decode_f16(scales)[:, g] + decode_f16(biases)[:, g]
+
+
+# ----------------------------------------------------------------------------- Hadamard
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """H_1 = [1],  H_2m = [[H_m, H_m], [H_m, -H_m]]  (integer matrix, n a power of two)."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("Hadamard order must be a power of two")
+    H = np.ones((1, 1), dtype=np.int64)
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def hadamard_rotate(x64: np.ndarray, block: int = 128) -> np.ndarray:
+    """x' = x @ blockdiag(H_block / sqrt(block)), applied to each aligned block of K."""
+    M, K = x64.shape
+    if K % block:
+        raise ValueError("K must be a multiple of the Hadamard block")
+    Hn = sylvester_hadamard(block).astype(np.float64) / np.sqrt(float(block))
+    return (x64.reshape(M, K // block, block) @ Hn).reshape(M, K)
+
+
+# ----------------------------------------------------------------------------- verify GEMMs
+def _matmul_chunked(x64: np.ndarray, N: int, dense_rows) -> np.ndarray:
+    y = np.empty((x64.shape[0], N), dtype=np.float64)
+    for n0 in range(0, N, N_CHUNK):
+        n1 = min(N, n0 + N_CHUNK)
+        y[:, n0:n1] = x64 @ dense_rows(n0, n1).T
+    return y
+
+
+def verify_sign1(x: np.ndarray, x_dtype: str, words: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """y[M, N] = x[M, K] @ W^T with W the dequantized 1-bit sign weights (fp64)."""
+    x64 = activations(x, x_dtype)
+    K = x64.shape[1]
+    return _matmul_chunked(x64, words.shape[0],
+                           lambda a, b: dequant_sign1(unpack_sign1(words[a:b], K), scales[a:b]))
+
+
+def verify_affine2(x: np.ndarray, x_dtype: str, words: np.ndarray, scales: np.ndarray,
+                   biases: np.ndarray) -> np.ndarray:
+    """y[M, N] = x[M, K] @ W^T with W the dequantized 2-bit affine weights (fp64)."""
+    x64 = activations(x, x_dtype)
+    K = x64.shape[1]
+    return _matmul_chunked(x64, words.shape[0],
+                           lambda a, b: dequant_affine2(unpack_affine2(words[a:b], K),
+                                                        scales[a:b], biases[a:b]))
+
+
+def verify_had2(x: np.ndarray, x_dtype: str, words: np.ndarray, scales: np.ndarray,
+                biases: np.ndarray, block: int = 128) -> np.ndarray:
+    """Unfused reference: rotate the activations, then the 2-bit affine product."""
+    x64 = hadamard_rotate(activations(x, x_dtype), block)
+    K = x64.shape[1]
+    return _matmul_chunked(x64, words.shape[0],
+                           lambda a, b: dequant_affine2(unpack_affine2(words[a:b], K),
+                                                        scales[a:b], biases[a:b]))
+
+
+def verify_columns(fmt: str, x: np.ndarray, x_dtype: str, words: np.ndarray,
+                   scales: np.ndarray, biases: np.ndarray | None, cols: np.ndarray) -> np.ndarray:
+    """The oracle restricted to a sample of output columns: y[:, cols]."""
+    cols = np.asarray(cols)
+    w = words[cols]
+    s = scales[cols]
+    b = None if biases is None else biases[cols]
+    if fmt == "sign1":
+        return verify_sign1(x, x_dtype, w, s)
+    if fmt == "affine2":
+        return verify_affine2(x, x_dtype, w, s, b)
+    if fmt == "had2":
+        return verify_had2(x, x_dtype, w, s, b)
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+def verify(fmt: str, x, x_dtype, words, scales, biases=None) -> np.ndarray:
+    if fmt == "sign1":
+        return verify_sign1(x, x_dtype, words, scales)
+    if fmt == "affine2":
+        return verify_affine2(x, x_dtype, words, scales, biases)
+    if fmt == "had2":
+        return verify_had2(x, x_dtype, words, scales, biases)
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+# ----------------------------------------------------------------------------- head + checks
+def argmax_rows(y: np.ndarray):
+    """Per-row argmax (first index on ties) and the gap between the top two values."""
+    y = np.asarray(y, dtype=np.float64)
+    idx = np.argmax(y, axis=1)
+    top2 = np.sort(y, axis=1)[:, -2:] if y.shape[1] > 1 else np.concatenate([y, y], axis=1)
+    return idx.astype(np.int64), top2[:, 1] - top2[:, 0]
+
+
+def normwise_rel_err(y_test: np.ndarray, y_ref: np.ndarray) -> float:
+    """max over rows m of  max_n |y_test - y_ref| / max_n |y_ref|."""
+    y_test = np.asarray(y_test, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    num = np.max(np.abs(y_test - y_ref), axis=1)
+    den = np.max(np.abs(y_ref), axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(num / den)) if num.size else 0.0
