@@ -1,0 +1,12 @@
+"""Few-row quantized verify GEMM for MI355X (gfx950): Python binding of libverifygemm.so.
+
+The verify GEMM multiplies M <= 8 drafted activation rows against packed 1-bit sign
+(g128) or 2-bit affine (g64) weights, optionally Hadamard-rotated, decoding each weight
+once inside the contraction.  All computation runs in the HIP library; this package
+only marshals tensors and streams.
+"""
+from .binding import (  # noqa: F401
+    DTYPES, FORMATS, VerifyGemmError, debug_unpack, force_variant, hadamard_rotate, lib,
+    plan_variant, variant_count, variant_name, verify_argmax_rows, verify_gemm,
+    verify_gemm_affine2, verify_gemm_had2, verify_gemm_sign1,
+)

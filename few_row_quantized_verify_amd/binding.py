@@ -1,0 +1,184 @@
+"""ctypes binding of libverifygemm.so (argument marshalling only).
+
+Every function takes device tensors, passes their pointers and the current HIP stream to
+the C ABI declared in include/verify_gemm.h, and raises VerifyGemmError on a non-OK
+status.  No step of the computation happens here; if the library is not built, import
+of the library fails loudly (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libverifygemm.so")
+
+VG_OK, VG_ERR_ARG, VG_ERR_SHAPE, VG_ERR_ALIGN, VG_ERR_DTYPE, VG_ERR_UNSUPPORTED, VG_ERR_HIP = range(7)
+STATUS_NAMES = ["VG_OK", "VG_ERR_ARG", "VG_ERR_SHAPE", "VG_ERR_ALIGN", "VG_ERR_DTYPE",
+                "VG_ERR_UNSUPPORTED", "VG_ERR_HIP"]
+VG_F32, VG_F16, VG_BF16 = 0, 1, 2
+FMT_SIGN1, FMT_AFFINE2, FMT_HAD2 = 0, 1, 2
+FORMATS = {"sign1": FMT_SIGN1, "affine2": FMT_AFFINE2, "had2": FMT_HAD2}
+DTYPES = {"f32": VG_F32, "f16": VG_F16, "bf16": VG_BF16}
+
+
+class VerifyGemmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{name}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGS = {
+    "verify_gemm_sign1": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P]),
+    "verify_gemm_affine2": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "verify_gemm_had2": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P]),
+    "hadamard_rotate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "verify_argmax_rows": (_I, [_P, _I, _I, _P, _P]),
+    "vg_last_error": (ctypes.c_char_p, []),
+    "vg_plan_variant": (_I, [_I, _I, _I, _I, _I]),
+    "vg_variant_name": (ctypes.c_char_p, [_I]),
+    "vg_force_variant": (_I, [_I]),
+    "vg_variant_count": (_I, []),
+    "vg_debug_unpack_sign1": (_I, [_P, _I, _I, _P, _P]),
+    "vg_debug_unpack_affine2": (_I, [_P, _I, _I, _P, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m few_row_quantized_verify_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != VG_OK:
+        raise VerifyGemmError(status, lib().vg_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _xdtype(x) -> int:
+    torch = _torch()
+    try:
+        return {torch.float32: VG_F32, torch.float16: VG_F16, torch.bfloat16: VG_BF16}[x.dtype]
+    except KeyError:
+        raise VerifyGemmError(VG_ERR_DTYPE, f"activation dtype {x.dtype} is not supported") from None
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _out(y, M, N, device):
+    torch = _torch()
+    if y is None:
+        return torch.empty((M, N), dtype=torch.float32, device=device)
+    return y
+
+
+def verify_gemm_sign1(x, wbits, scales, y=None, stream=None):
+    """y[M, N] = x[M, K] @ W^T, W 1-bit sign g128 (wbits int32 [N, K/32], scales fp16 [N, K/128])."""
+    M, K = x.shape
+    N = wbits.shape[0]
+    y = _out(y, M, N, x.device)
+    _check(lib().verify_gemm_sign1(_ptr(x), _xdtype(x), M, K, _ptr(wbits), _ptr(scales), N,
+                                   _ptr(y), _stream(stream)))
+    return y
+
+
+def verify_gemm_affine2(x, wq, scales, biases, y=None, stream=None):
+    """y[M, N] = x[M, K] @ W^T, W 2-bit affine g64 (wq int32 [N, K/16], scales/biases fp16 [N, K/64])."""
+    M, K = x.shape
+    N = wq.shape[0]
+    y = _out(y, M, N, x.device)
+    _check(lib().verify_gemm_affine2(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
+                                     _ptr(biases), N, _ptr(y), _stream(stream)))
+    return y
+
+
+def verify_gemm_had2(x, wq, scales, biases, had_block=128, y=None, stream=None):
+    """y = (x @ blockdiag(H_128/sqrt(128))) @ W^T with W 2-bit affine g64."""
+    M, K = x.shape
+    N = wq.shape[0]
+    y = _out(y, M, N, x.device)
+    _check(lib().verify_gemm_had2(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
+                                  _ptr(biases), N, had_block, _ptr(y), _stream(stream)))
+    return y
+
+
+def verify_gemm(fmt: str, x, w, scales, biases=None, y=None, stream=None):
+    if fmt == "sign1":
+        return verify_gemm_sign1(x, w, scales, y, stream)
+    if fmt == "affine2":
+        return verify_gemm_affine2(x, w, scales, biases, y, stream)
+    if fmt == "had2":
+        return verify_gemm_had2(x, w, scales, biases, 128, y, stream)
+    raise ValueError(fmt)
+
+
+def hadamard_rotate(x, block=128, out=None, stream=None):
+    torch = _torch()
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    _check(lib().hadamard_rotate(_ptr(x), _xdtype(x), M, K, block, _ptr(out), _stream(stream)))
+    return out
+
+
+def verify_argmax_rows(y, idx=None, stream=None):
+    torch = _torch()
+    M, N = y.shape
+    if idx is None:
+        idx = torch.empty((M,), dtype=torch.int32, device=y.device)
+    _check(lib().verify_argmax_rows(_ptr(y), M, N, _ptr(idx), _stream(stream)))
+    return idx
+
+
+def debug_unpack(fmt: str, w, K, codes=None, stream=None):
+    torch = _torch()
+    N = w.shape[0]
+    if codes is None:
+        codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    fn = lib().vg_debug_unpack_sign1 if fmt == "sign1" else lib().vg_debug_unpack_affine2
+    _check(fn(_ptr(w), N, K, _ptr(codes), _stream(stream)))
+    return codes
+
+
+def plan_variant(fmt: str, x_dtype: str, M: int, N: int, K: int) -> int:
+    return lib().vg_plan_variant(FORMATS[fmt], DTYPES[x_dtype], M, N, K)
+
+
+def variant_name(v: int) -> str:
+    return lib().vg_variant_name(v).decode()
+
+
+def variant_count() -> int:
+    return lib().vg_variant_count()
+
+
+def force_variant(v: int) -> None:
+    _check(lib().vg_force_variant(v))

@@ -1,0 +1,240 @@
+// vg_api.cpp -- the C ABI: argument validation, per-shape dispatch and launches.
+//
+// Every entry point validates its arguments on the host before touching the device, so an
+// invalid call enqueues nothing and returns a status with a message (a pack declaring a
+// transform that cannot be applied is refused rather than run as the plain format:
+// "Ishizuki" README; failures become errors, not crashes: "Ishizuki" release notes).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/verify_gemm.h"
+#include "vg_device.h"
+#include "vg_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+int g_forced = -1;  // forced variant (-1: dispatch)
+std::once_flag g_env_once;
+
+vg_status fail(vg_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void read_env() {
+  const char* v = std::getenv("VG_FORCE_VARIANT");
+  if (!v || !*v) return;
+  for (int i = 0; i < vg::VAR_COUNT; ++i)
+    if (std::strcmp(v, vg_variant_name(i)) == 0) g_forced = i;
+}
+
+constexpr int kMaxDevices = 64;
+vg::DeviceInfo g_dev[kMaxDevices];
+bool g_dev_ok[kMaxDevices];
+std::mutex g_dev_mu;
+
+vg_status device_info(vg::DeviceInfo* out) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices)
+    return fail(VG_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev_ok[d]) {
+    int cu = 0, lds = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess ||
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, d) != hipSuccess)
+      return fail(VG_ERR_HIP, "hipDeviceGetAttribute failed on device %d", d);
+    g_dev[d].cu_count = cu > 0 ? cu : 1;
+    g_dev[d].max_lds = lds;
+    g_dev_ok[d] = true;
+  }
+  *out = g_dev[d];
+  return VG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+vg_status check_common(const void* x, int x_dtype, int M, int K, int N) {
+  if (x_dtype != VG_F32 && x_dtype != VG_F16 && x_dtype != VG_BF16)
+    return fail(VG_ERR_DTYPE, "unknown activation dtype %d", x_dtype);
+  if (M < 1 || M > VG_MAX_ROWS) return fail(VG_ERR_SHAPE, "M=%d outside 1..%d", M, VG_MAX_ROWS);
+  if (N < 1) return fail(VG_ERR_SHAPE, "N=%d < 1", N);
+  if (K < 1) return fail(VG_ERR_SHAPE, "K=%d < 1", K);
+  if (!x) return fail(VG_ERR_ARG, "x is null");
+  if (!aligned16(x)) return fail(VG_ERR_ALIGN, "x is not 16-byte aligned");
+  return VG_OK;
+}
+
+vg_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(VG_ERR_ARG, "%s is null", name);
+  if (!aligned16(p)) return fail(VG_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return VG_OK;
+}
+
+int kstep_of(int fmt) { return fmt == vg::SIGN1 ? 512 : 256; }
+
+// Per-shape dispatch.  fp32 activations take the exact fp32 VALU kernel.  fp16/bf16 take
+// the MFMA kernels when K is a whole number of 4-group steps: mode Q up to 4 rows, mode H
+// up to 8.  Shapes the MFMA kernels cannot stage fall back to the VALU kernel.
+int plan(int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev) {
+  if (xt == VG_F32) return vg::VAR_VALU;
+  if (K % kstep_of(fmt) != 0) return vg::VAR_VALU;
+  const int var = M <= 4 ? vg::VAR_MFMA_Q : vg::VAR_MFMA_H;
+  const int tiles = (N + 15) / 16;
+  const int grid = tiles < dev.cu_count ? tiles : dev.cu_count;
+  int ws = 0;
+  vg::mfma_lds_bytes(fmt, var, M, K, N, grid, dev.max_lds, &ws);
+  return ws > 0 ? var : vg::VAR_VALU;
+}
+
+bool variant_supports(int var, int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev) {
+  if (var == vg::VAR_VALU) return true;
+  if (xt == VG_F32 || K % kstep_of(fmt) != 0) return false;
+  if (var == vg::VAR_MFMA_Q && M > 4) return false;
+  const int tiles = (N + 15) / 16;
+  const int grid = tiles < dev.cu_count ? tiles : dev.cu_count;
+  int ws = 0;
+  vg::mfma_lds_bytes(fmt, var, M, K, N, grid, dev.max_lds, &ws);
+  return ws > 0;
+}
+
+vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint32_t* w,
+                   const uint16_t* scales, const uint16_t* biases, int N, float* y, void* stream) {
+  std::call_once(g_env_once, read_env);
+  vg::DeviceInfo dev;
+  if (vg_status s = device_info(&dev)) return s;
+  int var = plan(fmt, x_dtype, M, N, K, dev);
+  if (g_forced >= 0) {
+    if (!variant_supports(g_forced, fmt, x_dtype, M, N, K, dev))
+      return fail(VG_ERR_UNSUPPORTED, "forced variant %s cannot run format %d dtype %d M=%d K=%d",
+                  vg_variant_name(g_forced), fmt, x_dtype, M, K);
+    var = g_forced;
+  }
+  vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, static_cast<hipStream_t>(stream)};
+  const hipError_t e = var == vg::VAR_VALU ? vg::launch_valu(c, dev) : vg::launch_mfma(c, var, dev);
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return VG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vg_status verify_gemm_sign1(const void* x, int x_dtype, int M, int K, const uint32_t* wbits,
+                            const uint16_t* scales, int N, float* y, void* stream) {
+  if (vg_status s = check_common(x, x_dtype, M, K, N)) return s;
+  if (K % 128 != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of 128 (1-bit group)", K);
+  if (vg_status s = check_ptr(wbits, "wbits")) return s;
+  if (vg_status s = check_ptr(scales, "scales")) return s;
+  if (vg_status s = check_ptr(y, "y")) return s;
+  return run_gemm(vg::SIGN1, x, x_dtype, M, K, wbits, scales, nullptr, N, y, stream);
+}
+
+vg_status verify_gemm_affine2(const void* x, int x_dtype, int M, int K, const uint32_t* wq,
+                              const uint16_t* scales, const uint16_t* biases, int N, float* y,
+                              void* stream) {
+  if (vg_status s = check_common(x, x_dtype, M, K, N)) return s;
+  if (K % 64 != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of 64 (2-bit group)", K);
+  if (vg_status s = check_ptr(wq, "wq")) return s;
+  if (vg_status s = check_ptr(scales, "scales")) return s;
+  if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_ptr(y, "y")) return s;
+  return run_gemm(vg::AFFINE2, x, x_dtype, M, K, wq, scales, biases, N, y, stream);
+}
+
+vg_status verify_gemm_had2(const void* x, int x_dtype, int M, int K, const uint32_t* wq,
+                           const uint16_t* scales, const uint16_t* biases, int N, int had_block,
+                           float* y, void* stream) {
+  if (had_block != 128)
+    return fail(VG_ERR_UNSUPPORTED, "Hadamard block %d is not supported (only 128)", had_block);
+  if (vg_status s = check_common(x, x_dtype, M, K, N)) return s;
+  if (K % 128 != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of the Hadamard block 128", K);
+  if (vg_status s = check_ptr(wq, "wq")) return s;
+  if (vg_status s = check_ptr(scales, "scales")) return s;
+  if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_ptr(y, "y")) return s;
+  return run_gemm(vg::HAD2, x, x_dtype, M, K, wq, scales, biases, N, y, stream);
+}
+
+vg_status hadamard_rotate(const void* x, int x_dtype, int M, int K, int block, float* x_out,
+                          void* stream) {
+  if (block != 128) return fail(VG_ERR_UNSUPPORTED, "Hadamard block %d is not supported (only 128)", block);
+  if (vg_status s = check_common(x, x_dtype, M, K, 1)) return s;
+  if (K % 128 != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of the Hadamard block 128", K);
+  if (vg_status s = check_ptr(x_out, "x_out")) return s;
+  const hipError_t e = vg::launch_hadamard(x, x_dtype, M, K, x_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return VG_OK;
+}
+
+vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* stream) {
+  if (M < 1 || M > VG_MAX_ROWS) return fail(VG_ERR_SHAPE, "M=%d outside 1..%d", M, VG_MAX_ROWS);
+  if (N < 1) return fail(VG_ERR_SHAPE, "N=%d < 1", N);
+  if (vg_status s = check_ptr(y, "y")) return s;
+  if (vg_status s = check_ptr(idx, "idx")) return s;
+  const hipError_t e = vg::launch_argmax(y, M, N, idx, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return VG_OK;
+}
+
+const char* vg_last_error(void) { return g_err; }
+
+int vg_plan_variant(int format, int x_dtype, int M, int N, int K) {
+  if (format < 0 || format > 2) return -1;
+  if (x_dtype < 0 || x_dtype > 2 || M < 1 || M > VG_MAX_ROWS || N < 1 || K < 1) return -1;
+  if (K % (format == vg::SIGN1 || format == vg::HAD2 ? 128 : 64) != 0) return -1;
+  std::call_once(g_env_once, read_env);
+  vg::DeviceInfo dev;
+  if (device_info(&dev) != VG_OK) return -1;
+  if (g_forced >= 0) return variant_supports(g_forced, format, x_dtype, M, N, K, dev) ? g_forced : -1;
+  return plan(format, x_dtype, M, N, K, dev);
+}
+
+const char* vg_variant_name(int variant) {
+  switch (variant) {
+    case vg::VAR_MFMA_Q: return "vg_mfma_q";
+    case vg::VAR_MFMA_H: return "vg_mfma_h";
+    case vg::VAR_VALU: return "vg_valu";
+    default: return "";
+  }
+}
+
+vg_status vg_force_variant(int variant) {
+  std::call_once(g_env_once, read_env);
+  if (variant < -1 || variant >= vg::VAR_COUNT) return fail(VG_ERR_ARG, "unknown variant %d", variant);
+  g_forced = variant;
+  return VG_OK;
+}
+
+int vg_variant_count(void) { return vg::VAR_COUNT; }
+
+vg_status vg_debug_unpack_sign1(const uint32_t* wbits, int N, int K, uint8_t* codes, void* stream) {
+  if (N < 1 || K < 32 || K % 32 != 0) return fail(VG_ERR_SHAPE, "bad shape N=%d K=%d", N, K);
+  if (vg_status s = check_ptr(wbits, "wbits")) return s;
+  if (!codes) return fail(VG_ERR_ARG, "codes is null");
+  const hipError_t e = vg::launch_debug_unpack(vg::SIGN1, wbits, N, K, codes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return VG_OK;
+}
+
+vg_status vg_debug_unpack_affine2(const uint32_t* wq, int N, int K, uint8_t* codes, void* stream) {
+  if (N < 1 || K < 16 || K % 16 != 0) return fail(VG_ERR_SHAPE, "bad shape N=%d K=%d", N, K);
+  if (vg_status s = check_ptr(wq, "wq")) return s;
+  if (!codes) return fail(VG_ERR_ARG, "codes is null");
+  const hipError_t e = vg::launch_debug_unpack(vg::AFFINE2, wq, N, K, codes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return VG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,232 @@
+// vg_aux.hip -- the VALU verify kernel (fp32 activations, any row count), the standalone
+// block-Hadamard rotation, the output-head argmax and the code-decoding debug kernel.
+#include "vg_device.h"
+#include "vg_launch.h"
+
+namespace vg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int VALU_THREADS = 256;
+constexpr int VALU_WK = 2048;   // K per LDS window (fp32 activations, 8 rows: 64 KB)
+constexpr int MAXM = 8;
+
+__device__ __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+__device__ __forceinline__ float x_at(const void* x, int xt, size_t idx) {
+  if (xt == 0) return static_cast<const float*>(x)[idx];
+  const uint32_t h = static_cast<const uint16_t*>(x)[idx];
+  return xt == 2 ? __uint_as_float(h << 16) : h2f(h);
+}
+
+struct ValuArgs {
+  const void* x;
+  int xt;
+  const uint32_t* w;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  float* y;
+  int M, K, N;
+};
+
+// In-place unnormalized Walsh-Hadamard transform of 128-blocks of an LDS buffer
+// [MAXM][len] (len a multiple of 128), butterfly stage by stage.
+__device__ void lds_fwht(float* xs, int M, int len) {
+  const int pairs = M * len / 2;
+  for (int h = 1; h < 128; h <<= 1) {
+    for (int p = threadIdx.x; p < pairs; p += blockDim.x) {
+      const int m = p / (len / 2), q = p - m * (len / 2);
+      const int blk = q / 64, r = q - blk * 64;              // 64 butterflies per block
+      const int lo = (r / h) * (2 * h) + (r % h);
+      float* b = xs + m * len + blk * 128;
+      const float a0 = b[lo], a1 = b[lo + h];
+      b[lo] = a0 + a1;
+      b[lo + h] = a0 - a1;
+    }
+    __syncthreads();
+  }
+}
+
+// One thread per output row; exact fp32 dequantization, fp32 fused multiply-adds.
+template <int FMT>
+__global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
+  __shared__ float xs[MAXM * VALU_WK];
+  const int n = blockIdx.x * VALU_THREADS + threadIdx.x;
+  const bool live = n < A.N;
+  constexpr int G = FMT == SIGN1 ? 128 : 64;
+  float acc[MAXM];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
+  for (int k0 = 0; k0 < A.K; k0 += VALU_WK) {
+    const int len = min(VALU_WK, A.K - k0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < A.M * len; e += VALU_THREADS) {
+      const int m = e / len, k = e - m * len;
+      xs[m * len + k] = x_at(A.x, A.xt, (size_t)m * A.K + k0 + k);
+    }
+    __syncthreads();
+    if constexpr (FMT == HAD2) {
+      lds_fwht(xs, A.M, len);
+      for (int e = threadIdx.x; e < A.M * len; e += VALU_THREADS) xs[e] *= 0.08838834764831845f;
+      __syncthreads();
+    }
+    if (live) {
+      if constexpr (FMT == SIGN1) {
+        for (int wi = 0; wi < len / 32; ++wi) {
+          const int k = k0 + 32 * wi;
+          const uint32_t word = A.w[(size_t)n * (A.K / 32) + k / 32];
+          const float s = h2f(A.scales[(size_t)n * (A.K / G) + k / G]);
+          for (int bit = 0; bit < 32; ++bit) {
+            const float wv = ((word >> bit) & 1u) ? s : -s;
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m)
+              if (m < A.M) acc[m] = __builtin_fmaf(xs[m * len + 32 * wi + bit], wv, acc[m]);
+          }
+        }
+      } else {
+        for (int wi = 0; wi < len / 16; ++wi) {
+          const int k = k0 + 16 * wi;
+          const uint32_t word = A.w[(size_t)n * (A.K / 16) + k / 16];
+          const size_t gi = (size_t)n * (A.K / G) + k / G;
+          const float s = h2f(A.scales[gi]), b = h2f(A.biases[gi]);
+          for (int c = 0; c < 16; ++c) {
+            const float wv = (float)((word >> (2 * c)) & 3u) * s + b;   // exact in fp32
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m)
+              if (m < A.M) acc[m] = __builtin_fmaf(xs[m * len + 16 * wi + c], wv, acc[m]);
+          }
+        }
+      }
+    }
+  }
+  if (live)
+    for (int m = 0; m < A.M; ++m) A.y[(size_t)m * A.N + n] = acc[m];
+}
+
+hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev) {
+  (void)dev;
+  ValuArgs A{c.x, c.xt, c.w, c.scales, c.biases, c.y, c.M, c.K, c.N};
+  const dim3 grid((c.N + VALU_THREADS - 1) / VALU_THREADS);
+  switch (c.fmt) {
+    case SIGN1: hipLaunchKernelGGL(vg_valu<SIGN1>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
+    case AFFINE2: hipLaunchKernelGGL(vg_valu<AFFINE2>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
+    case HAD2: hipLaunchKernelGGL(vg_valu<HAD2>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Standalone rotation: x_out = x * blockdiag(H_128 / sqrt(128)), one quad of lanes per
+// (row, block), each lane 32 consecutive elements; same butterfly scheme as the fused
+// GEMM prologue.
+template <int CTRL>
+__device__ __forceinline__ float dpp_quad_aux(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__global__ __launch_bounds__(256) void vg_hadamard_kernel(const void* x, int xt, int M, int K, float* out) {
+  const int gt = blockIdx.x * 256 + threadIdx.x;
+  const int nquads = M * (K / 128);
+  const int quad = gt >> 2, ql = gt & 3;
+  if (quad >= nquads) return;          // whole quads leave together (4 | 256)
+  const int m = quad / (K / 128), blk = quad - m * (K / 128);
+  const size_t base = (size_t)m * K + blk * 128 + ql * 32;
+  float v[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[e] = x_at(x, xt, base + e);
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if ((e & h) == 0) { const float a = v[e], b = v[e + h]; v[e] = a + b; v[e + h] = a - b; }
+  const float c1 = (ql & 1) ? -1.0f : 1.0f, c2 = (ql & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c1, dpp_quad_aux<0xB1>(v[e]), v[e]);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c2, dpp_quad_aux<0x4E>(v[e]), v[e]);
+  const float sg = (((ql & 1) ^ ((ql >> 1) & 1)) != 0) ? -1.0f : 1.0f;
+  const float sc = sg * 0.08838834764831845f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) out[base + e] = v[e] * sc;
+}
+
+hipError_t launch_hadamard(const void* x, int xt, int M, int K, float* out, hipStream_t s) {
+  const int threads = 4 * M * (K / 128);
+  hipLaunchKernelGGL(vg_hadamard_kernel, dim3((threads + 255) / 256), dim3(256), 0, s, x, xt, M, K, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Per-row argmax of fp32 logits, lowest index on ties, NaN never selected (a row of only
+// NaN gives index 0).  One workgroup per row.
+__global__ __launch_bounds__(1024) void vg_argmax_kernel(const float* y, int N, int32_t* idx) {
+  __shared__ float sv[1024];
+  __shared__ int si[1024];
+  const int m = blockIdx.x;
+  const float* row = y + (size_t)m * N;
+  float best = -INFINITY;
+  int bi = -1;
+  for (int n = threadIdx.x; n < N; n += 1024) {
+    const float v = row[n];
+    if (v > best || (bi < 0 && v == v)) { best = v; bi = n; }
+  }
+  sv[threadIdx.x] = best;
+  si[threadIdx.x] = bi;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (threadIdx.x < off) {
+      const float v2 = sv[threadIdx.x + off];
+      const int i2 = si[threadIdx.x + off];
+      const int i1 = si[threadIdx.x];
+      const bool take = i2 >= 0 && (i1 < 0 || v2 > sv[threadIdx.x] || (v2 == sv[threadIdx.x] && i2 < i1));
+      if (take) { sv[threadIdx.x] = v2; si[threadIdx.x] = i2; }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) idx[m] = si[0] < 0 ? 0 : si[0];
+}
+
+hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, hipStream_t s) {
+  hipLaunchKernelGGL(vg_argmax_kernel, dim3(M), dim3(1024), 0, s, y, N, idx);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode codes through the GEMM's register extraction: a register half holds
+// BETA + DELTA * code, so code = (half - BETA) / DELTA exactly.
+__global__ __launch_bounds__(256) void vg_debug_unpack_kernel(int fmt, const uint32_t* w, int N, int K, uint8_t* codes) {
+  const size_t wpr = fmt == SIGN1 ? K / 32 : K / 16;
+  const size_t gw = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (gw >= (size_t)N * wpr) return;
+  const size_t n = gw / wpr, wi = gw - n * wpr;
+  const uint32_t word = w[gw];
+  uint8_t* out = codes + n * (size_t)K;
+  if (fmt == SIGN1) {
+    uint32_t pr[16];
+    unpack_sign1_word(word, pr);
+#pragma unroll
+    for (int b0 = 0; b0 < 16; ++b0) {
+      const float beta = sign1_beta(b0);
+      out[32 * wi + b0] = (uint8_t)((h2f(pr[b0] & 0xFFFFu) - beta) / SIGN1_DELTA);
+      out[32 * wi + b0 + 16] = (uint8_t)((h2f(pr[b0] >> 16) - beta) / SIGN1_DELTA);
+    }
+  } else {
+    uint32_t pr[8];
+    unpack_affine2_word(word, pr);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float beta = affine2_beta(j);
+      out[16 * wi + j] = (uint8_t)((h2f(pr[j] & 0xFFFFu) - beta) / AFFINE2_DELTA);
+      out[16 * wi + j + 8] = (uint8_t)((h2f(pr[j] >> 16) - beta) / AFFINE2_DELTA);
+    }
+  }
+}
+
+hipError_t launch_debug_unpack(int fmt, const uint32_t* w, int N, int K, uint8_t* codes, hipStream_t s) {
+  const size_t words = (size_t)N * (fmt == SIGN1 ? K / 32 : K / 16);
+  hipLaunchKernelGGL(vg_debug_unpack_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
+                     fmt, w, N, K, codes);
+  return hipGetLastError();
+}
+
+}  // namespace vg

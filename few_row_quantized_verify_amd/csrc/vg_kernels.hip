@@ -1,0 +1,581 @@
+// vg_kernels.hip -- few-row quantized verify GEMM kernels for MI355X (gfx950).
+//
+// y[M, N] = x[M, K] * W^T for M <= 8 drafted rows and packed 1-bit sign (g128) or 2-bit
+// affine (g64) weights, optionally after a block-128 Hadamard rotation of x.  Each packed
+// weight is read from HBM once and decoded once, straight into MFMA operand registers,
+// and multiplied against every drafted row ("Ishizuki" README, "Kernels written for the
+// verify"; "dflash-mlx-bonsai2" README, "What this fork adds").
+//
+// Work decomposition (MFMA variants)
+//   * One workgroup (8 waves) per CU owns a contiguous, balanced range of output rows;
+//     rows are grouped in tiles of 16 (the MFMA N dimension).  A "unit" is one tile times
+//     one K-step of 4 quantization groups; a wave loads one 16-byte group per lane per
+//     unit (16 rows x 64 bytes), i.e. 1 KB of packed codes per wave instruction.
+//   * K is processed in windows.  Per window the workgroup stages its activations into
+//     LDS once, already in the operand layout the unpacked codes need (and rotated, for
+//     the Hadamard format), together with per-(group, row) correction sums.  The
+//     window's units are split evenly across the 8 waves in tile-major order; partial
+//     tiles are reduced through LDS in a fixed order, so results are deterministic.
+//   * MFMA rows: the 16 A rows are split into independent row-blocks, each fed only by
+//     one lane-group's K slots.  Mode Q: 4 blocks of 4 rows (M <= 4), each lane-group
+//     decodes its own quantization group.  Mode H: 2 blocks of 8 rows (M <= 8), lane-group
+//     pairs share a group after one permlane16 swap of two words.  Every accumulator
+//     register therefore holds one quantization group's dot products, and the per-group
+//     scale (and bias) is applied once per group in fp32.
+#include "vg_device.h"
+#include "vg_launch.h"
+
+namespace vg {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum XType : int { XF32 = 0, XF16 = 1, XBF16 = 2 };
+
+constexpr int NW = 8;               // waves per workgroup
+constexpr int NTHREADS = NW * 64;
+constexpr int PREF = 4;             // units in flight per wave
+constexpr int MAXM = 8;
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<SIGN1> {
+  static constexpr int G = 128, WORD_K = 32, PAIRS = 16, NQ = 4;
+  static constexpr int WB = 64;           // LDS bytes of one word's operand window
+  static constexpr int GS = 4 * WB + 16;  // LDS bytes per group (+16 pad vs bank conflicts)
+  static constexpr bool AFFINE = false;
+};
+template <> struct Fmt<AFFINE2> {
+  static constexpr int G = 64, WORD_K = 16, PAIRS = 8, NQ = 2;
+  static constexpr int WB = 32;
+  static constexpr int GS = 4 * WB + 16;
+  static constexpr bool AFFINE = true;
+};
+template <> struct Fmt<HAD2> : Fmt<AFFINE2> {};
+
+__host__ __device__ constexpr int fmt_group(int fmt) { return fmt == SIGN1 ? 128 : 64; }
+__host__ __device__ constexpr int fmt_gs(int fmt) { return fmt == SIGN1 ? 4 * 64 + 16 : 4 * 32 + 16; }
+__host__ __device__ constexpr int fmt_word_k(int fmt) { return fmt == SIGN1 ? 32 : 16; }
+
+struct MfmaArgs {
+  const void* x;
+  const uint32_t* w;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  float* y;
+  int M, K, N;
+  int win_steps;   // K-steps (of 4 groups) per staging window
+  int tiles_max;   // ytile capacity
+  int a_pitch;     // LDS bytes per activation row in a window
+};
+
+// LDS carve-up (byte offsets), computed identically on host and device.
+struct LdsLayout {
+  int a_off, e_off, x_off, ytile_off, slot_off, row_off, total;
+  __host__ __device__ LdsLayout(int fmt, int M, int win_steps, int tiles_max) {
+    const int groups = win_steps * 4;
+    const int pitch = groups * fmt_gs(fmt) + 16;
+    a_off = 0;
+    e_off = a_off + M * pitch;
+    x_off = e_off + groups * MAXM * 4;
+    ytile_off = x_off + (fmt == SIGN1 ? 0 : groups * MAXM * 4);
+    slot_off = ytile_off + tiles_max * MAXM * 16 * 4;
+    row_off = slot_off + NW * 2 * MAXM * 16 * 4;
+    total = row_off + 2 * MAXM * 4;
+  }
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float v) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);  // round to nearest even
+}
+// CTRL 0xB1: quad_perm [1,0,3,2] (partner lane ^1); 0x4E: quad_perm [2,3,0,1] (lane ^2).
+template <int CTRL>
+__device__ __forceinline__ float dpp_quad(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+
+// Fast Walsh-Hadamard transform of a 128-block held by 4 consecutive lanes (a quad), 32
+// fp32 values per lane, lane l holding block elements 32l .. 32l+31.  Five butterfly
+// stages run inside each lane's registers, two across the quad.  The cross-lane stages
+// use one fused multiply-add each and leave the upper results negated; the known final
+// sign of each lane is returned so the caller can fold it into its scale.  Unnormalized:
+// out[k] = sign * sum_j (-1)^popcount(k & j) in[j].
+__device__ __forceinline__ float fwht128_quad(float v[32], int quad_lane) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      if ((e & h) == 0) {
+        const float a = v[e], b = v[e + h];
+        v[e] = a + b;
+        v[e + h] = a - b;
+      }
+    }
+  }
+  const float c1 = (quad_lane & 1) ? -1.0f : 1.0f;
+  const float c2 = (quad_lane & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c1, dpp_quad<0xB1>(v[e]), v[e]);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c2, dpp_quad<0x4E>(v[e]), v[e]);
+  return (((quad_lane & 1) ^ ((quad_lane >> 1) & 1)) != 0) ? -1.0f : 1.0f;
+}
+
+// Loads 32 consecutive activations of row m starting at k0 as fp32 (XT: F16 or BF16).
+template <int XT>
+__device__ __forceinline__ void load_x32_f32(const void* x, int K, int m, int k0, float v[32]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + (size_t)m * K + k0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 d = p[q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = d[i] & 0xFFFFu, hi = d[i] >> 16;
+      v[8 * q + 2 * i] = XT == XBF16 ? bf16_to_f32(lo) : f16_to_f32(lo);
+      v[8 * q + 2 * i + 1] = XT == XBF16 ? bf16_to_f32(hi) : f16_to_f32(hi);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Activation staging for one window: x[m, k0 .. k0 + WK) -> LDS operand layout + sums.
+//
+// Operand layout: for each row m, group gr and word w of the group, the word's window of
+// WORD_K activations is stored as PAIRS dwords, dword j = (x[k_j], x[k_j + WORD_K/2]) in
+// fp16, k_j = j-th K index of the window, i.e. exactly the pairing of unpacked code
+// registers (bits p and p+16).  An MFMA operand of 4 consecutive registers therefore maps
+// to 16 contiguous bytes.
+// Sums per (group, row), fp32, computed from the same fp16 operand values:
+//   1-bit:  E = sum_k a_k * (BETA_k + 1)          (stored negated)
+//   2-bit:  R = sum_k a_k * BETA_k (stored negated),  X = sum_k a_k
+// The activations a are x * f (f a per-row power of two chosen so the fp16 values cannot
+// overflow; f = 1 for fp16 input without rotation), rotated first for the Hadamard format.
+template <int FMT, int XT>
+__device__ void stage_window(const MfmaArgs& A, char* smem, const LdsLayout& L, int k0, int WK) {
+  using F = Fmt<FMT>;
+  constexpr bool HAD = FMT == HAD2;
+  constexpr bool NORM = HAD || XT == XBF16;
+  const int tid = threadIdx.x;
+  const int M = A.M;
+  const int nchunks = WK / 32;
+  const int ntask = M * nchunks;
+  const int pitch = A.a_pitch;
+  float* rowf = reinterpret_cast<float*>(smem + L.row_off);  // [0..7] f, [8..15] 1/f
+  uint32_t* rowmax = reinterpret_cast<uint32_t*>(smem + L.row_off);
+
+  if constexpr (NORM) {
+    if (tid < MAXM) rowmax[tid] = 0u;
+    __syncthreads();
+    for (int t = tid; t < ntask; t += NTHREADS) {
+      const int m = t / nchunks, c = t - m * nchunks;
+      float v[32];
+      load_x32_f32<XT>(A.x, A.K, m, k0 + 32 * c, v);
+      float mx = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(v[e]));
+      atomicMax(&rowmax[m], __float_as_uint(mx));
+    }
+    __syncthreads();
+    if (tid < MAXM) {
+      const float mx = __uint_as_float(rowmax[tid]);
+      int ex = 0;
+      float f = 1.0f;
+      if (mx > 0.0f && mx == mx) {
+        frexpf(mx, &ex);                      // mx < 2^ex
+        int e = 14 - ex - (HAD ? 4 : 0);      // rotated values are below sqrt(128) * max < 16 * max
+        e = e < -120 ? -120 : (e > 120 ? 120 : e);
+        f = ldexpf(1.0f, e);
+      }
+      rowf[tid] = f;
+      rowf[MAXM + tid] = 1.0f / f;
+    }
+    __syncthreads();
+  }
+
+  for (int t = tid; t < ntask; t += NTHREADS) {
+    const int m = t / nchunks, c = t - m * nchunks;
+    uint32_t hv[32];  // fp16 bits, natural K order within the chunk
+    if constexpr (!NORM) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.x) + (size_t)m * A.K + k0 + 32 * c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 d = p[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hv[8 * q + 2 * i] = d[i] & 0xFFFFu;
+          hv[8 * q + 2 * i + 1] = d[i] >> 16;
+        }
+      }
+    } else {
+      float v[32];
+      load_x32_f32<XT>(A.x, A.K, m, k0 + 32 * c, v);
+      float scale = rowf[m];
+      if constexpr (HAD) scale *= fwht128_quad(v, c & 3) * 0.08838834764831845f;  // 1/sqrt(128)
+#pragma unroll
+      for (int e = 0; e < 32; ++e) hv[e] = f32_to_f16_bits(v[e] * scale);
+    }
+
+    // pair dwords, sums, LDS writes
+    char* arow = smem + L.a_off + m * pitch;
+    if constexpr (FMT == SIGN1) {
+      // chunk = one word window (32 K) = word (c % 4) of group (c / 4)
+      uint32_t pd[16];
+      float e = 0.0f;
+#pragma unroll
+      for (int b0 = 0; b0 < 16; ++b0) {
+        pd[b0] = hv[b0] | (hv[b0 + 16] << 16);
+        const _Float16 cf = (_Float16)(sign1_beta(b0) + 1.0f);
+        e = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pd[b0]), f16x2{cf, cf}, e, false);
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(arow + (c >> 2) * F::GS + (c & 3) * F::WB);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = u32x4{pd[4 * q], pd[4 * q + 1], pd[4 * q + 2], pd[4 * q + 3]};
+      e += __shfl_xor(e, 1);
+      e += __shfl_xor(e, 2);
+      if ((c & 3) == 0) reinterpret_cast<float*>(smem + L.e_off)[(c >> 2) * MAXM + m] = -e;
+    } else {
+      // chunk = two word windows (16 K each) = words 2(c%2), 2(c%2)+1 of group c/2
+      float r = 0.0f, xs = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < 2; ++ww) {
+        uint32_t pd[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pd[j] = hv[16 * ww + j] | (hv[16 * ww + j + 8] << 16);
+          const _Float16 bj = (_Float16)affine2_beta(j);
+          const f16x2 ph = __builtin_bit_cast(f16x2, pd[j]);
+          r = __builtin_amdgcn_fdot2(ph, f16x2{bj, bj}, r, false);
+          xs = __builtin_amdgcn_fdot2(ph, f16x2{(_Float16)1.0f, (_Float16)1.0f}, xs, false);
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(arow + (c >> 1) * F::GS + (2 * (c & 1) + ww) * F::WB);
+        dst[0] = u32x4{pd[0], pd[1], pd[2], pd[3]};
+        dst[1] = u32x4{pd[4], pd[5], pd[6], pd[7]};
+      }
+      r += __shfl_xor(r, 1);
+      xs += __shfl_xor(xs, 1);
+      if ((c & 1) == 0) {
+        reinterpret_cast<float*>(smem + L.e_off)[(c >> 1) * MAXM + m] = -r;
+        reinterpret_cast<float*>(smem + L.x_off)[(c >> 1) * MAXM + m] = xs;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+struct Unit {
+  u32x4 w;          // one quantization group (16 bytes) of this lane's row
+  uint32_t sb[2];   // fp16 scale | fp16 bias << 16, for the lane's group(s)
+};
+
+template <int FMT, int MODE>
+__device__ __forceinline__ void load_unit(const MfmaArgs& A, int r0, int r1, int ws0, int ns,
+                                          int u, int g, int i, Unit& U) {
+  constexpr int WORD_K = Fmt<FMT>::WORD_K, G = Fmt<FMT>::G;
+  const int t = u / ns, s = ws0 + (u - t * ns);
+  const int row = r0 + 16 * t + i;
+  if (row < r1) {
+    const size_t wpr = (size_t)A.K / WORD_K, gpr = (size_t)A.K / G;
+    U.w = *reinterpret_cast<const u32x4*>(A.w + row * wpr + (size_t)s * 16 + g * 4);
+    const size_t sbase = row * gpr + (size_t)s * 4;
+    if constexpr (MODE == VAR_MFMA_Q) {
+      const size_t gi = sbase + g;
+      U.sb[0] = A.scales[gi] | (Fmt<FMT>::AFFINE ? (uint32_t)A.biases[gi] << 16 : 0u);
+    } else {
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const size_t gi = sbase + 2 * (g >> 1) + uu;
+        U.sb[uu] = A.scales[gi] | (Fmt<FMT>::AFFINE ? (uint32_t)A.biases[gi] << 16 : 0u);
+      }
+    }
+  }
+}
+
+// One unit: decode the lane's codes and accumulate every drafted row's group sums.
+template <int FMT, int MODE>
+__device__ __forceinline__ void compute_unit(const Unit& U, const char* smem, const LdsLayout& L,
+                                             int pitch, int sl, int g, int i, int M, float yacc[4]) {
+  using F = Fmt<FMT>;
+  const float* E = reinterpret_cast<const float*>(smem + L.e_off);
+  const float* X = reinterpret_cast<const float*>(smem + L.x_off);
+  if constexpr (MODE == VAR_MFMA_Q) {
+    const int m = i - 4 * g;
+    const bool av = m >= 0 && m < M && m < 4;
+    const int gl = sl * 4 + g;
+    const char* abase = smem + L.a_off + (av ? m : 0) * pitch + gl * F::GS;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(E + gl * MAXM);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t pr[F::PAIRS];
+      if constexpr (FMT == SIGN1) unpack_sign1_word(U.w[w], pr); else unpack_affine2_word(U.w[w], pr);
+#pragma unroll
+      for (int q = 0; q < F::NQ; ++q) {
+        const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pr[4 * q], pr[4 * q + 1], pr[4 * q + 2], pr[4 * q + 3]});
+        f16x8 a = {};
+        if (av) a = *reinterpret_cast<const f16x8*>(abase + w * F::WB + 16 * q);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+      }
+    }
+    const float s = f16_to_f32(U.sb[0] & 0xFFFFu);
+    if constexpr (F::AFFINE) {
+      const float bb = f16_to_f32(U.sb[0] >> 16);
+      const f32x4 xs = *reinterpret_cast<const f32x4*>(X + gl * MAXM);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc[r], __builtin_fmaf(bb, xs[r], yacc[r]));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc[r], yacc[r]);
+    }
+  } else {
+    // lane-group pairs (0,1) and (2,3) share a group: exchange words 2,3 of the even
+    // lane-group with words 0,1 of the odd one.
+    const auto s02 = __builtin_amdgcn_permlane16_swap(U.w[0], U.w[2], false, false);
+    const auto s13 = __builtin_amdgcn_permlane16_swap(U.w[1], U.w[3], false, false);
+    const uint32_t W[4] = {s02[0], s13[0], s02[1], s13[1]};
+    const int m = (g < 2) ? i : i - 8;
+    const bool av = m >= 0 && m < M;
+    const int m0 = 4 * (g & 1);
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int gl = sl * 4 + 2 * (g >> 1) + uu;
+      const char* abase = smem + L.a_off + (av ? m : 0) * pitch + gl * F::GS + 2 * (g & 1) * F::WB;
+      f32x4 acc = *reinterpret_cast<const f32x4*>(E + gl * MAXM + m0);
+#pragma unroll
+      for (int wl = 0; wl < 2; ++wl) {
+        uint32_t pr[F::PAIRS];
+        if constexpr (FMT == SIGN1) unpack_sign1_word(W[2 * uu + wl], pr); else unpack_affine2_word(W[2 * uu + wl], pr);
+#pragma unroll
+        for (int q = 0; q < F::NQ; ++q) {
+          const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pr[4 * q], pr[4 * q + 1], pr[4 * q + 2], pr[4 * q + 3]});
+          f16x8 a = {};
+          if (av) a = *reinterpret_cast<const f16x8*>(abase + wl * F::WB + 16 * q);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+        }
+      }
+      const float s = f16_to_f32(U.sb[uu] & 0xFFFFu);
+      if constexpr (F::AFFINE) {
+        const float bb = f16_to_f32(U.sb[uu] >> 16);
+        const f32x4 xs = *reinterpret_cast<const f32x4*>(X + gl * MAXM + m0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc[r], __builtin_fmaf(bb, xs[r], yacc[r]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc[r], yacc[r]);
+      }
+    }
+  }
+}
+
+// Finishes a wave's contribution to tile t for the current window: undo the row scaling,
+// sum the lane-groups holding the same rows, then either add into the tile accumulator
+// (sole contributor) or park it in the wave's slot for the fixed-order reduction.
+template <int FMT, int MODE>
+__device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t, bool sole, int slot,
+                                           int wid, int g, int i, float yacc[4]) {
+  const float* invf = reinterpret_cast<const float*>(smem + L.row_off) + MAXM;
+  const int m0 = MODE == VAR_MFMA_Q ? 0 : 4 * (g & 1);
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = yacc[r] * invf[m0 + r];
+  if constexpr (MODE == VAR_MFMA_Q) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { v[r] += __shfl_xor(v[r], 16); v[r] += __shfl_xor(v[r], 32); }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] += __shfl_xor(v[r], 32);
+  }
+  const bool writer = MODE == VAR_MFMA_Q ? (g == 0) : (g < 2);
+  if (writer) {
+    float* dst = sole ? reinterpret_cast<float*>(smem + L.ytile_off) + t * (MAXM * 16)
+                      : reinterpret_cast<float*>(smem + L.slot_off) + (wid * 2 + slot) * (MAXM * 16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* p = dst + (m0 + r) * 16 + i;
+      *p = sole ? *p + v[r] : v[r];
+    }
+  }
+}
+
+template <int FMT, int MODE, int XT>
+__device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
+  using F = Fmt<FMT>;
+  constexpr int KSTEP = 4 * F::G;
+  constexpr bool NORM = FMT == HAD2 || XT == XBF16;
+  const LdsLayout L(FMT, A.M, A.win_steps, A.tiles_max);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, i = lane & 15;
+  const int P = gridDim.x, b = blockIdx.x;
+  const int r0 = (int)(((long long)A.N * b) / P), r1 = (int)(((long long)A.N * (b + 1)) / P);
+  const int T = (r1 - r0 + 15) / 16;
+  const int S = A.K / KSTEP;
+
+  float* ytile = reinterpret_cast<float*>(smem + L.ytile_off);
+  for (int e = tid; e < T * MAXM * 16; e += NTHREADS) ytile[e] = 0.0f;
+  if (!NORM && tid < MAXM) reinterpret_cast<float*>(smem + L.row_off)[MAXM + tid] = 1.0f;
+
+  for (int ws0 = 0; ws0 < S; ws0 += A.win_steps) {
+    const int ns = min(A.win_steps, S - ws0);
+    const int UW = T * ns;
+    const int ua = (int)(((long long)UW * wid) / NW), ub = (int)(((long long)UW * (wid + 1)) / NW);
+
+    // first units' loads go out before the staging so they overlap it
+    Unit ring[PREF];
+#pragma unroll
+    for (int d = 0; d < PREF; ++d)
+      if (ua + d < ub) load_unit<FMT, MODE>(A, r0, r1, ws0, ns, ua + d, g, i, ring[d]);
+
+    __syncthreads();  // previous window's readers are done with the LDS
+    stage_window<FMT, XT>(A, smem, L, ws0 * KSTEP, ns * KSTEP);
+    __syncthreads();
+
+    int cur = -1;
+    float yacc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int base = ua; base < ub; base += PREF) {
+#pragma unroll
+      for (int d = 0; d < PREF; ++d) {
+        const int u = base + d;
+        if (u < ub) {
+          const int t = u / ns, sl = u - t * ns;
+          if (t != cur) {
+            if (cur >= 0) {
+              const bool sole = ua <= cur * ns && ub >= (cur + 1) * ns;
+              flush_tile<FMT, MODE>(smem, L, cur, sole, cur == ua / ns ? 0 : 1, wid, g, i, yacc);
+            }
+            cur = t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[r] = 0.f;
+          }
+          compute_unit<FMT, MODE>(ring[d], smem, L, A.a_pitch, sl, g, i, A.M, yacc);
+          if (u + PREF < ub) load_unit<FMT, MODE>(A, r0, r1, ws0, ns, u + PREF, g, i, ring[d]);
+        }
+      }
+    }
+    if (cur >= 0) {
+      const bool sole = ua <= cur * ns && ub >= (cur + 1) * ns;
+      flush_tile<FMT, MODE>(smem, L, cur, sole, cur == ua / ns ? 0 : 1, wid, g, i, yacc);
+    }
+    __syncthreads();
+
+    // fixed-order reduction of tiles split between waves: a tile is split when a wave
+    // boundary falls strictly inside it; its contributors are the non-empty waves whose
+    // unit range meets it, summed in wave order.
+    {
+      const float* slots = reinterpret_cast<const float*>(smem + L.slot_off);
+      const int e = tid & 127;                 // element (row, col) of a tile
+      for (int bw = 1 + (tid >> 7); bw < NW; bw += NTHREADS / 128) {
+        const int B = (int)(((long long)UW * bw) / NW);
+        if (B <= 0 || B >= UW || B % ns == 0) continue;
+        const int t = B / ns;
+        // handle tile t once: by the first boundary inside it
+        const int Bprev = (int)(((long long)UW * (bw - 1)) / NW);
+        if (bw > 1 && Bprev > t * ns && Bprev % ns != 0 && Bprev / ns == t) continue;
+        float sum = 0.0f;
+        for (int w2 = 0; w2 < NW; ++w2) {
+          const int a2 = (int)(((long long)UW * w2) / NW), b2 = (int)(((long long)UW * (w2 + 1)) / NW);
+          if (a2 >= b2 || b2 <= t * ns || a2 >= (t + 1) * ns) continue;
+          const int slot = (t == a2 / ns) ? 0 : 1;
+          sum += slots[(w2 * 2 + slot) * (MAXM * 16) + e];
+        }
+        ytile[t * (MAXM * 16) + e] += sum;
+      }
+    }
+  }
+  __syncthreads();
+
+  // write y[m, r0 .. r1) from the tile accumulators
+  const int nr = r1 - r0;
+  for (int e = tid; e < A.M * nr; e += NTHREADS) {
+    const int m = e / nr, rr = e - m * nr;
+    A.y[(size_t)m * A.N + r0 + rr] = ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)];
+  }
+}
+
+// The kernel names carry the variant name, so a trace shows which variant ran.
+template <int FMT, int XT>
+__global__ __launch_bounds__(NTHREADS) void vg_mfma_q(MfmaArgs A) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  mfma_body<FMT, VAR_MFMA_Q, XT>(A, smem);
+}
+template <int FMT, int XT>
+__global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  mfma_body<FMT, VAR_MFMA_H, XT>(A, smem);
+}
+
+// ---------------------------------------------------------------------------------------
+// Host side of the MFMA variants.
+static int pick_grid(int N, const DeviceInfo& dev) {
+  const int tiles = (N + 15) / 16;
+  return tiles < dev.cu_count ? tiles : dev.cu_count;
+}
+
+size_t mfma_lds_bytes(int fmt, int variant, int M, int K, int N, int grid, int max_lds, int* win_steps) {
+  (void)variant;
+  const int kstep = 4 * fmt_group(fmt);
+  const int S = K / kstep;
+  const int rows_max = (N + grid - 1) / grid + 1;
+  const int tiles_max = (rows_max + 15) / 16 + 1;
+  // largest window that fits, then balanced so windows have equal step counts
+  int best = 0;
+  for (int ws = S; ws >= 1; --ws) {
+    const LdsLayout L(fmt, M, ws, tiles_max);
+    if (L.total <= max_lds) { best = ws; break; }
+  }
+  if (best == 0) { *win_steps = 0; return 0; }
+  const int nwin = (S + best - 1) / best;
+  const int ws = (S + nwin - 1) / nwin;
+  *win_steps = ws;
+  return (size_t)LdsLayout(fmt, M, ws, tiles_max).total;
+}
+
+template <int FMT, int MODE, int XT>
+static hipError_t launch_one(const GemmCall& c, const DeviceInfo& dev) {
+  const int grid = pick_grid(c.N, dev);
+  int ws = 0;
+  const size_t lds = mfma_lds_bytes(FMT, MODE, c.M, c.K, c.N, grid, dev.max_lds, &ws);
+  if (ws == 0) return hipErrorInvalidValue;
+  MfmaArgs A;
+  A.x = c.x; A.w = c.w; A.scales = c.scales; A.biases = c.biases; A.y = c.y;
+  A.M = c.M; A.K = c.K; A.N = c.N;
+  A.win_steps = ws;
+  const int rows_max = (c.N + grid - 1) / grid + 1;
+  A.tiles_max = (rows_max + 15) / 16 + 1;
+  A.a_pitch = ws * 4 * fmt_gs(FMT) + 16;
+  void (*kern)(MfmaArgs) = MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT> : vg_mfma_h<FMT, XT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, dev.max_lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHREADS), lds, c.stream, A);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma(const GemmCall& c, int variant, const DeviceInfo& dev) {
+#define VG_DISPATCH_XT(FMT, MODE)                                                   \
+  switch (c.xt) {                                                                    \
+    case XF16: return launch_one<FMT, MODE, XF16>(c, dev);                           \
+    case XBF16: return launch_one<FMT, MODE, XBF16>(c, dev);                         \
+    default: return hipErrorInvalidValue;                                            \
+  }
+#define VG_DISPATCH_MODE(FMT)                                                       \
+  if (variant == VAR_MFMA_Q) { VG_DISPATCH_XT(FMT, VAR_MFMA_Q) }                     \
+  else { VG_DISPATCH_XT(FMT, VAR_MFMA_H) }
+  switch (c.fmt) {
+    case SIGN1: VG_DISPATCH_MODE(SIGN1)
+    case AFFINE2: VG_DISPATCH_MODE(AFFINE2)
+    case HAD2: VG_DISPATCH_MODE(HAD2)
+    default: return hipErrorInvalidValue;
+  }
+#undef VG_DISPATCH_MODE
+#undef VG_DISPATCH_XT
+}
+
+}  // namespace vg

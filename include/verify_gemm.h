@@ -1,0 +1,147 @@
+/*
+ * verify_gemm.h -- C ABI of the few-row quantized verify GEMM for MI355X (gfx950).
+ *
+ * Speculative decoding checks a block of M drafted rows in one target pass.  The verify
+ * GEMM multiplies those M <= 8 activation rows against packed low-bit weights, decoding
+ * each weight once inside the contraction and never writing a dense copy, so the cost is
+ * nearly flat in M ("Ishizuki" README, section "Kernels written for the verify";
+ * "dflash-mlx-bonsai2" README, sections "Why" and "What this fork adds").
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named x, w*, scales, biases, y, x_out, idx, codes are DEVICE pointers owned
+ *     by the caller.  The library never frees or keeps them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls only
+ *     enqueue work and return; results are valid once the caller synchronizes the stream.
+ *   - Arguments are validated on the host before anything is enqueued.  On error the call
+ *     returns a non-zero vg_status, enqueues nothing, and vg_last_error() returns a message
+ *     (per calling thread).
+ *   - The library allocates no device memory in these calls.  It keeps a small read-only
+ *     per-device state (device attributes) created on first use.
+ *   - Activations x are row-major [M, K] of dtype VG_F32, VG_F16 or VG_BF16 (raw IEEE bits);
+ *     outputs y are row-major fp32 [M, N]; rows >= M are never read or written.
+ *   - Packed weights, row-major over the N output rows, little-endian words, LSB first:
+ *       1-bit sign:  wbits[N, K/32] uint32; weight k of a row is bit k%32 of word k/32;
+ *                    bit 0 -> -scale, bit 1 -> +scale; one fp16 scale per 128 weights,
+ *                    scales[N, K/128] ("Bonsai-27B-mlx-1bit" model card, binary weight
+ *                    format).
+ *       2-bit affine: wq[N, K/16] uint32; code k is bits 2(k%16)..2(k%16)+1 of word k/16;
+ *                    w = q*s + b with one fp16 scale and one fp16 bias per 64 weights,
+ *                    scales[N, K/64], biases[N, K/64] (MLX grouped affine format: a scale
+ *                    and a bias per group; same model card, MLX paragraph).
+ *   - x, weights, scales, biases and y must be 16-byte aligned (whole-word vector loads).
+ */
+#ifndef VERIFY_GEMM_H
+#define VERIFY_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VG_OK = 0,
+  VG_ERR_ARG = 1,          /* null pointer, unknown enum, bad count                         */
+  VG_ERR_SHAPE = 2,        /* M outside 1..8, N < 1, K not a multiple of the group          */
+  VG_ERR_ALIGN = 3,        /* a pointer is not 16-byte aligned                              */
+  VG_ERR_DTYPE = 4,        /* activation dtype not one of vg_dtype                          */
+  VG_ERR_UNSUPPORTED = 5,  /* a transform the library cannot apply (e.g. Hadamard block
+                              other than 128): refused, never run as the plain format       */
+  VG_ERR_HIP = 6           /* the HIP runtime reported an error while enqueueing            */
+} vg_status;
+
+typedef enum { VG_F32 = 0, VG_F16 = 1, VG_BF16 = 2 } vg_dtype;
+
+typedef enum { VG_FMT_SIGN1 = 0, VG_FMT_AFFINE2 = 1, VG_FMT_HAD2 = 2 } vg_format;
+
+/* Maximum drafted rows per call (verify blocks of up to 8 rows are padded to 8:
+   "dflash-mlx-bonsai2" README, "What this fork adds"). */
+#define VG_MAX_ROWS 8
+
+/*
+ * y[M, N] = x[M, K] * W^T with W the 1-bit sign g128 weights.
+ * Requires 1 <= M <= 8, N >= 1, K >= 128, K % 128 == 0.
+ * Source: "Bonsai-27B-mlx-1bit" model card (each weight one sign bit, 0 -> -scale,
+ * 1 -> +scale, one FP16 scale per group of 128 weights).
+ */
+vg_status verify_gemm_sign1(const void* x, int x_dtype, int M, int K,
+                            const uint32_t* wbits, const uint16_t* scales, int N,
+                            float* y, void* stream);
+
+/*
+ * y[M, N] = x[M, K] * W^T with W the 2-bit affine g64 weights, w = q*s + b.
+ * Requires 1 <= M <= 8, N >= 1, K >= 64, K % 64 == 0.
+ * Source: MLX grouped affine codes ("Ishizuki" README, "Kernels written for the verify":
+ * the verify kernel for MLX affine codes; scale and bias per group: "Bonsai-27B-mlx-1bit"
+ * model card, MLX paragraph).
+ */
+vg_status verify_gemm_affine2(const void* x, int x_dtype, int M, int K,
+                              const uint32_t* wq, const uint16_t* scales,
+                              const uint16_t* biases, int N, float* y, void* stream);
+
+/*
+ * y[M, N] = (x[M, K] * H_bd) * W^T with H_bd block-diagonal, each block the normalized
+ * Sylvester Hadamard H_128 / sqrt(128), and W 2-bit affine g64 as above.  The rotation
+ * runs inside the GEMM's prologue on each workgroup's activations; no rotated copy of x
+ * is written.  had_block must be 128 (anything else -> VG_ERR_UNSUPPORTED).
+ * Requires 1 <= M <= 8, N >= 1, K >= 128, K % 128 == 0.
+ * Source: "dflash-mlx-bonsai2" README, "What this fork adds" (Hadamard-rotated 2-bit pack,
+ * verify GEMM with the Hadamard fused into its prep); "Ishizuki" README (a pack declaring
+ * a transform that cannot be applied is refused, not loaded as plain affine).
+ */
+vg_status verify_gemm_had2(const void* x, int x_dtype, int M, int K,
+                           const uint32_t* wq, const uint16_t* scales,
+                           const uint16_t* biases, int N, int had_block, float* y,
+                           void* stream);
+
+/*
+ * x_out[M, K] (fp32) = x[M, K] * H_bd, the same block-128 normalized Sylvester rotation
+ * as verify_gemm_had2, as a standalone call.  block must be 128.  Requires 1 <= M <= 8,
+ * K % 128 == 0.
+ */
+vg_status hadamard_rotate(const void* x, int x_dtype, int M, int K, int block,
+                          float* x_out, void* stream);
+
+/*
+ * idx[m] = argmax_n y[m, n] for m < M (lowest n on ties; NaN never wins), for the output
+ * head of a verify pass.  y is fp32 [M, N] row-major, idx is int32 [M].
+ * Requires 1 <= M <= 8, N >= 1.
+ */
+vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* vg_last_error(void);
+
+/*
+ * Kernel variant the per-shape dispatch picks for (format, x_dtype, M, N, K), or -1 if the
+ * shape is invalid.  vg_variant_name() gives its name, which is also the kernel's name
+ * prefix in a rocprofv3 trace.
+ */
+int vg_plan_variant(int format, int x_dtype, int M, int N, int K);
+const char* vg_variant_name(int variant);
+
+/*
+ * Force a variant for later calls on this process (tests and A/B timing); -1 restores
+ * the dispatch.  Returns VG_ERR_ARG for an unknown variant.  A forced variant that does
+ * not support a call's (format, dtype, M) makes that call fail with VG_ERR_UNSUPPORTED.
+ */
+vg_status vg_force_variant(int variant);
+
+/* Number of variants; variant ids are 0 .. vg_variant_count()-1. */
+int vg_variant_count(void);
+
+/*
+ * Debug: decode the packed codes on the GPU into one byte per weight, codes[N, K] uint8
+ * (0/1 for sign bits, 0..3 for 2-bit codes), using the same bit extraction as the GEMM
+ * kernels, so tests can compare codes bit for bit.
+ */
+vg_status vg_debug_unpack_sign1(const uint32_t* wbits, int N, int K, uint8_t* codes,
+                                void* stream);
+vg_status vg_debug_unpack_affine2(const uint32_t* wq, int N, int K, uint8_t* codes,
+                                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERIFY_GEMM_H */

@@ -1,0 +1,124 @@
+"""CPU tests of the C ABI: the library loads, exports what the header declares, and
+rejects every invalid argument with its status before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import few_row_quantized_verify_amd as vgm
+from few_row_quantized_verify_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "verify_gemm.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:vg_status|int|const char\*|char\*)\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ("verify_gemm_sign1", "verify_gemm_affine2", "verify_gemm_had2", "hadamard_rotate",
+               "verify_argmax_rows", "vg_last_error", "vg_plan_variant", "vg_variant_name",
+               "vg_force_variant", "vg_variant_count", "vg_debug_unpack_sign1", "vg_debug_unpack_affine2"):
+        assert fn in names, fn
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_signatures_cover_header():
+    assert set(declared_functions()) == set(B._SIGS)
+
+
+ALIGNED = 1 << 20   # a fake, 16-byte aligned address: never dereferenced on the error paths
+MISALIGNED = ALIGNED + 4
+
+
+def _err():
+    return B.lib().vg_last_error().decode()
+
+
+@pytest.mark.parametrize("M", [0, -1, 9, 100])
+def test_bad_row_count(M):
+    st = B.lib().verify_gemm_sign1(ALIGNED, B.VG_F16, M, 512, ALIGNED, ALIGNED, 256, ALIGNED, None)
+    assert st == B.VG_ERR_SHAPE and "M=" in _err()
+
+
+def test_bad_n_and_k():
+    L = B.lib()
+    assert L.verify_gemm_sign1(ALIGNED, B.VG_F16, 1, 512, ALIGNED, ALIGNED, 0, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.verify_gemm_sign1(ALIGNED, B.VG_F16, 1, 500, ALIGNED, ALIGNED, 8, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.verify_gemm_sign1(ALIGNED, B.VG_F16, 1, 64, ALIGNED, ALIGNED, 8, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.verify_gemm_affine2(ALIGNED, B.VG_F16, 1, 96, ALIGNED, ALIGNED, ALIGNED, 8, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.verify_gemm_had2(ALIGNED, B.VG_F16, 1, 192, ALIGNED, ALIGNED, ALIGNED, 8, 128, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.hadamard_rotate(ALIGNED, B.VG_F16, 1, 200, 128, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.verify_argmax_rows(ALIGNED, 1, 0, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.verify_argmax_rows(ALIGNED, 9, 10, ALIGNED, None) == B.VG_ERR_SHAPE
+
+
+def test_bad_dtype():
+    st = B.lib().verify_gemm_affine2(ALIGNED, 7, 1, 256, ALIGNED, ALIGNED, ALIGNED, 8, ALIGNED, None)
+    assert st == B.VG_ERR_DTYPE and "dtype" in _err()
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_null_pointers(which):
+    ptrs = [ALIGNED] * 5
+    ptrs[which] = None
+    x, w, s, b, y = ptrs
+    st = B.lib().verify_gemm_affine2(x, B.VG_F16, 2, 256, w, s, b, 8, y, None)
+    assert st == B.VG_ERR_ARG and "null" in _err()
+
+
+@pytest.mark.parametrize("which", range(4))
+def test_misaligned_pointers(which):
+    ptrs = [ALIGNED] * 4
+    ptrs[which] = MISALIGNED
+    x, w, s, y = ptrs
+    st = B.lib().verify_gemm_sign1(x, B.VG_BF16, 2, 512, w, s, 8, y, None)
+    assert st == B.VG_ERR_ALIGN and "aligned" in _err()
+
+
+@pytest.mark.parametrize("block", [0, 64, 256, 127])
+def test_unsupported_hadamard_block_is_refused(block):
+    L = B.lib()
+    st = L.verify_gemm_had2(ALIGNED, B.VG_F16, 1, 256, ALIGNED, ALIGNED, ALIGNED, 8, block, ALIGNED, None)
+    assert st == B.VG_ERR_UNSUPPORTED and "Hadamard block" in _err()
+    assert L.hadamard_rotate(ALIGNED, B.VG_F16, 1, 256, block, ALIGNED, None) == B.VG_ERR_UNSUPPORTED
+
+
+def test_debug_unpack_validation():
+    L = B.lib()
+    assert L.vg_debug_unpack_sign1(ALIGNED, 4, 48, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.vg_debug_unpack_affine2(None, 4, 64, ALIGNED, None) == B.VG_ERR_ARG
+    assert L.vg_debug_unpack_affine2(ALIGNED, 0, 64, ALIGNED, None) == B.VG_ERR_SHAPE
+
+
+def test_variants_and_forcing():
+    names = [vgm.variant_name(i) for i in range(vgm.variant_count())]
+    assert names == ["vg_mfma_q", "vg_mfma_h", "vg_valu"]
+    assert vgm.variant_name(99) == ""
+    with pytest.raises(vgm.VerifyGemmError) as e:
+        vgm.force_variant(99)
+    assert e.value.status == B.VG_ERR_ARG
+    vgm.force_variant(-1)
+
+
+def test_plan_rejects_invalid_shapes():
+    assert vgm.plan_variant("sign1", "f16", 0, 16, 512) == -1
+    assert vgm.plan_variant("sign1", "f16", 9, 16, 512) == -1
+    assert vgm.plan_variant("affine2", "f16", 1, 16, 100) == -1
+
+
+def test_python_binding_rejects_unknown_dtype():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 128), dtype=torch.int32)
+    with pytest.raises(vgm.VerifyGemmError) as e:
+        vgm.verify_gemm_sign1(x, x, x)
+    assert e.value.status == B.VG_ERR_DTYPE

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP verify GEMMs, called through the C ABI, against the fp64 oracle.
+
+Bar (from the method's acceptance rule): per-row normwise relative error
+max_n |y - y_ref| / max_n |y_ref| <= 2e-3 for fp16/bf16 activations with fp32
+accumulation; decoded codes bit-exact; per-row argmax of the output head identical.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synthetic import draw_case, workload_case
+from synthetic.torch_io import case_tensors, words_tensor, x_tensor
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def vg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import few_row_quantized_verify_amd as m
+    m.lib()  # fails loudly if the library is missing
+    m.force_variant(-1)
+    yield m
+    m.force_variant(-1)
+
+
+def run(vg, case, M, y=None):
+    x, w, s, b = case_tensors(case, M)
+    out = vg.verify_gemm(case.fmt, x, w, s, b, y=y)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def check(case, M, y_gpu, cols=None, tol=TOL, label=""):
+    if cols is None:
+        y_ref = oracle.verify(case.fmt, case.x(M), case.x_dtype, case.words, case.scales, case.biases)
+        got = y_gpu
+    else:
+        y_ref = oracle.verify_columns(case.fmt, case.x(M), case.x_dtype, case.words, case.scales,
+                                      case.biases, cols)
+        got = y_gpu[:, cols]
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    err = oracle.normwise_rel_err(got, y_ref)
+    print(f"{label} fmt={case.fmt} x={case.x_dtype} K={case.K} N={case.N} M={M} err={err:.2e}", flush=True)
+    assert err <= tol, f"{label}: normwise error {err:.3e} > {tol}"
+    return err
+
+
+# ----------------------------------------------------------------------------- codes
+@pytest.mark.parametrize("fmt,K", [("sign1", 512), ("affine2", 256), ("sign1", 1024), ("affine2", 640)])
+def test_debug_unpack_is_bit_exact(vg, fmt, K):
+    rng = np.random.default_rng(K)
+    WK = 32 if fmt == "sign1" else 16
+    words = rng.integers(0, 1 << 32, size=(37, K // WK), dtype=np.uint64).astype(np.uint32)
+    words[0, :4] = [0x00000001, 0x80000000, 0xAAAAAAAA, 0xE4E4E4E4]
+    words[1, :] = 0xFFFFFFFF
+    words[2, :] = 0
+    codes = vg.debug_unpack(fmt, words_tensor(words), K)
+    torch.cuda.synchronize()
+    ref = oracle.unpack_sign1(words, K) if fmt == "sign1" else oracle.unpack_affine2(words, K)
+    assert np.array_equal(codes.cpu().numpy(), ref)
+
+
+# ----------------------------------------------------------------------------- small shapes
+SMALL = [("sign1", 1024, 100), ("affine2", 768, 100), ("had2", 768, 100)]
+
+
+@pytest.mark.parametrize("fmt,K,N", SMALL)
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16", "f32"])
+def test_small_all_rows(vg, fmt, K, N, x_dtype):
+    """Several 16-row tiles, a ragged last tile and several K-steps, every row count."""
+    case = draw_case(fmt, K, N, x_dtype, seed=1)
+    for M in range(1, 9):
+        check(case, M, run(vg, case, M), label=f"small[{vg.variant_name(vg.plan_variant(fmt, x_dtype, M, N, K))}]")
+
+
+@pytest.mark.parametrize("fmt,K", [("sign1", 512), ("affine2", 256), ("had2", 256)])
+@pytest.mark.parametrize("N", [1, 17, 33, 257])
+def test_ragged_n(vg, fmt, K, N):
+    case = draw_case(fmt, K, N, "f16", seed=2)
+    for M in (1, 4, 5, 8):
+        check(case, M, run(vg, case, M), label="ragged")
+
+
+@pytest.mark.parametrize("fmt,K,N", SMALL)
+def test_every_variant(vg, fmt, K, N):
+    case = draw_case(fmt, K, N, "f16", seed=3)
+    try:
+        for v in range(vg.variant_count()):
+            vg.force_variant(v)
+            for M in (1, 3, 4, 6, 8):
+                if vg.plan_variant(fmt, "f16", M, N, K) < 0:
+                    continue
+                check(case, M, run(vg, case, M), label=f"forced[{vg.variant_name(v)}]")
+    finally:
+        vg.force_variant(-1)
+
+
+def test_forced_variant_refuses_unsupported_rows(vg):
+    case = draw_case("sign1", 512, 32, "f16", seed=4)
+    vg.force_variant(0)  # the 4-row variant
+    try:
+        with pytest.raises(vg.VerifyGemmError) as e:
+            run(vg, case, 8)
+        assert e.value.status == 5
+    finally:
+        vg.force_variant(-1)
+
+
+@pytest.mark.parametrize("fmt,K", [("affine2", 320), ("had2", 384), ("sign1", 640)])
+def test_k_not_multiple_of_step_falls_back(vg, fmt, K):
+    case = draw_case(fmt, K, 40, "f16", seed=5)
+    for M in (1, 8):
+        check(case, M, run(vg, case, M), label="k-ragged")
+
+
+def test_dtype_alternation_same_shape(vg):
+    """fp16, bf16 and fp32 calls on one shape must each use their own build."""
+    outs = []
+    for x_dtype in ("f16", "bf16", "f32", "f16", "bf16"):
+        case = draw_case("affine2", 512, 64, x_dtype, seed=6)
+        outs.append(check(case, 5, run(vg, case, 5), label="alternate"))
+    assert len(outs) == 5
+
+
+def test_multi_window_long_k(vg):
+    """K long enough that the activations are staged in more than one LDS window."""
+    case = draw_case("sign1", 17408, 48, "bf16", seed=7)
+    for M in (1, 5, 8):
+        check(case, M, run(vg, case, M), label="long-k")
+    case = draw_case("had2", 16384, 40, "f16", seed=8)
+    for M in (2, 8):
+        check(case, M, run(vg, case, M), label="long-k-had")
+
+
+def test_output_rows_beyond_m_untouched(vg):
+    case = draw_case("affine2", 512, 50, "f16", seed=9)
+    y = torch.full((8, 50), 7.25, dtype=torch.float32, device="cuda")
+    x, w, s, b = case_tensors(case, 3)
+    vg.verify_gemm_affine2(x, w, s, b, y=y[:3])
+    torch.cuda.synchronize()
+    assert torch.all(y[3:] == 7.25)
+
+
+def test_large_magnitude_bf16_rows(vg):
+    """bf16 rows far outside fp16 range are handled by per-row scaling."""
+    case = draw_case("sign1", 1024, 64, "bf16", seed=10)
+    from synthetic import bf16_bits
+    x64 = oracle.decode_bf16(case.x_all)
+    x64[0] *= 2.0 ** 40
+    x64[1] *= 2.0 ** -40
+    case.x_all = bf16_bits(x64)
+    for M in (2, 8):
+        check(case, M, run(vg, case, M), label="bf16-range")
+
+
+# ----------------------------------------------------------------------------- Hadamard, argmax
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16", "f32"])
+def test_hadamard_rotate(vg, x_dtype):
+    case = draw_case("had2", 1024, 1, x_dtype, seed=11)
+    for M in (1, 8):
+        x = x_tensor(case.x(M), x_dtype)
+        out = vg.hadamard_rotate(x).cpu().numpy().astype(np.float64)
+        ref = oracle.hadamard_rotate(oracle.activations(case.x(M), x_dtype), 128)
+        err = np.max(np.abs(out - ref)) / np.max(np.abs(ref))
+        assert err < 1e-6, err
+
+
+def test_argmax_kernel_exact(vg):
+    rng = np.random.default_rng(12)
+    y = rng.standard_normal((8, 151936)).astype(np.float32)
+    y[0, 100] = y[0, 7] = 50.0          # tie: lowest index wins
+    y[1, :] = -3.0                      # all equal
+    y[2, 5] = np.nan                    # NaN never wins
+    y[2, 9] = 60.0
+    idx = vg.verify_argmax_rows(torch.from_numpy(y).cuda()).cpu().numpy()
+    assert idx[0] == 7 and idx[1] == 0 and idx[2] == 9
+    yy = y.copy()
+    yy[2, 5] = -np.inf
+    assert list(idx) == list(np.argmax(yy, axis=1))
+
+
+# ----------------------------------------------------------------------------- full workloads
+def sample_cols(N, k=384, seed=0):
+    rng = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([rng.choice(N, size=min(k, N), replace=False),
+                                     [0, 1, 15, 16, N // 2, N - 17, N - 16, N - 1]]))
+    return cols
+
+
+@pytest.mark.parametrize("name,Ms", [
+    ("mlp_up_affine2_k5120_n17408", (1, 2, 4, 5, 8)),
+    ("mlp_up_sign1_k5120_n17408", (1, 4, 8)),
+    ("mlp_down_sign1_k17408_n5120", (1, 5, 8)),
+    ("attn_had2_k5120_n6144", (1, 3, 8)),
+    ("tiny_sign1_k512_n256", tuple(range(1, 9))),
+])
+def test_full_workload_sampled(vg, name, Ms):
+    case = workload_case(name, seed=0)
+    cols = sample_cols(case.N) if case.N > 1024 else None
+    for M in Ms:
+        check(case, M, run(vg, case, M), cols=cols, label=name)
+
+
+def test_head_argmax_matches_oracle(vg):
+    with open(os.path.join(GOLDEN, "head_affine2_k5120_n151936_argmax.json")) as f:
+        gold = json.load(f)
+    case = workload_case(gold["workload"], seed=gold["seed"])
+    cols = sample_cols(case.N, k=256)
+    for M in (5, 6, 7, 8):
+        x, w, s, b = case_tensors(case, M)
+        y = vg.verify_gemm_affine2(x, w, s, b)
+        idx = vg.verify_argmax_rows(y).cpu().numpy()
+        y_np = y.cpu().numpy().astype(np.float64)
+        err = check(case, M, y_np, cols=cols, label="head")
+        for m in range(M):
+            if idx[m] != gold["argmax"][m]:
+                # a flip is only acceptable as a diagnosed near-tie, and none is expected
+                # at these gaps; report it loudly either way
+                raise AssertionError(f"row {m}: argmax {idx[m]} != oracle {gold['argmax'][m]} "
+                                     f"(oracle top-2 gap {gold['top2_gap'][m]:.3e}, err {err:.2e})")
+        assert np.array_equal(idx, np.argmax(y_np, axis=1))
