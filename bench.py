@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the few-row quantized verify GEMM on one MI355X.
+
+Default workload: 2-bit affine g64 weights, MLP up-projection shape K=5120, N=17408,
+fp16 activations, verify calls at every row count M = 1..8.  A "step" is one verify call
+at each M (8 calls).  The timed region runs `--steps` steps as eight blocks of calls of
+one row count each, with a HIP event pair around each block (events on the stream the
+kernels run on), and cycles through a pool of >= 1 GiB of distinct weight copies so the
+256 MB Infinity Cache cannot serve repeated calls.  Inputs are resident in HBM before
+timing starts.
+
+Prints one JSON line: value = packed-weight bytes (codes + fp16 scales + fp16 biases)
+moved per second over all timed calls (GB/s, 1e9), plus per-M microseconds per call,
+t(M=8)/t(M=1), a roofline object for the dominant kernel and the CPU oracle baseline.
+
+Options:
+  --workload NAME    another named workload (see synthetic.inputs.WORKLOADS)
+  --table            also print one JSON line per workload and M (not the default)
+  --no-cpu           skip the CPU oracle baseline leg
+  --copy-calibration run only a device-to-device copy of known size (for HBM counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synthetic import WORKLOADS, workload_case  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+POOL_BYTES = 1 << 30
+METRIC = "µs/call and packed-weight GB/s (% of HBM peak) at M=1..8; t(M=8)/t(M=1)"
+KERNEL_SOURCES = ["few_row_quantized_verify_amd/csrc/vg_kernels.hip",
+                  "few_row_quantized_verify_amd/csrc/vg_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def packed_bytes(case) -> int:
+    n = case.words.nbytes + case.scales.nbytes
+    return n + (case.biases.nbytes if case.biases is not None else 0)
+
+
+def x_bytes(case, M):
+    return M * case.K * (4 if case.x_dtype == "f32" else 2)
+
+
+def cpu_baseline(case) -> dict:
+    """The oracle (fp64 numpy, untuned) on the host, on a bounded sample of columns."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    M = 8
+    ncols = min(case.N, 8192)
+    cols = np.arange(ncols)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.verify_columns(case.fmt, case.x(M), case.x_dtype, case.words, case.scales,
+                              case.biases, cols)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 20:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    frac = ncols / case.N
+    gbs = packed_bytes(case) * frac / dt / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"M=8, first {ncols} of {case.N} output columns of {case.fmt} K={case.K}, "
+                      f"{reps} reps, {dt * 1e3:.1f} ms/rep; us/call-equivalent "
+                      f"{dt / frac * 1e6:.0f}"}
+
+
+def load_traffic(kernel: str, digest: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    ent = t.get("kernels", {}).get(kernel)
+    if not ent or ent.get("source_digest") != digest:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mlp_up_affine2_k5120_n17408")
+    ap.add_argument("--table", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the verify GEMM runs on one device here; "
+              "run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import few_row_quantized_verify_amd as vg
+    from synthetic.torch_io import case_tensors, f16_tensor, words_tensor
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        a = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}))
+        return 0
+
+    names = list(WORKLOADS) if args.table else [args.workload]
+    lines = []
+    headline = None
+    for name in names:
+        fmt, K, N, x_dtype, Ms = WORKLOADS[name]
+        case = workload_case(name, seed=0)
+        pb = packed_bytes(case)
+        ncopy = max(2, -(-POOL_BYTES // pb))
+        x_all = {M: case_tensors(case, M, dev)[0] for M in Ms}
+        w0 = words_tensor(case.words, dev)
+        s0 = f16_tensor(case.scales, dev)
+        b0 = f16_tensor(case.biases, dev) if case.biases is not None else None
+        pool = [(w0.clone(), s0.clone(), None if b0 is None else b0.clone()) for _ in range(ncopy)]
+        ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
+
+        def call(M, j):
+            w, s, b = pool[j % ncopy]
+            vg.verify_gemm(fmt, x_all[M], w, s, b, y=ys[M])
+
+        for M in Ms:
+            for j in range(args.warmup):
+                call(M, j)
+        torch.cuda.synchronize()
+
+        ev = {M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        j = 0
+        for M in Ms:
+            ev[M][0].record()
+            for _ in range(args.steps):
+                call(M, j)
+                j += 1
+            ev[M][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        us = {M: ev[M][0].elapsed_time(ev[M][1]) * 1e3 / args.steps for M in Ms}
+        total_s = sum(us.values()) * args.steps * 1e-6
+        value = pb * len(Ms) * args.steps / total_s / 1e9
+        per_m = {str(M): {"us_per_call": round(us[M], 3),
+                          "gbs": round(pb / (us[M] * 1e-6) / 1e9, 1),
+                          "pct_hbm_peak": round(100 * pb / (us[M] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                          "variant": vg.variant_name(vg.plan_variant(fmt, x_dtype, M, N, K))}
+                 for M in Ms}
+        Mtop = max(Ms)
+        kern = per_m[str(Mtop)]["variant"]
+        algo = pb + x_bytes(case, Mtop) + Mtop * N * 4
+        achieved = algo / (us[Mtop] * 1e-6) / 1e9
+        traffic = load_traffic(f"{kern}/{name}/M{Mtop}", kernel_source_digest())
+        line = {
+            "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(sum(us.values()) * 1e-3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16" if x_dtype != "f32" else "f32", "data": "synthetic",
+            "config": {"workload": name, "format": fmt, "K": K, "N": N, "x_dtype": x_dtype,
+                       "M": list(Ms), "packed_bytes_per_call": pb, "weight_pool_copies": ncopy},
+            "per_m": per_m,
+            "t8_over_t1": round(us[Mtop] / us[min(Ms)], 3),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic, "kernel": kern, "M": Mtop,
+                         "algorithmic_bytes_per_launch": algo},
+            "wall_s_timed": round(wall, 4),
+        }
+        if name == args.workload:
+            headline = line
+        lines.append(line)
+        del pool
+        torch.cuda.empty_cache()
+
+    if headline is None:
+        headline = lines[0]
+    if not args.no_cpu:
+        headline["cpu_baseline"] = cpu_baseline(workload_case(headline["config"]["workload"], seed=0))
+    if args.table:
+        for l in lines:
+            if l is not headline:
+                print(json.dumps(l))
+    print(json.dumps(headline))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -79,7 +79,7 @@ vg_status check_ptr(const void* p, const char* name) {
   return VG_OK;
 }
 
-int kstep_of(int fmt) { return fmt == vg::SIGN1 ? 512 : 256; }
+int kstep_of(int fmt) { (void)fmt; return 1024; }   // K per MFMA-kernel unit, both formats
 
 // Per-shape dispatch.  fp32 activations take the exact fp32 VALU kernel.  fp16/bf16 take
 // the MFMA kernels when K is a whole number of 4-group steps: mode Q up to 4 rows, mode H

@@ -36,18 +36,20 @@ enum XType : int { XF32 = 0, XF16 = 1, XBF16 = 2 };
 
 constexpr int NW = 8;               // waves per workgroup
 constexpr int NTHREADS = NW * 64;
-constexpr int PREF = 4;             // units in flight per wave
 constexpr int MAXM = 8;
 
 template <int FMT> struct Fmt;
+// GL: consecutive quantization groups each lane loads per unit (16*GL bytes of codes and
+// 2*GL bytes of scales in single loads, 64*GL contiguous bytes per row and unit); a unit
+// covers 4*GL groups = 1024 K for both formats.  PREF: units in flight per wave.
 template <> struct Fmt<SIGN1> {
-  static constexpr int G = 128, WORD_K = 32, PAIRS = 16, NQ = 4;
+  static constexpr int G = 128, WORD_K = 32, PAIRS = 16, NQ = 4, GL = 2, PREF = 4;
   static constexpr int WB = 64;           // LDS bytes of one word's operand window
   static constexpr int GS = 4 * WB + 16;  // LDS bytes per group (+16 pad vs bank conflicts)
   static constexpr bool AFFINE = false;
 };
 template <> struct Fmt<AFFINE2> {
-  static constexpr int G = 64, WORD_K = 16, PAIRS = 8, NQ = 2;
+  static constexpr int G = 64, WORD_K = 16, PAIRS = 8, NQ = 2, GL = 4, PREF = 2;
   static constexpr int WB = 32;
   static constexpr int GS = 4 * WB + 16;
   static constexpr bool AFFINE = true;
@@ -57,6 +59,8 @@ template <> struct Fmt<HAD2> : Fmt<AFFINE2> {};
 __host__ __device__ constexpr int fmt_group(int fmt) { return fmt == SIGN1 ? 128 : 64; }
 __host__ __device__ constexpr int fmt_gs(int fmt) { return fmt == SIGN1 ? 4 * 64 + 16 : 4 * 32 + 16; }
 __host__ __device__ constexpr int fmt_word_k(int fmt) { return fmt == SIGN1 ? 32 : 16; }
+__host__ __device__ constexpr int fmt_gps(int fmt) { return fmt == SIGN1 ? 8 : 16; }   // groups per K-step
+constexpr int KSTEP = 1024;   // K per unit, both formats
 
 struct MfmaArgs {
   const void* x;
@@ -65,17 +69,19 @@ struct MfmaArgs {
   const uint16_t* biases;
   float* y;
   int M, K, N;
-  int win_steps;   // K-steps (of 4 groups) per staging window
+  int win_steps;   // K-steps (of KSTEP) per staging window
   int tiles_max;   // ytile capacity
   int a_pitch;     // LDS bytes per activation row in a window
+  uint32_t mask[6];   // code-extraction masks per bit position (see vg_device.h)
+  uint32_t magic[6];  // fp16 magic pairs per bit position
 };
 
 // LDS carve-up (byte offsets), computed identically on host and device.
 struct LdsLayout {
   int a_off, e_off, x_off, ytile_off, slot_off, row_off, total;
   __host__ __device__ LdsLayout(int fmt, int M, int win_steps, int tiles_max) {
-    const int groups = win_steps * 4;
-    const int pitch = groups * fmt_gs(fmt) + 16;
+    const int groups = win_steps * fmt_gps(fmt);
+    const int pitch = groups * fmt_gs(fmt) + 16;   // must equal MfmaArgs::a_pitch
     a_off = 0;
     e_off = a_off + M * pitch;
     x_off = e_off + groups * MAXM * 4;
@@ -268,112 +274,163 @@ __device__ void stage_window(const MfmaArgs& A, char* smem, const LdsLayout& L, 
 }
 
 // ---------------------------------------------------------------------------------------
-struct Unit {
-  u32x4 w;          // one quantization group (16 bytes) of this lane's row
-  uint32_t sb[2];   // fp16 scale | fp16 bias << 16, for the lane's group(s)
+// Loaded data of one unit for one lane: GL consecutive 16-byte groups of the lane's row
+// and their fp16 scales (and biases) as packed pairs.  Nothing consumes a load where it
+// is issued, so the loads of later units stay in flight.
+template <int FMT> struct Unit {
+  u32x4 w[Fmt<FMT>::GL];
+  uint32_t s[Fmt<FMT>::GL / 2];
+  uint32_t b[Fmt<FMT>::GL / 2];
 };
 
-template <int FMT, int MODE>
-__device__ __forceinline__ void load_unit(const MfmaArgs& A, int r0, int r1, int ws0, int ns,
-                                          int u, int g, int i, Unit& U) {
-  constexpr int WORD_K = Fmt<FMT>::WORD_K, G = Fmt<FMT>::G;
-  const int t = u / ns, s = ws0 + (u - t * ns);
-  const int row = r0 + 16 * t + i;
-  if (row < r1) {
-    const size_t wpr = (size_t)A.K / WORD_K, gpr = (size_t)A.K / G;
-    U.w = *reinterpret_cast<const u32x4*>(A.w + row * wpr + (size_t)s * 16 + g * 4);
-    const size_t sbase = row * gpr + (size_t)s * 4;
-    if constexpr (MODE == VAR_MFMA_Q) {
-      const size_t gi = sbase + g;
-      U.sb[0] = A.scales[gi] | (Fmt<FMT>::AFFINE ? (uint32_t)A.biases[gi] << 16 : 0u);
-    } else {
+__device__ __forceinline__ float half_of(uint32_t pair, int hi) {
+  return (float)__builtin_bit_cast(f16x2, pair)[hi];
+}
+
+// Code extraction with the masks and magics held in registers (one v_and_or_b32 per
+// operand register; as literals the compiler would split it into an AND and an OR).
+template <int FMT>
+__device__ __forceinline__ void unpack_word_rt(uint32_t w, uint32_t* out, const uint32_t* mk, const uint32_t* mg) {
+  if constexpr (FMT == SIGN1) {
+    const uint32_t src[3] = {w, w << 5, w >> 6};
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
-        const size_t gi = sbase + 2 * (g >> 1) + uu;
-        U.sb[uu] = A.scales[gi] | (Fmt<FMT>::AFFINE ? (uint32_t)A.biases[gi] << 16 : 0u);
-      }
+    for (int b0 = 0; b0 < 16; ++b0) {
+      const int k = sign1_pos(b0) - 5;
+      out[b0] = (src[sign1_src(b0)] & mk[k]) | mg[k];
+    }
+  } else {
+    const uint32_t src[3] = {w, w << 6, w >> 6};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = (affine2_pos(j) - 4) >> 1;
+      out[j] = (src[affine2_src(j)] & mk[k]) | mg[k];
     }
   }
 }
 
-// One unit: decode the lane's codes and accumulate every drafted row's group sums.
-template <int FMT, int MODE>
-__device__ __forceinline__ void compute_unit(const Unit& U, const char* smem, const LdsLayout& L,
-                                             int pitch, int sl, int g, int i, int M, float yacc[4]) {
+// One quantization group of one lane: 4 words -> 4*NQ MFMAs into two accumulators (two
+// chains halve the dependent-MFMA latency), then the group's fp32 scale/bias epilogue.
+//   words: the 4 (mode Q) or 2+2 (mode H, two slot-halves) operand words
+//   a_off: LDS byte address of the lane's operand window for this group
+template <int FMT>
+__device__ __forceinline__ void group_mfma(const uint32_t* words, const char* smem, uint32_t a_off, bool av,
+                                           f16x8* a, const uint32_t* mk, const uint32_t* mg, f32x4& acc0,
+                                           f32x4& acc1) {
   using F = Fmt<FMT>;
-  const float* E = reinterpret_cast<const float*>(smem + L.e_off);
-  const float* X = reinterpret_cast<const float*>(smem + L.x_off);
-  if constexpr (MODE == VAR_MFMA_Q) {
-    const int m = i - 4 * g;
-    const bool av = m >= 0 && m < M && m < 4;
-    const int gl = sl * 4 + g;
-    const char* abase = smem + L.a_off + (av ? m : 0) * pitch + gl * F::GS;
-    f32x4 acc = *reinterpret_cast<const f32x4*>(E + gl * MAXM);
+  constexpr int NA = 4 * F::NQ;
+  if (av) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t pr[F::PAIRS];
-      if constexpr (FMT == SIGN1) unpack_sign1_word(U.w[w], pr); else unpack_affine2_word(U.w[w], pr);
+    for (int k = 0; k < NA; ++k)
+      a[k] = *reinterpret_cast<const f16x8*>(smem + a_off + (k / F::NQ) * F::WB + 16 * (k % F::NQ));
+  }
 #pragma unroll
-      for (int q = 0; q < F::NQ; ++q) {
-        const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pr[4 * q], pr[4 * q + 1], pr[4 * q + 2], pr[4 * q + 3]});
-        f16x8 a = {};
-        if (av) a = *reinterpret_cast<const f16x8*>(abase + w * F::WB + 16 * q);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-      }
+  for (int w = 0; w < 4; ++w) {
+    uint32_t pr[F::PAIRS];
+    unpack_word_rt<FMT>(words[w], pr, mk, mg);
+#pragma unroll
+    for (int q = 0; q < F::NQ; ++q) {
+      const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pr[4 * q], pr[4 * q + 1], pr[4 * q + 2], pr[4 * q + 3]});
+      const int k = w * F::NQ + q;
+      if (k & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[k], b, acc1, 0, 0, 0);
+      else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[k], b, acc0, 0, 0, 0);
     }
-    const float s = f16_to_f32(U.sb[0] & 0xFFFFu);
-    if constexpr (F::AFFINE) {
-      const float bb = f16_to_f32(U.sb[0] >> 16);
-      const f32x4 xs = *reinterpret_cast<const f32x4*>(X + gl * MAXM);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void group_epilogue(const char* smem, uint32_t e_off, uint32_t x_delta, float s,
+                                               float bb, const f32x4& acc0, const f32x4& acc1, float yacc[4]) {
+  if constexpr (Fmt<FMT>::AFFINE) {
+    const f32x4 xs = *reinterpret_cast<const f32x4*>(smem + e_off + x_delta);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc[r], __builtin_fmaf(bb, xs[r], yacc[r]));
-    } else {
+    for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc0[r] + acc1[r], __builtin_fmaf(bb, xs[r], yacc[r]));
+  } else {
+    (void)bb;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc[r], yacc[r]);
+    for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc0[r] + acc1[r], yacc[r]);
+  }
+}
+
+// One unit: decode the lane's GL groups and accumulate every drafted row's group sums.
+//   a_lane: LDS byte address of the operand window of the lane's first group at this step
+//   e_lane: LDS byte address of the correction sums of that group for the lane's rows
+// Mode Q: lane-group g owns groups GL*g + h.  Mode H: lane-group pair p = g/2 shares
+// groups (2p + u)*GL + h, u = slot-half, after a permlane16 swap of two words per group.
+template <int FMT, int MODE>
+__device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* smem, uint32_t a_lane, uint32_t e_lane,
+                                             uint32_t x_delta, bool av, f16x8* a, const uint32_t* mk,
+                                             const uint32_t* mg, float yacc[4]) {
+  using F = Fmt<FMT>;
+  constexpr int GL = F::GL;
+  if constexpr (MODE == VAR_MFMA_Q) {
+#pragma unroll
+    for (int h = 0; h < GL; ++h) {
+      f32x4 acc0 = *reinterpret_cast<const f32x4*>(smem + e_lane + h * (MAXM * 4));
+      f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
+      const uint32_t words[4] = {U.w[h][0], U.w[h][1], U.w[h][2], U.w[h][3]};
+      group_mfma<FMT>(words, smem, a_lane + h * F::GS, av, a, mk, mg, acc0, acc1);
+      const float s = half_of(U.s[h >> 1], h & 1);
+      const float bb = F::AFFINE ? half_of(U.b[h >> 1], h & 1) : 0.0f;
+      group_epilogue<FMT>(smem, e_lane + h * (MAXM * 4), x_delta, s, bb, acc0, acc1, yacc);
     }
   } else {
-    // lane-group pairs (0,1) and (2,3) share a group: exchange words 2,3 of the even
-    // lane-group with words 0,1 of the odd one.
-    const auto s02 = __builtin_amdgcn_permlane16_swap(U.w[0], U.w[2], false, false);
-    const auto s13 = __builtin_amdgcn_permlane16_swap(U.w[1], U.w[3], false, false);
-    const uint32_t W[4] = {s02[0], s13[0], s02[1], s13[1]};
-    const int m = (g < 2) ? i : i - 8;
-    const bool av = m >= 0 && m < M;
-    const int m0 = 4 * (g & 1);
+    // scales: the swap of a register with itself hands lane-group pair p the pairs of both
+    // lane-groups 2p ([0]) and 2p+1 ([1])
+    uint32_t sc[2][GL / 2], bs[2][GL / 2];
 #pragma unroll
-    for (int uu = 0; uu < 2; ++uu) {
-      const int gl = sl * 4 + 2 * (g >> 1) + uu;
-      const char* abase = smem + L.a_off + (av ? m : 0) * pitch + gl * F::GS + 2 * (g & 1) * F::WB;
-      f32x4 acc = *reinterpret_cast<const f32x4*>(E + gl * MAXM + m0);
-#pragma unroll
-      for (int wl = 0; wl < 2; ++wl) {
-        uint32_t pr[F::PAIRS];
-        if constexpr (FMT == SIGN1) unpack_sign1_word(W[2 * uu + wl], pr); else unpack_affine2_word(W[2 * uu + wl], pr);
-#pragma unroll
-        for (int q = 0; q < F::NQ; ++q) {
-          const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pr[4 * q], pr[4 * q + 1], pr[4 * q + 2], pr[4 * q + 3]});
-          f16x8 a = {};
-          if (av) a = *reinterpret_cast<const f16x8*>(abase + wl * F::WB + 16 * q);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
-        }
-      }
-      const float s = f16_to_f32(U.sb[uu] & 0xFFFFu);
+    for (int d = 0; d < GL / 2; ++d) {
+      const auto t = __builtin_amdgcn_permlane16_swap(U.s[d], U.s[d], false, false);
+      sc[0][d] = t[0];
+      sc[1][d] = t[1];
       if constexpr (F::AFFINE) {
-        const float bb = f16_to_f32(U.sb[uu] >> 16);
-        const f32x4 xs = *reinterpret_cast<const f32x4*>(X + gl * MAXM + m0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc[r], __builtin_fmaf(bb, xs[r], yacc[r]));
+        const auto tb = __builtin_amdgcn_permlane16_swap(U.b[d], U.b[d], false, false);
+        bs[0][d] = tb[0];
+        bs[1][d] = tb[1];
       } else {
+        bs[0][d] = bs[1][d] = 0u;
+      }
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc[r], yacc[r]);
+    for (int h = 0; h < GL; ++h) {
+      // exchange words 2,3 of the even lane-group with words 0,1 of the odd one
+      const auto s02 = __builtin_amdgcn_permlane16_swap(U.w[h][0], U.w[h][2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane16_swap(U.w[h][1], U.w[h][3], false, false);
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const uint32_t words[4] = {uu == 0 ? s02[0] : s02[1], uu == 0 ? s13[0] : s13[1], 0u, 0u};
+        f32x4 acc0 = *reinterpret_cast<const f32x4*>(smem + e_lane + (uu * GL + h) * (MAXM * 4));
+        f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
+        const uint32_t a_off = a_lane + (uu * GL + h) * F::GS;
+        // two words per slot-half: operands k = wl*NQ + q
+        if (av) {
+#pragma unroll
+          for (int k = 0; k < 2 * F::NQ; ++k)
+            a[k] = *reinterpret_cast<const f16x8*>(smem + a_off + (k / F::NQ) * F::WB + 16 * (k % F::NQ));
+        }
+#pragma unroll
+        for (int wl = 0; wl < 2; ++wl) {
+          uint32_t pr[F::PAIRS];
+          unpack_word_rt<FMT>(words[wl], pr, mk, mg);
+#pragma unroll
+          for (int q = 0; q < F::NQ; ++q) {
+            const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pr[4 * q], pr[4 * q + 1], pr[4 * q + 2], pr[4 * q + 3]});
+            const int k = wl * F::NQ + q;
+            if (k & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[k], b, acc1, 0, 0, 0);
+            else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[k], b, acc0, 0, 0, 0);
+          }
+        }
+        const float s = half_of(sc[uu][h >> 1], h & 1);
+        const float bb = F::AFFINE ? half_of(bs[uu][h >> 1], h & 1) : 0.0f;
+        group_epilogue<FMT>(smem, e_lane + (uu * GL + h) * (MAXM * 4), x_delta, s, bb, acc0, acc1, yacc);
       }
     }
   }
 }
 
 // Finishes a wave's contribution to tile t for the current window: undo the row scaling,
-// sum the lane-groups holding the same rows, then either add into the tile accumulator
-// (sole contributor) or park it in the wave's slot for the fixed-order reduction.
+// sum the lane-groups holding the same rows (register swaps between lane rows), then
+// either add into the tile accumulator (sole contributor) or park it in the wave's slot
+// for the fixed-order reduction.
 template <int FMT, int MODE>
 __device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t, bool sole, int slot,
                                            int wid, int g, int i, float yacc[4]) {
@@ -381,13 +438,14 @@ __device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t
   const int m0 = MODE == VAR_MFMA_Q ? 0 : 4 * (g & 1);
   float v[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = yacc[r] * invf[m0 + r];
-  if constexpr (MODE == VAR_MFMA_Q) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) { v[r] += __shfl_xor(v[r], 16); v[r] += __shfl_xor(v[r], 32); }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] += __shfl_xor(v[r], 32);
+  for (int r = 0; r < 4; ++r) {
+    v[r] = yacc[r] * invf[m0 + r];
+    if constexpr (MODE == VAR_MFMA_Q) {
+      const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[r]), __float_as_uint(v[r]), false, false);
+      v[r] = __uint_as_float(p[0]) + __uint_as_float(p[1]);   // rows 0+1 and 2+3
+    }
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[r]), __float_as_uint(v[r]), false, false);
+    v[r] = __uint_as_float(h[0]) + __uint_as_float(h[1]);     // lanes l and l^32
   }
   const bool writer = MODE == VAR_MFMA_Q ? (g == 0) : (g < 2);
   if (writer) {
@@ -404,60 +462,122 @@ __device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t
 template <int FMT, int MODE, int XT>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
-  constexpr int KSTEP = 4 * F::G;
+  constexpr int GL = F::GL, PREF = F::PREF, GPS = 4 * GL;
+  constexpr int NA = 4 * F::NQ;
   constexpr bool NORM = FMT == HAD2 || XT == XBF16;
   const LdsLayout L(FMT, A.M, A.win_steps, A.tiles_max);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
   const int P = gridDim.x, b = blockIdx.x;
   const int r0 = (int)(((long long)A.N * b) / P), r1 = (int)(((long long)A.N * (b + 1)) / P);
   const int T = (r1 - r0 + 15) / 16;
   const int S = A.K / KSTEP;
+  const uint32_t wrow = (uint32_t)(A.K / F::WORD_K) * 4u;   // bytes of codes per row
+  const uint32_t srow = (uint32_t)(A.K / F::G) * 2u;        // bytes of scales per row
+  // masks stay in SGPRs, magics are moved into VGPRs once: v_and_or_b32 may read only one
+  // scalar operand, and with both scalar the compiler would emit a separate AND and OR.
+  uint32_t mk[6], mg[6];
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    mk[k] = A.mask[k];
+    asm volatile("v_mov_b32 %0, %1" : "=v"(mg[k]) : "s"(A.magic[k]));
+  }
+
+  // this lane's operand row and whether it carries a drafted row (others stay zero)
+  const int am = MODE == VAR_MFMA_Q ? i - 4 * g : (g < 2 ? i : i - 8);
+  const bool av = am >= 0 && am < A.M && (MODE == VAR_MFMA_H || am < 4);
+  const int m0 = MODE == VAR_MFMA_Q ? 0 : 4 * (g & 1);
+  const uint32_t a_lane0 = L.a_off + (uint32_t)(av ? am : 0) * A.a_pitch +
+                           (MODE == VAR_MFMA_Q ? GL * g * F::GS : 2 * (g >> 1) * GL * F::GS + 2 * (g & 1) * F::WB);
+  const uint32_t e_lane0 = L.e_off + ((MODE == VAR_MFMA_Q ? GL * g : 2 * (g >> 1) * GL) * MAXM + m0) * 4;
+  const uint32_t x_delta = L.x_off - L.e_off;
+  f16x8 a[NA];
+#pragma unroll
+  for (int k = 0; k < NA; ++k) a[k] = f16x8{};
 
   float* ytile = reinterpret_cast<float*>(smem + L.ytile_off);
   for (int e = tid; e < T * MAXM * 16; e += NTHREADS) ytile[e] = 0.0f;
   if (!NORM && tid < MAXM) reinterpret_cast<float*>(smem + L.row_off)[MAXM + tid] = 1.0f;
 
+  const char* wbase = reinterpret_cast<const char*>(A.w) + (size_t)r0 * wrow;
+  const char* sbase = reinterpret_cast<const char*>(A.scales) + (size_t)r0 * srow;
+  const char* bbase = reinterpret_cast<const char*>(A.biases) + (size_t)r0 * srow;
+
   for (int ws0 = 0; ws0 < S; ws0 += A.win_steps) {
     const int ns = min(A.win_steps, S - ws0);
     const int UW = T * ns;
     const int ua = (int)(((long long)UW * wid) / NW), ub = (int)(((long long)UW * (wid + 1)) / NW);
+    const int nu = ub - ua;
 
-    // first units' loads go out before the staging so they overlap it
-    Unit ring[PREF];
+    // Load cursor (tile lt, step ls), kept uniform; the lane part of a load address is a
+    // per-tile constant, the rest is a scalar offset.  Loads past the wave's last unit
+    // repeat the last unit, so every ring slot is reloaded unconditionally and the loads
+    // of later units stay in flight while earlier ones compute.
+    int lt = nu > 0 ? ua / ns : 0, ls = nu > 0 ? ua - lt * ns : 0, issued = 0;
+    uint32_t lw_lane = 0, ls_lane = 0;
+    auto set_load_tile = [&](int t) {
+      const int rr = min(16 * t + i, r1 - 1 - r0) - 16 * t;   // clamp rows past the range
+      lw_lane = (uint32_t)rr * wrow + (uint32_t)(g * GL) * 16u;
+      ls_lane = (uint32_t)rr * srow + (uint32_t)(g * GL) * 2u;
+    };
+    set_load_tile(lt);
+    auto issue = [&](Unit<FMT>& U) {
+      const size_t tw = (size_t)(16 * lt) * wrow + (size_t)(ws0 + ls) * (GPS * 16);
+      const size_t ts = (size_t)(16 * lt) * srow + (size_t)(ws0 + ls) * (GPS * 2);
+      const char* wp = wbase + tw + lw_lane;
 #pragma unroll
-    for (int d = 0; d < PREF; ++d)
-      if (ua + d < ub) load_unit<FMT, MODE>(A, r0, r1, ws0, ns, ua + d, g, i, ring[d]);
+      for (int h = 0; h < GL; ++h) U.w[h] = *reinterpret_cast<const u32x4*>(wp + 16 * h);
+      if constexpr (GL == 2) {
+        U.s[0] = *reinterpret_cast<const uint32_t*>(sbase + ts + ls_lane);
+        if constexpr (F::AFFINE) U.b[0] = *reinterpret_cast<const uint32_t*>(bbase + ts + ls_lane);
+      } else {
+        const uint2 sv = *reinterpret_cast<const uint2*>(sbase + ts + ls_lane);
+        U.s[0] = sv.x;
+        U.s[1] = sv.y;
+        if constexpr (F::AFFINE) {
+          const uint2 bv = *reinterpret_cast<const uint2*>(bbase + ts + ls_lane);
+          U.b[0] = bv.x;
+          U.b[1] = bv.y;
+        }
+      }
+      if (issued + 1 < nu) {
+        ++issued;
+        if (++ls == ns) { ls = 0; ++lt; set_load_tile(lt); }
+      }
+    };
+
+    // the first units' loads go out before the staging so they overlap it
+    Unit<FMT> ring[PREF];
+    if (nu > 0) {
+#pragma unroll
+      for (int d = 0; d < PREF; ++d) issue(ring[d]);
+    }
 
     __syncthreads();  // previous window's readers are done with the LDS
     stage_window<FMT, XT>(A, smem, L, ws0 * KSTEP, ns * KSTEP);
     __syncthreads();
 
-    int cur = -1;
+    int ct = nu > 0 ? ua / ns : 0, cs = nu > 0 ? ua - ct * ns : 0;
     float yacc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int base = ua; base < ub; base += PREF) {
+    for (int base = 0; base < nu; base += PREF) {
 #pragma unroll
       for (int d = 0; d < PREF; ++d) {
-        const int u = base + d;
-        if (u < ub) {
-          const int t = u / ns, sl = u - t * ns;
-          if (t != cur) {
-            if (cur >= 0) {
-              const bool sole = ua <= cur * ns && ub >= (cur + 1) * ns;
-              flush_tile<FMT, MODE>(smem, L, cur, sole, cur == ua / ns ? 0 : 1, wid, g, i, yacc);
-            }
-            cur = t;
+        if (base + d < nu) {
+          const uint32_t a_lane = a_lane0 + (uint32_t)cs * (GPS * F::GS);
+          const uint32_t e_lane = e_lane0 + (uint32_t)cs * (GPS * MAXM * 4);
+          compute_unit<FMT, MODE>(ring[d], smem, a_lane, e_lane, x_delta, av, a, mk, mg, yacc);
+          if (++cs == ns || base + d + 1 == nu) {
+            const bool sole = ua <= ct * ns && ub >= (ct + 1) * ns;
+            flush_tile<FMT, MODE>(smem, L, ct, sole, ct == ua / ns ? 0 : 1, wid, g, i, yacc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) yacc[r] = 0.f;
+            cs = 0;
+            ++ct;
           }
-          compute_unit<FMT, MODE>(ring[d], smem, L, A.a_pitch, sl, g, i, A.M, yacc);
-          if (u + PREF < ub) load_unit<FMT, MODE>(A, r0, r1, ws0, ns, u + PREF, g, i, ring[d]);
         }
+        issue(ring[d]);
       }
-    }
-    if (cur >= 0) {
-      const bool sole = ua <= cur * ns && ub >= (cur + 1) * ns;
-      flush_tile<FMT, MODE>(smem, L, cur, sole, cur == ua / ns ? 0 : 1, wid, g, i, yacc);
     }
     __syncthreads();
 
@@ -516,8 +636,7 @@ static int pick_grid(int N, const DeviceInfo& dev) {
 
 size_t mfma_lds_bytes(int fmt, int variant, int M, int K, int N, int grid, int max_lds, int* win_steps) {
   (void)variant;
-  const int kstep = 4 * fmt_group(fmt);
-  const int S = K / kstep;
+  const int S = K / KSTEP;
   const int rows_max = (N + grid - 1) / grid + 1;
   const int tiles_max = (rows_max + 15) / 16 + 1;
   // largest window that fits, then balanced so windows have equal step counts
@@ -545,7 +664,18 @@ static hipError_t launch_one(const GemmCall& c, const DeviceInfo& dev) {
   A.win_steps = ws;
   const int rows_max = (c.N + grid - 1) / grid + 1;
   A.tiles_max = (rows_max + 15) / 16 + 1;
-  A.a_pitch = ws * 4 * fmt_gs(FMT) + 16;
+  A.a_pitch = ws * fmt_gps(FMT) * fmt_gs(FMT) + 16;
+  for (int k = 0; k < 6; ++k) {
+    if (FMT == SIGN1) {
+      const int p = 5 + k;   // positions 5..10
+      A.mask[k] = (1u << p) | (1u << (p + 16));
+      A.magic[k] = half_magic_sign1(p) | (half_magic_sign1(p) << 16);
+    } else {
+      const int p = 4 + 2 * (k < 3 ? k : 2);   // positions 4, 6, 8
+      A.mask[k] = (3u << p) | (3u << (p + 16));
+      A.magic[k] = half_magic_affine2(p) | (half_magic_affine2(p) << 16);
+    }
+  }
   void (*kern)(MfmaArgs) = MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT> : vg_mfma_h<FMT, XT>;
   static bool attr_set = false;
   if (!attr_set) {
