@@ -9,11 +9,15 @@
 // Work decomposition (MFMA variants)
 //   * One workgroup (8 waves) per CU owns a contiguous, balanced range of output rows;
 //     rows are grouped in tiles of 16 (the MFMA N dimension).  A "unit" is one tile times
-//     one K-step of 4 quantization groups; a wave loads one 16-byte group per lane per
-//     unit (16 rows x 64 bytes), i.e. 1 KB of packed codes per wave instruction.
-//   * K is processed in windows.  Per window the workgroup stages its activations into
-//     LDS once, already in the operand layout the unpacked codes need (and rotated, for
-//     the Hadamard format), together with per-(group, row) correction sums.  The
+//     one K-step of 1024 (8 sign groups or 16 affine groups).  Per unit each lane loads
+//     GL consecutive groups of one row in single wide loads (codes, then the scales and
+//     biases of those groups), so a row's unit is fetched by 4 lanes as 256 contiguous
+//     bytes of codes.  Every wave keeps PREF units in flight in a register ring.
+//   * K is processed in windows.  Per window the workgroup first stages its activations
+//     into LDS, already in the operand layout the unpacked codes need (and rotated, for
+//     the Hadamard format), together with per-(group, row) correction sums; only then are
+//     the window's weight loads issued, since loads leave a CU in order and a burst of
+//     weight loads ahead of the activations would delay every MFMA behind it.  The
 //     window's units are split evenly across the 8 waves in tile-major order; partial
 //     tiles are reduced through LDS in a fixed order, so results are deterministic.
 //   * MFMA rows: the 16 A rows are split into independent row-blocks, each fed only by
@@ -162,8 +166,46 @@ __device__ __forceinline__ void load_x32_f32(const void* x, int K, int m, int k0
 //   2-bit:  R = sum_k a_k * BETA_k (stored negated),  X = sum_k a_k
 // The activations a are x * f (f a per-row power of two chosen so the fp16 values cannot
 // overflow; f = 1 for fp16 input without rotation), rotated first for the Hadamard format.
+// The staging is split in two so the activation loads can be issued before a wave's
+// weight prefetch: loads enter the memory pipeline in order, and staged behind the weight
+// burst they would delay every workgroup's first MFMA by that whole burst.
+constexpr int MAXT = 3;   // activation chunks (32 K of one row) per thread and window
+struct XStage {
+  u32x4 d[MAXT][4];       // raw fp16/bf16 bits of 32 consecutive activations
+};
+
+template <int XT>
+__device__ __forceinline__ void stage_load(const MfmaArgs& A, int k0, int WK, XStage& xs) {
+  const int nchunks = WK / 32, ntask = A.M * nchunks;
+#pragma unroll
+  for (int j = 0; j < MAXT; ++j) {
+    const int t = threadIdx.x + j * NTHREADS;
+    if (t < ntask) {
+      const int m = t / nchunks, c = t - m * nchunks;
+      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.x) + (size_t)m * A.K + k0 + 32 * c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xs.d[j][q] = p[q];
+    }
+  }
+}
+
+__device__ __forceinline__ void chunk_halves(const XStage& xs, int j, uint32_t hv[32]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hv[8 * q + 2 * i] = xs.d[j][q][i] & 0xFFFFu;
+      hv[8 * q + 2 * i + 1] = xs.d[j][q][i] >> 16;
+    }
+}
+
+template <int XT>
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
+  return XT == XBF16 ? bf16_to_f32(h) : f16_to_f32(h);
+}
+
 template <int FMT, int XT>
-__device__ void stage_window(const MfmaArgs& A, char* smem, const LdsLayout& L, int k0, int WK) {
+__device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L, int WK, const XStage& xs) {
   using F = Fmt<FMT>;
   constexpr bool HAD = FMT == HAD2;
   constexpr bool NORM = HAD || XT == XBF16;
@@ -178,14 +220,17 @@ __device__ void stage_window(const MfmaArgs& A, char* smem, const LdsLayout& L, 
   if constexpr (NORM) {
     if (tid < MAXM) rowmax[tid] = 0u;
     __syncthreads();
-    for (int t = tid; t < ntask; t += NTHREADS) {
-      const int m = t / nchunks, c = t - m * nchunks;
-      float v[32];
-      load_x32_f32<XT>(A.x, A.K, m, k0 + 32 * c, v);
-      float mx = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(v[e]));
-      atomicMax(&rowmax[m], __float_as_uint(mx));
+    for (int j = 0; j < MAXT; ++j) {
+      const int t = tid + j * NTHREADS;
+      if (t < ntask) {
+        uint32_t hv[32];
+        chunk_halves(xs, j, hv);
+        float mx = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(half_bits_to_f32<XT>(hv[e])));
+        atomicMax(&rowmax[t / nchunks], __float_as_uint(mx));
+      }
     }
     __syncthreads();
     if (tid < MAXM) {
@@ -204,23 +249,17 @@ __device__ void stage_window(const MfmaArgs& A, char* smem, const LdsLayout& L, 
     __syncthreads();
   }
 
-  for (int t = tid; t < ntask; t += NTHREADS) {
+#pragma unroll
+  for (int j = 0; j < MAXT; ++j) {
+    const int t = tid + j * NTHREADS;
+    if (t >= ntask) continue;   // whole quads skip together (ntask and NTHREADS are multiples of 4)
     const int m = t / nchunks, c = t - m * nchunks;
     uint32_t hv[32];  // fp16 bits, natural K order within the chunk
-    if constexpr (!NORM) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.x) + (size_t)m * A.K + k0 + 32 * c);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4 d = p[q];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hv[8 * q + 2 * i] = d[i] & 0xFFFFu;
-          hv[8 * q + 2 * i + 1] = d[i] >> 16;
-        }
-      }
-    } else {
+    chunk_halves(xs, j, hv);
+    if constexpr (NORM) {
       float v[32];
-      load_x32_f32<XT>(A.x, A.K, m, k0 + 32 * c, v);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) v[e] = half_bits_to_f32<XT>(hv[e]);
       float scale = rowf[m];
       if constexpr (HAD) scale *= fwht128_quad(v, c & 3) * 0.08838834764831845f;  // 1/sqrt(128)
 #pragma unroll
@@ -247,27 +286,27 @@ __device__ void stage_window(const MfmaArgs& A, char* smem, const LdsLayout& L, 
       if ((c & 3) == 0) reinterpret_cast<float*>(smem + L.e_off)[(c >> 2) * MAXM + m] = -e;
     } else {
       // chunk = two word windows (16 K each) = words 2(c%2), 2(c%2)+1 of group c/2
-      float r = 0.0f, xs = 0.0f;
+      float r = 0.0f, xsum = 0.0f;
 #pragma unroll
       for (int ww = 0; ww < 2; ++ww) {
         uint32_t pd[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pd[j] = hv[16 * ww + j] | (hv[16 * ww + j + 8] << 16);
-          const _Float16 bj = (_Float16)affine2_beta(j);
-          const f16x2 ph = __builtin_bit_cast(f16x2, pd[j]);
+        for (int jj = 0; jj < 8; ++jj) {
+          pd[jj] = hv[16 * ww + jj] | (hv[16 * ww + jj + 8] << 16);
+          const _Float16 bj = (_Float16)affine2_beta(jj);
+          const f16x2 ph = __builtin_bit_cast(f16x2, pd[jj]);
           r = __builtin_amdgcn_fdot2(ph, f16x2{bj, bj}, r, false);
-          xs = __builtin_amdgcn_fdot2(ph, f16x2{(_Float16)1.0f, (_Float16)1.0f}, xs, false);
+          xsum = __builtin_amdgcn_fdot2(ph, f16x2{(_Float16)1.0f, (_Float16)1.0f}, xsum, false);
         }
         u32x4* dst = reinterpret_cast<u32x4*>(arow + (c >> 1) * F::GS + (2 * (c & 1) + ww) * F::WB);
         dst[0] = u32x4{pd[0], pd[1], pd[2], pd[3]};
         dst[1] = u32x4{pd[4], pd[5], pd[6], pd[7]};
       }
       r += __shfl_xor(r, 1);
-      xs += __shfl_xor(xs, 1);
+      xsum += __shfl_xor(xsum, 1);
       if ((c & 1) == 0) {
         reinterpret_cast<float*>(smem + L.e_off)[(c >> 1) * MAXM + m] = -r;
-        reinterpret_cast<float*>(smem + L.x_off)[(c >> 1) * MAXM + m] = xs;
+        reinterpret_cast<float*>(smem + L.x_off)[(c >> 1) * MAXM + m] = xsum;
       }
     }
   }
@@ -547,15 +586,18 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       }
     };
 
-    // the first units' loads go out before the staging so they overlap it
+    // Activations are staged before any weight load is issued: loads leave a CU in order
+    // and a wave stalls at issue once the memory queues are full, so weight loads issued
+    // first would hold back the staging (and every MFMA after it) by the whole burst.
+    XStage xs;
+    stage_load<XT>(A, ws0 * KSTEP, ns * KSTEP, xs);
+    __syncthreads();  // previous window's readers are done with the LDS
+    stage_compute<FMT, XT>(A, smem, L, ns * KSTEP, xs);
     Unit<FMT> ring[PREF];
     if (nu > 0) {
 #pragma unroll
       for (int d = 0; d < PREF; ++d) issue(ring[d]);
     }
-
-    __syncthreads();  // previous window's readers are done with the LDS
-    stage_window<FMT, XT>(A, smem, L, ws0 * KSTEP, ns * KSTEP);
     __syncthreads();
 
     int ct = nu > 0 ? ua / ns : 0, cs = nu > 0 ? ua - ct * ns : 0;
@@ -641,7 +683,9 @@ size_t mfma_lds_bytes(int fmt, int variant, int M, int K, int N, int grid, int m
   const int tiles_max = (rows_max + 15) / 16 + 1;
   // largest window that fits, then balanced so windows have equal step counts
   int best = 0;
-  for (int ws = S; ws >= 1; --ws) {
+  // at most MAXT activation chunks of 32 K per thread: M * ws * KSTEP / 32 <= NTHREADS * MAXT
+  const int ws_cap = (NTHREADS * MAXT * 32) / (M * KSTEP);
+  for (int ws = S < ws_cap ? S : ws_cap; ws >= 1; --ws) {
     const LdsLayout L(fmt, M, ws, tiles_max);
     if (L.total <= max_lds) { best = ws; break; }
   }

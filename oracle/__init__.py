@@ -5,7 +5,7 @@ import this package.  The HIP product path never calls it and shares no code wit
 """
 from .verify_ref import (  # noqa: F401
     activations, argmax_rows, decode_bf16, decode_f16, dequant_affine2, dequant_sign1,
-    hadamard_rotate, normwise_rel_err, pack_affine2, pack_sign1, sylvester_hadamard,
+    hadamard_rotate, magnitude_columns, normwise_rel_err, pack_affine2, pack_sign1, sylvester_hadamard,
     unpack_affine2, unpack_sign1, verify, verify_affine2, verify_columns, verify_had2,
     verify_sign1,
 )

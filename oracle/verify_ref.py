@@ -201,6 +201,29 @@ def verify(fmt: str, x, x_dtype, words, scales, biases=None) -> np.ndarray:
     raise ValueError(f"unknown format {fmt!r}")
 
 
+def magnitude_columns(fmt: str, x: np.ndarray, x_dtype: str, words: np.ndarray,
+                      scales: np.ndarray, biases: np.ndarray | None, cols=None) -> np.ndarray:
+    """mag[m, n] = sum_k |a[m, k]| * |w[n, k]|, the sum of the magnitudes of the terms of
+    y[m, n] (a = the activations, rotated for had2; w = the dequantized weights), for the
+    columns `cols` (all if None).  Bounds how far any summation order and any rounding of
+    the individual terms can move y: a relative rounding u of each term moves y by at
+    most u * mag."""
+    cols = np.arange(words.shape[0]) if cols is None else np.asarray(cols)
+    x64 = activations(x, x_dtype)
+    if fmt == "had2":
+        x64 = hadamard_rotate(x64, 128)
+    K = x64.shape[1]
+    w, s = words[cols], scales[cols]
+    if fmt == "sign1":
+        dense = lambda a, b: dequant_sign1(unpack_sign1(w[a:b], K), s[a:b])
+    elif fmt in ("affine2", "had2"):
+        bb = biases[cols]
+        dense = lambda a, b: dequant_affine2(unpack_affine2(w[a:b], K), s[a:b], bb[a:b])
+    else:
+        raise ValueError(f"unknown format {fmt!r}")
+    return _matmul_chunked(np.abs(x64), len(cols), lambda a, b: np.abs(dense(a, b)))
+
+
 # ----------------------------------------------------------------------------- head + checks
 def argmax_rows(y: np.ndarray):
     """Per-row argmax (first index on ties) and the gap between the top two values."""

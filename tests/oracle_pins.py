@@ -357,7 +357,45 @@ def pin_normwise(ref):
     assert ref.normwise_rel_err(yr, yr) == 0.0
 
 
+def pin_magnitude(ref):
+    """magnitude_columns = sum_k |a_k| |w_k|, by brute force with the independent bit-by-bit
+    decoder (and the independent transform for the rotated format); it dominates |y| and
+    equals y when every term is non-negative."""
+    rng = np.random.default_rng(14)
+    for fmt, x_dtype, M, K, N in (("sign1", "bf16", 2, 256, 3), ("affine2", "f16", 2, 128, 3),
+                                  ("had2", "f16", 2, 256, 2)):
+        words, s, b, x = _rand_case(rng, "sign1" if fmt == "sign1" else "affine2", M, K, N, x_dtype)
+        bb = None if fmt == "sign1" else b
+        mag = ref.magnitude_columns(fmt, x, x_dtype, words, s, bb)
+        y = ref.verify(fmt, x, x_dtype, words, s, bb)
+        assert mag.shape == y.shape and np.all(mag >= np.abs(y) * (1 - 1e-12))
+        conv = _bf16_fraction if x_dtype == "bf16" else _f16_fraction
+        for m in range(M):
+            a = [float(conv(int(v))) for v in x[m]]
+            if fmt == "had2":
+                a = list(_fwht(np.array(a).reshape(K // 128, 128)).reshape(K) / math.sqrt(128))
+            for n in range(N):
+                tot = 0.0
+                for k in range(K):
+                    if fmt == "sign1":
+                        w = float(_f16_fraction(int(s[n, k // 128])))
+                    else:
+                        code = (int(words[n, k // 16]) >> (2 * (k % 16))) & 3
+                        w = float(code * _f16_fraction(int(s[n, k // 64])) + _f16_fraction(int(b[n, k // 64])))
+                    tot += abs(a[k]) * abs(w)
+                assert abs(mag[m, n] - tot) <= 1e-12 * tot, (fmt, m, n, mag[m, n], tot)
+        cols = np.array([N - 1, 0])
+        assert _close(ref.magnitude_columns(fmt, x, x_dtype, words, s, bb, cols), mag[:, cols])
+    # all terms non-negative: positive activations, codes, scales and biases
+    words, s, b, x = _rand_case(rng, "affine2", 2, 128, 3, "f16")
+    x = x & np.uint16(0x7FFF)
+    b = s.copy()
+    assert _close(ref.magnitude_columns("affine2", x, "f16", words, s, b),
+                  ref.verify("affine2", x, "f16", words, s, b), rtol=1e-13, atol=0)
+
+
 ALL_PINS = [pin_decode, pin_unpack_hand_words, pin_pack_roundtrip, pin_golden,
             pin_sign1_closed_form, pin_affine2_known_codes, pin_rowsum_identity,
             pin_bruteforce_fraction, pin_hadamard_identities, pin_had2_weight_side,
-            pin_mlx_1bit_encoding, pin_argmax, pin_columns_and_chunks, pin_normwise]
+            pin_mlx_1bit_encoding, pin_argmax, pin_columns_and_chunks, pin_normwise,
+            pin_magnitude]

@@ -131,11 +131,36 @@ def _mut_normwise_elementwise(m):
     m.normwise_rel_err = normwise_rel_err
 
 
+def _mut_magnitude_signed_x(m):
+    def magnitude_columns(fmt, x, x_dtype, words, scales, biases, cols=None):
+        # forgets |a|: the signed activations leak into the bound
+        cols = np.arange(words.shape[0]) if cols is None else np.asarray(cols)
+        x64 = m.activations(x, x_dtype)
+        if fmt == "had2":
+            x64 = m.hadamard_rotate(x64, 128)
+        K = x64.shape[1]
+        if fmt == "sign1":
+            w = m.dequant_sign1(m.unpack_sign1(words[cols], K), scales[cols])
+        else:
+            w = m.dequant_affine2(m.unpack_affine2(words[cols], K), scales[cols], biases[cols])
+        return x64 @ np.abs(w).T
+    m.magnitude_columns = magnitude_columns
+
+
+def _mut_magnitude_unrotated(m):
+    orig = m.magnitude_columns
+
+    def magnitude_columns(fmt, x, x_dtype, words, scales, biases, cols=None):
+        return orig("affine2" if fmt == "had2" else fmt, x, x_dtype, words, scales, biases, cols)
+    m.magnitude_columns = magnitude_columns
+
+
 MUTATIONS = [_mut_sign1_msb_first, _mut_affine2_code_order, _mut_sign_polarity, _mut_drop_bias,
              _mut_sign1_group_size, _mut_affine2_group_index, _mut_hadamard_unnormalized,
              _mut_hadamard_wrong_recursion, _mut_hadamard_skipped, _mut_bf16_shift,
              _mut_f16_as_bf16, _mut_rows_reversed, _mut_chunk_offset, _mut_argmax_last_tie,
-             _mut_normwise_elementwise]
+             _mut_normwise_elementwise, _mut_magnitude_signed_x,
+             _mut_magnitude_unrotated]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__[5:])
