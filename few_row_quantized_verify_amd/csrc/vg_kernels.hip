@@ -64,6 +64,7 @@ __host__ __device__ constexpr int fmt_group(int fmt) { return fmt == SIGN1 ? 128
 __host__ __device__ constexpr int fmt_gs(int fmt) { return fmt == SIGN1 ? 4 * 64 + 16 : 4 * 32 + 16; }
 __host__ __device__ constexpr int fmt_word_k(int fmt) { return fmt == SIGN1 ? 32 : 16; }
 __host__ __device__ constexpr int fmt_gps(int fmt) { return fmt == SIGN1 ? 8 : 16; }   // groups per K-step
+__host__ __device__ constexpr int fmt_gl(int fmt) { return fmt == SIGN1 ? 2 : 4; }     // Fmt<>::GL
 constexpr int KSTEP = 1024;   // K per unit, both formats
 
 struct MfmaArgs {
@@ -81,15 +82,21 @@ struct MfmaArgs {
 };
 
 // LDS carve-up (byte offsets), computed identically on host and device.
+//   a:  activation operand rows 0..M-1 of the window, then row M, all zeros (read by the
+//       lanes whose operand row carries no drafted row)
+//   e:  fp32 per-(group, row) offset sums, the accumulators' initial values
+//   xp: 2-bit formats: per (row, lane-group quad of GL groups) the group sums / 64 as
+//       fp16 hi parts then lo parts (16 bytes), rows 0..M-1 and a zero row M
 struct LdsLayout {
-  int a_off, e_off, x_off, ytile_off, slot_off, row_off, total;
+  int a_off, e_off, xp_off, xp_pitch, ytile_off, slot_off, row_off, total;
   __host__ __device__ LdsLayout(int fmt, int M, int win_steps, int tiles_max) {
     const int groups = win_steps * fmt_gps(fmt);
     const int pitch = groups * fmt_gs(fmt) + 16;   // must equal MfmaArgs::a_pitch
     a_off = 0;
-    e_off = a_off + M * pitch;
-    x_off = e_off + groups * MAXM * 4;
-    ytile_off = x_off + (fmt == SIGN1 ? 0 : groups * MAXM * 4);
+    e_off = a_off + (M + 1) * pitch;
+    xp_off = e_off + groups * MAXM * 4;
+    xp_pitch = (groups / fmt_gl(fmt)) * 16 + 16;
+    ytile_off = xp_off + (fmt == SIGN1 ? 0 : (M + 1) * xp_pitch);
     slot_off = ytile_off + tiles_max * MAXM * 16 * 4;
     row_off = slot_off + NW * 2 * MAXM * 16 * 4;
     total = row_off + 2 * MAXM * 4;
@@ -135,6 +142,15 @@ __device__ __forceinline__ float fwht128_quad(float v[32], int quad_lane) {
 #pragma unroll
   for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c2, dpp_quad<0x4E>(v[e]), v[e]);
   return (((quad_lane & 1) ^ ((quad_lane >> 1) & 1)) != 0) ? -1.0f : 1.0f;
+}
+
+// Workgroup barrier for hand-offs through LDS.  The fences order LDS accesses only, so a
+// wave waits for its own LDS operations but not for its global loads: a __syncthreads
+// would also drain every weight load in flight and serialize the prefetch with it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Loads 32 consecutive activations of row m starting at k0 as fp32 (XT: F16 or BF16).
@@ -219,7 +235,7 @@ __device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L,
 
   if constexpr (NORM) {
     if (tid < MAXM) rowmax[tid] = 0u;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       const int t = tid + j * NTHREADS;
@@ -232,7 +248,7 @@ __device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L,
         atomicMax(&rowmax[t / nchunks], __float_as_uint(mx));
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < MAXM) {
       const float mx = __uint_as_float(rowmax[tid]);
       int ex = 0;
@@ -246,7 +262,7 @@ __device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L,
       rowf[tid] = f;
       rowf[MAXM + tid] = 1.0f / f;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
 #pragma unroll
@@ -305,8 +321,16 @@ __device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L,
       r += __shfl_xor(r, 1);
       xsum += __shfl_xor(xsum, 1);
       if ((c & 1) == 0) {
-        reinterpret_cast<float*>(smem + L.e_off)[(c >> 1) * MAXM + m] = -r;
-        reinterpret_cast<float*>(smem + L.x_off)[(c >> 1) * MAXM + m] = xsum;
+        const int grp = c >> 1;
+        reinterpret_cast<float*>(smem + L.e_off)[grp * MAXM + m] = -r;
+        // the group sum enters the bias product as an exact-enough fp16 pair: X/64 is
+        // bounded by the largest activation, so neither part can overflow
+        const float xm = xsum * 0.015625f;
+        const _Float16 hi = (_Float16)xm;
+        const _Float16 lo = (_Float16)(xm - (float)hi);
+        _Float16* xp = reinterpret_cast<_Float16*>(smem + L.xp_off + m * L.xp_pitch + (grp / F::GL) * 16);
+        xp[grp % F::GL] = hi;
+        xp[4 + grp % F::GL] = lo;
       }
     }
   }
@@ -347,122 +371,121 @@ __device__ __forceinline__ void unpack_word_rt(uint32_t w, uint32_t* out, const 
   }
 }
 
-// One quantization group of one lane: 4 words -> 4*NQ MFMAs into two accumulators (two
-// chains halve the dependent-MFMA latency), then the group's fp32 scale/bias epilogue.
-//   words: the 4 (mode Q) or 2+2 (mode H, two slot-halves) operand words
-//   a_off: LDS byte address of the lane's operand window for this group
+// One unit of one lane, as a pipeline over pairs of quantization groups.  The two groups
+// of a pair run as two independent MFMA chains (each accumulator holds one group's dot
+// products, so the group's scale applies once per accumulator); the A operands of the
+// next step are read from LDS while the current step's words are decoded and multiplied.
+//   Mode Q: lane-group g owns groups GL*g + h; pairs (h, h+1), 4 words each.
+//   Mode H: lane-group pair p = g/2 shares groups (2p + u)*GL + h (u = 0, 1); pair = the
+//           two groups u = 0, 1 at one h, 2 words each after a permlane16 swap of words.
+//   a_lane: LDS address of the lane's operand window for its first group at this step
+//   e_lane: LDS address of the offset sums of that group for the lane's accumulator rows
+//   xp_lane: LDS address of the lane's quad of group sums (2-bit formats)
+// The 2-bit bias term sum_g b_g X_g is one more MFMA per unit: A = (X/64 hi, X/64 lo) of
+// the lane-group's GL groups, B = (b, b) of the same groups, accumulated into yb.
 template <int FMT>
-__device__ __forceinline__ void group_mfma(const uint32_t* words, const char* smem, uint32_t a_off, bool av,
-                                           f16x8* a, const uint32_t* mk, const uint32_t* mg, f32x4& acc0,
-                                           f32x4& acc1) {
-  using F = Fmt<FMT>;
-  constexpr int NA = 4 * F::NQ;
-  if (av) {
+__device__ __forceinline__ void read_a(const char* smem, uint32_t addr, f16x8* dst) {
 #pragma unroll
-    for (int k = 0; k < NA; ++k)
-      a[k] = *reinterpret_cast<const f16x8*>(smem + a_off + (k / F::NQ) * F::WB + 16 * (k % F::NQ));
-  }
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t pr[F::PAIRS];
-    unpack_word_rt<FMT>(words[w], pr, mk, mg);
-#pragma unroll
-    for (int q = 0; q < F::NQ; ++q) {
-      const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pr[4 * q], pr[4 * q + 1], pr[4 * q + 2], pr[4 * q + 3]});
-      const int k = w * F::NQ + q;
-      if (k & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[k], b, acc1, 0, 0, 0);
-      else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[k], b, acc0, 0, 0, 0);
-    }
-  }
+  for (int q = 0; q < Fmt<FMT>::NQ; ++q) dst[q] = *reinterpret_cast<const f16x8*>(smem + addr + 16 * q);
 }
 
-template <int FMT>
-__device__ __forceinline__ void group_epilogue(const char* smem, uint32_t e_off, uint32_t x_delta, float s,
-                                               float bb, const f32x4& acc0, const f32x4& acc1, float yacc[4]) {
-  if constexpr (Fmt<FMT>::AFFINE) {
-    const f32x4 xs = *reinterpret_cast<const f32x4*>(smem + e_off + x_delta);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc0[r] + acc1[r], __builtin_fmaf(bb, xs[r], yacc[r]));
-  } else {
-    (void)bb;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, acc0[r] + acc1[r], yacc[r]);
-  }
-}
-
-// One unit: decode the lane's GL groups and accumulate every drafted row's group sums.
-//   a_lane: LDS byte address of the operand window of the lane's first group at this step
-//   e_lane: LDS byte address of the correction sums of that group for the lane's rows
-// Mode Q: lane-group g owns groups GL*g + h.  Mode H: lane-group pair p = g/2 shares
-// groups (2p + u)*GL + h, u = slot-half, after a permlane16 swap of two words per group.
 template <int FMT, int MODE>
 __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* smem, uint32_t a_lane, uint32_t e_lane,
-                                             uint32_t x_delta, bool av, f16x8* a, const uint32_t* mk,
-                                             const uint32_t* mg, float yacc[4]) {
+                                             uint32_t xp_lane, const uint32_t* mk, const uint32_t* mg,
+                                             float yacc[4], f32x4& yb) {
   using F = Fmt<FMT>;
-  constexpr int GL = F::GL;
+  constexpr int GL = F::GL, NQ = F::NQ;
+  constexpr int NPAIR = MODE == VAR_MFMA_Q ? GL / 2 : GL;
+  constexpr int WPP = MODE == VAR_MFMA_Q ? 4 : 2;   // words per group and pair member
+  constexpr int NSTEP = NPAIR * WPP;
+
+  uint32_t wa[NPAIR][WPP], wb[NPAIR][WPP];
+  float sa[NPAIR], sb[NPAIR];
+  int ga[NPAIR], gb[NPAIR];   // unit-relative group slots (units of GS) of the pair
   if constexpr (MODE == VAR_MFMA_Q) {
 #pragma unroll
-    for (int h = 0; h < GL; ++h) {
-      f32x4 acc0 = *reinterpret_cast<const f32x4*>(smem + e_lane + h * (MAXM * 4));
-      f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
-      const uint32_t words[4] = {U.w[h][0], U.w[h][1], U.w[h][2], U.w[h][3]};
-      group_mfma<FMT>(words, smem, a_lane + h * F::GS, av, a, mk, mg, acc0, acc1);
-      const float s = half_of(U.s[h >> 1], h & 1);
-      const float bb = F::AFFINE ? half_of(U.b[h >> 1], h & 1) : 0.0f;
-      group_epilogue<FMT>(smem, e_lane + h * (MAXM * 4), x_delta, s, bb, acc0, acc1, yacc);
+    for (int pi = 0; pi < NPAIR; ++pi) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        wa[pi][w] = U.w[2 * pi][w];
+        wb[pi][w] = U.w[2 * pi + 1][w];
+      }
+      sa[pi] = half_of(U.s[pi], 0);
+      sb[pi] = half_of(U.s[pi], 1);
+      ga[pi] = 2 * pi;
+      gb[pi] = 2 * pi + 1;
     }
   } else {
-    // scales: the swap of a register with itself hands lane-group pair p the pairs of both
+    // the swap of a register with itself hands lane-group pair p the scale pairs of both
     // lane-groups 2p ([0]) and 2p+1 ([1])
-    uint32_t sc[2][GL / 2], bs[2][GL / 2];
+    uint32_t sc[2][GL / 2];
 #pragma unroll
     for (int d = 0; d < GL / 2; ++d) {
       const auto t = __builtin_amdgcn_permlane16_swap(U.s[d], U.s[d], false, false);
       sc[0][d] = t[0];
       sc[1][d] = t[1];
-      if constexpr (F::AFFINE) {
-        const auto tb = __builtin_amdgcn_permlane16_swap(U.b[d], U.b[d], false, false);
-        bs[0][d] = tb[0];
-        bs[1][d] = tb[1];
-      } else {
-        bs[0][d] = bs[1][d] = 0u;
-      }
     }
 #pragma unroll
     for (int h = 0; h < GL; ++h) {
-      // exchange words 2,3 of the even lane-group with words 0,1 of the odd one
+      // words 2,3 of the even lane-group trade places with words 0,1 of the odd one
       const auto s02 = __builtin_amdgcn_permlane16_swap(U.w[h][0], U.w[h][2], false, false);
       const auto s13 = __builtin_amdgcn_permlane16_swap(U.w[h][1], U.w[h][3], false, false);
+      wa[h][0] = s02[0];
+      wa[h][1] = s13[0];
+      wb[h][0] = s02[1];
+      wb[h][1] = s13[1];
+      sa[h] = half_of(sc[0][h >> 1], h & 1);
+      sb[h] = half_of(sc[1][h >> 1], h & 1);
+      ga[h] = h;
+      gb[h] = GL + h;
+    }
+  }
+
+  f16x8 abuf[2][2 * NQ];
+  read_a<FMT>(smem, a_lane + ga[0] * F::GS, abuf[0]);
+  read_a<FMT>(smem, a_lane + gb[0] * F::GS, abuf[0] + NQ);
+  f32x4 ea = *reinterpret_cast<const f32x4*>(smem + e_lane + ga[0] * (MAXM * 4));
+  f32x4 eb = *reinterpret_cast<const f32x4*>(smem + e_lane + gb[0] * (MAXM * 4));
+  f32x4 acc_a = ea, acc_b = eb;
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
-        const uint32_t words[4] = {uu == 0 ? s02[0] : s02[1], uu == 0 ? s13[0] : s13[1], 0u, 0u};
-        f32x4 acc0 = *reinterpret_cast<const f32x4*>(smem + e_lane + (uu * GL + h) * (MAXM * 4));
-        f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
-        const uint32_t a_off = a_lane + (uu * GL + h) * F::GS;
-        // two words per slot-half: operands k = wl*NQ + q
-        if (av) {
-#pragma unroll
-          for (int k = 0; k < 2 * F::NQ; ++k)
-            a[k] = *reinterpret_cast<const f16x8*>(smem + a_off + (k / F::NQ) * F::WB + 16 * (k % F::NQ));
-        }
-#pragma unroll
-        for (int wl = 0; wl < 2; ++wl) {
-          uint32_t pr[F::PAIRS];
-          unpack_word_rt<FMT>(words[wl], pr, mk, mg);
-#pragma unroll
-          for (int q = 0; q < F::NQ; ++q) {
-            const f16x8 b = __builtin_bit_cast(f16x8, u32x4{pr[4 * q], pr[4 * q + 1], pr[4 * q + 2], pr[4 * q + 3]});
-            const int k = wl * F::NQ + q;
-            if (k & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[k], b, acc1, 0, 0, 0);
-            else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[k], b, acc0, 0, 0, 0);
-          }
-        }
-        const float s = half_of(sc[uu][h >> 1], h & 1);
-        const float bb = F::AFFINE ? half_of(bs[uu][h >> 1], h & 1) : 0.0f;
-        group_epilogue<FMT>(smem, e_lane + (uu * GL + h) * (MAXM * 4), x_delta, s, bb, acc0, acc1, yacc);
+  for (int st = 0; st < NSTEP; ++st) {
+    const int pi = st / WPP, w = st % WPP;
+    if (st + 1 < NSTEP) {
+      const int pn = (st + 1) / WPP, wn = (st + 1) % WPP;
+      read_a<FMT>(smem, a_lane + ga[pn] * F::GS + wn * F::WB, abuf[(st + 1) & 1]);
+      read_a<FMT>(smem, a_lane + gb[pn] * F::GS + wn * F::WB, abuf[(st + 1) & 1] + NQ);
+    }
+    if (w == 0) {
+      acc_a = ea;
+      acc_b = eb;
+      if (pi + 1 < NPAIR) {   // the next pair's offset sums, one pair ahead
+        ea = *reinterpret_cast<const f32x4*>(smem + e_lane + ga[pi + 1] * (MAXM * 4));
+        eb = *reinterpret_cast<const f32x4*>(smem + e_lane + gb[pi + 1] * (MAXM * 4));
       }
     }
+    uint32_t pa[F::PAIRS], pb[F::PAIRS];
+    unpack_word_rt<FMT>(wa[pi][w], pa, mk, mg);
+    unpack_word_rt<FMT>(wb[pi][w], pb, mk, mg);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const f16x8 ba = __builtin_bit_cast(f16x8, u32x4{pa[4 * q], pa[4 * q + 1], pa[4 * q + 2], pa[4 * q + 3]});
+      const f16x8 bb = __builtin_bit_cast(f16x8, u32x4{pb[4 * q], pb[4 * q + 1], pb[4 * q + 2], pb[4 * q + 3]});
+      acc_a = __builtin_amdgcn_mfma_f32_16x16x32_f16(abuf[st & 1][q], ba, acc_a, 0, 0, 0);
+      acc_b = __builtin_amdgcn_mfma_f32_16x16x32_f16(abuf[st & 1][NQ + q], bb, acc_b, 0, 0, 0);
+    }
+    if (w == WPP - 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(sa[pi], acc_a[r], __builtin_fmaf(sb[pi], acc_b[r], yacc[r]));
+    }
+  }
+  if constexpr (F::AFFINE) {
+    static_assert(GL == 4, "bias product takes four groups per lane");
+    const f16x8 xa = *reinterpret_cast<const f16x8*>(smem + xp_lane);
+    const f16x8 bv = __builtin_bit_cast(f16x8, u32x4{U.b[0], U.b[1], U.b[0], U.b[1]});
+    yb = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bv, yb, 0, 0, 0);
+  } else {
+    (void)xp_lane;
+    (void)yb;
   }
 }
 
@@ -472,13 +495,13 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
 // for the fixed-order reduction.
 template <int FMT, int MODE>
 __device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t, bool sole, int slot,
-                                           int wid, int g, int i, float yacc[4]) {
+                                           int wid, int g, int i, const float yacc[4], const f32x4& yb) {
   const float* invf = reinterpret_cast<const float*>(smem + L.row_off) + MAXM;
   const int m0 = MODE == VAR_MFMA_Q ? 0 : 4 * (g & 1);
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    v[r] = yacc[r] * invf[m0 + r];
+    v[r] = (Fmt<FMT>::AFFINE ? __builtin_fmaf(64.0f, yb[r], yacc[r]) : yacc[r]) * invf[m0 + r];
     if constexpr (MODE == VAR_MFMA_Q) {
       const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[r]), __float_as_uint(v[r]), false, false);
       v[r] = __uint_as_float(p[0]) + __uint_as_float(p[1]);   // rows 0+1 and 2+3
@@ -502,7 +525,6 @@ template <int FMT, int MODE, int XT>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, PREF = F::PREF, GPS = 4 * GL;
-  constexpr int NA = 4 * F::NQ;
   constexpr bool NORM = FMT == HAD2 || XT == XBF16;
   const LdsLayout L(FMT, A.M, A.win_steps, A.tiles_max);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -523,20 +545,28 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     asm volatile("v_mov_b32 %0, %1" : "=v"(mg[k]) : "s"(A.magic[k]));
   }
 
-  // this lane's operand row and whether it carries a drafted row (others stay zero)
+  // this lane's operand row: a drafted row, or the zero row M when the lane's A row
+  // carries none (rows of other row-blocks must read zeros in this lane's K slots)
   const int am = MODE == VAR_MFMA_Q ? i - 4 * g : (g < 2 ? i : i - 8);
   const bool av = am >= 0 && am < A.M && (MODE == VAR_MFMA_H || am < 4);
+  const int arow = av ? am : A.M;
   const int m0 = MODE == VAR_MFMA_Q ? 0 : 4 * (g & 1);
-  const uint32_t a_lane0 = L.a_off + (uint32_t)(av ? am : 0) * A.a_pitch +
+  const uint32_t a_lane0 = L.a_off + (uint32_t)arow * A.a_pitch +
                            (MODE == VAR_MFMA_Q ? GL * g * F::GS : 2 * (g >> 1) * GL * F::GS + 2 * (g & 1) * F::WB);
   const uint32_t e_lane0 = L.e_off + ((MODE == VAR_MFMA_Q ? GL * g : 2 * (g >> 1) * GL) * MAXM + m0) * 4;
-  const uint32_t x_delta = L.x_off - L.e_off;
-  f16x8 a[NA];
-#pragma unroll
-  for (int k = 0; k < NA; ++k) a[k] = f16x8{};
+  const uint32_t xp_lane0 = L.xp_off + (uint32_t)arow * L.xp_pitch + (uint32_t)g * 16u;
 
   float* ytile = reinterpret_cast<float*>(smem + L.ytile_off);
   for (int e = tid; e < T * MAXM * 16; e += NTHREADS) ytile[e] = 0.0f;
+  {
+    // the zero rows: never written by the staging, so cleared once per launch
+    uint32_t* za = reinterpret_cast<uint32_t*>(smem + L.a_off + A.M * A.a_pitch);
+    for (int e = tid; e < A.a_pitch / 4; e += NTHREADS) za[e] = 0u;
+    if constexpr (F::AFFINE) {
+      uint32_t* zx = reinterpret_cast<uint32_t*>(smem + L.xp_off + A.M * L.xp_pitch);
+      for (int e = tid; e < L.xp_pitch / 4; e += NTHREADS) zx[e] = 0u;
+    }
+  }
   if (!NORM && tid < MAXM) reinterpret_cast<float*>(smem + L.row_off)[MAXM + tid] = 1.0f;
 
   const char* wbase = reinterpret_cast<const char*>(A.w) + (size_t)r0 * wrow;
@@ -591,29 +621,32 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     // first would hold back the staging (and every MFMA after it) by the whole burst.
     XStage xs;
     stage_load<XT>(A, ws0 * KSTEP, ns * KSTEP, xs);
-    __syncthreads();  // previous window's readers are done with the LDS
+    lds_barrier();  // previous window's readers are done with the LDS
     stage_compute<FMT, XT>(A, smem, L, ns * KSTEP, xs);
     Unit<FMT> ring[PREF];
     if (nu > 0) {
 #pragma unroll
       for (int d = 0; d < PREF; ++d) issue(ring[d]);
     }
-    __syncthreads();
+    lds_barrier();
 
     int ct = nu > 0 ? ua / ns : 0, cs = nu > 0 ? ua - ct * ns : 0;
     float yacc[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 yb = {0.f, 0.f, 0.f, 0.f};
     for (int base = 0; base < nu; base += PREF) {
 #pragma unroll
       for (int d = 0; d < PREF; ++d) {
         if (base + d < nu) {
           const uint32_t a_lane = a_lane0 + (uint32_t)cs * (GPS * F::GS);
           const uint32_t e_lane = e_lane0 + (uint32_t)cs * (GPS * MAXM * 4);
-          compute_unit<FMT, MODE>(ring[d], smem, a_lane, e_lane, x_delta, av, a, mk, mg, yacc);
+          const uint32_t xp_lane = xp_lane0 + (uint32_t)cs * 64u;   // 4 quads of groups per unit
+          compute_unit<FMT, MODE>(ring[d], smem, a_lane, e_lane, xp_lane, mk, mg, yacc, yb);
           if (++cs == ns || base + d + 1 == nu) {
             const bool sole = ua <= ct * ns && ub >= (ct + 1) * ns;
-            flush_tile<FMT, MODE>(smem, L, ct, sole, ct == ua / ns ? 0 : 1, wid, g, i, yacc);
+            flush_tile<FMT, MODE>(smem, L, ct, sole, ct == ua / ns ? 0 : 1, wid, g, i, yacc, yb);
 #pragma unroll
             for (int r = 0; r < 4; ++r) yacc[r] = 0.f;
+            yb = f32x4{0.f, 0.f, 0.f, 0.f};
             cs = 0;
             ++ct;
           }
@@ -621,7 +654,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
         issue(ring[d]);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // fixed-order reduction of tiles split between waves: a tile is split when a wave
     // boundary falls strictly inside it; its contributors are the non-empty waves whose
@@ -647,7 +680,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // write y[m, r0 .. r1) from the tile accumulators
   const int nr = r1 - r0;
