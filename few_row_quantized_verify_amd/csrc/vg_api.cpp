@@ -52,6 +52,7 @@ vg_status device_info(vg::DeviceInfo* out) {
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess ||
         hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, d) != hipSuccess)
       return fail(VG_ERR_HIP, "hipDeviceGetAttribute failed on device %d", d);
+    g_dev[d].id = d;
     g_dev[d].cu_count = cu > 0 ? cu : 1;
     g_dev[d].max_lds = lds;
     g_dev_ok[d] = true;

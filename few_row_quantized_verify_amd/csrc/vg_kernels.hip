@@ -12,7 +12,8 @@
 //     one K-step of 1024 (8 sign groups or 16 affine groups).  Per unit each lane loads
 //     GL consecutive groups of one row in single wide loads (codes, then the scales and
 //     biases of those groups), so a row's unit is fetched by 4 lanes as 256 contiguous
-//     bytes of codes.  Every wave keeps PREF units in flight in a register ring.
+//     bytes of codes.  Every wave keeps PREF units in flight in a register ring; PREF is
+//     chosen per shape at launch (deeper only when each wave has many units to stream).
 //   * K is processed in windows.  Per window the workgroup first stages its activations
 //     into LDS, already in the operand layout the unpacked codes need (and rotated, for
 //     the Hadamard format), together with per-(group, row) correction sums; only then are
@@ -26,6 +27,8 @@
 //     pairs share a group after one permlane16 swap of two words.  Every accumulator
 //     register therefore holds one quantization group's dot products, and the per-group
 //     scale (and bias) is applied once per group in fp32.
+#include <atomic>
+
 #include "vg_device.h"
 #include "vg_launch.h"
 
@@ -45,15 +48,15 @@ constexpr int MAXM = 8;
 template <int FMT> struct Fmt;
 // GL: consecutive quantization groups each lane loads per unit (16*GL bytes of codes and
 // 2*GL bytes of scales in single loads, 64*GL contiguous bytes per row and unit); a unit
-// covers 4*GL groups = 1024 K for both formats.  PREF: units in flight per wave.
+// covers 4*GL groups = 1024 K for both formats.
 template <> struct Fmt<SIGN1> {
-  static constexpr int G = 128, WORD_K = 32, PAIRS = 16, NQ = 4, GL = 2, PREF = 4;
+  static constexpr int G = 128, WORD_K = 32, PAIRS = 16, NQ = 4, GL = 2;
   static constexpr int WB = 64;           // LDS bytes of one word's operand window
   static constexpr int GS = 4 * WB + 16;  // LDS bytes per group (+16 pad vs bank conflicts)
   static constexpr bool AFFINE = false;
 };
 template <> struct Fmt<AFFINE2> {
-  static constexpr int G = 64, WORD_K = 16, PAIRS = 8, NQ = 2, GL = 4, PREF = 2;
+  static constexpr int G = 64, WORD_K = 16, PAIRS = 8, NQ = 2, GL = 4;
   static constexpr int WB = 32;
   static constexpr int GS = 4 * WB + 16;
   static constexpr bool AFFINE = true;
@@ -521,10 +524,10 @@ __device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t
   }
 }
 
-template <int FMT, int MODE, int XT>
+template <int FMT, int MODE, int XT, int PREF>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
-  constexpr int GL = F::GL, PREF = F::PREF, GPS = 4 * GL;
+  constexpr int GL = F::GL, GPS = 4 * GL;
   constexpr bool NORM = FMT == HAD2 || XT == XBF16;
   const LdsLayout L(FMT, A.M, A.win_steps, A.tiles_max);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -691,15 +694,15 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
 }
 
 // The kernel names carry the variant name, so a trace shows which variant ran.
-template <int FMT, int XT>
+template <int FMT, int XT, int PREF>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_q(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_Q, XT>(A, smem);
+  mfma_body<FMT, VAR_MFMA_Q, XT, PREF>(A, smem);
 }
-template <int FMT, int XT>
+template <int FMT, int XT, int PREF>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_H, XT>(A, smem);
+  mfma_body<FMT, VAR_MFMA_H, XT, PREF>(A, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -729,6 +732,26 @@ size_t mfma_lds_bytes(int fmt, int variant, int M, int K, int N, int grid, int m
   return (size_t)LdsLayout(fmt, M, ws, tiles_max).total;
 }
 
+// Raises a kernel's dynamic-LDS limit once per device.
+static hipError_t allow_lds(void (*kern)(MfmaArgs), std::atomic<uint64_t>& done, const DeviceInfo& dev) {
+  const uint64_t bit = 1ull << (dev.id & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, dev.max_lds);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
+template <int FMT, int MODE, int XT, int PREF>
+static hipError_t launch_kern(const MfmaArgs& A, int grid, size_t lds, hipStream_t stream, const DeviceInfo& dev) {
+  void (*kern)(MfmaArgs) = MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT, PREF> : vg_mfma_h<FMT, XT, PREF>;
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t e = allow_lds(kern, attr_done, dev);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHREADS), lds, stream, A);
+  return hipGetLastError();
+}
+
 template <int FMT, int MODE, int XT>
 static hipError_t launch_one(const GemmCall& c, const DeviceInfo& dev) {
   const int grid = pick_grid(c.N, dev);
@@ -753,16 +776,13 @@ static hipError_t launch_one(const GemmCall& c, const DeviceInfo& dev) {
       A.magic[k] = half_magic_affine2(p) | (half_magic_affine2(p) << 16);
     }
   }
-  void (*kern)(MfmaArgs) = MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT> : vg_mfma_h<FMT, XT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, dev.max_lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHREADS), lds, c.stream, A);
-  return hipGetLastError();
+  // Units in flight per wave: one when each wave streams only a few units (the first
+  // loads then reach the compute sooner), two for long streams; the 1-bit format's units
+  // are half as large and always keep two.
+  if (FMT == SIGN1) return launch_kern<FMT, MODE, XT, 2>(A, grid, lds, c.stream, dev);
+  const int units_per_wave = ((rows_max + 15) / 16) * (c.K / KSTEP) / NW;
+  if (units_per_wave < 8) return launch_kern<FMT, MODE, XT, 1>(A, grid, lds, c.stream, dev);
+  return launch_kern<FMT, MODE, XT, 2>(A, grid, lds, c.stream, dev);
 }
 
 hipError_t launch_mfma(const GemmCall& c, int variant, const DeviceInfo& dev) {

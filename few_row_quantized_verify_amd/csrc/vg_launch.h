@@ -27,6 +27,7 @@ struct GemmCall {
 };
 
 struct DeviceInfo {
+  int id;             // HIP device ordinal
   int cu_count;
   int max_lds;        // bytes per workgroup
 };

@@ -271,3 +271,14 @@ def test_many_workgroups_full_check(vg, fmt, x_dtype):
     case = draw_case(fmt, K, N, x_dtype, seed=13)
     for M in (1, 4, 7, 8):
         check(case, M, run(vg, case, M), label="many-wg")
+
+
+@pytest.mark.parametrize("fmt,x_dtype", [("had2", "f16"), ("affine2", "bf16")])
+def test_long_row_ranges_deep_ring(vg, fmt, x_dtype):
+    """Enough rows per workgroup that each wave streams many units (the deeper weight
+    ring), in both row-block modes; sampled columns."""
+    K, N = 8192, 40000
+    case = draw_case(fmt, K, N, x_dtype, seed=14)
+    cols = sample_cols(N, k=300, seed=1)
+    for M in (1, 3, 8):
+        check(case, M, run(vg, case, M), cols=cols, label="deep-ring")
