@@ -15,13 +15,20 @@ t(M=8)/t(M=1), a roofline object for the dominant kernel and the CPU oracle base
 
 Options:
   --workload NAME    another named workload (see synthetic.inputs.WORKLOADS)
+  --m LIST           only these row counts, e.g. "8" (for profiling one kernel)
   --table            also print one JSON line per workload and M (not the default)
   --no-cpu           skip the CPU oracle baseline leg
   --copy-calibration run only a device-to-device copy of known size (for HBM counters)
+  --ingest-counters FETCH WRITE CFETCH CWRITE
+                     write profiles/hbm_traffic.json from four rocprofv3 --pmc output
+                     directories: FETCH_SIZE and WRITE_SIZE of a `--m 8 --no-cpu` run,
+                     and of a `--copy-calibration` run (no GPU needed)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -100,6 +107,59 @@ def load_traffic(kernel: str, digest: str):
     return ent.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(d: str):
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _mean_counter(d: str, counter: str, kernel_prefix: str):
+    vals = [float(r["Counter_Value"]) for r in _counter_rows(d)
+            if r["Counter_Name"] == counter and kernel_prefix in r["Kernel_Name"]]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def ingest_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload, M) -> int:
+    """HBM bytes per launch of the row count's kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a copy of known size."""
+    import few_row_quantized_verify_amd as vg
+    fmt, K, N, x_dtype, _ = WORKLOADS[workload]
+    kern = vg.variant_name(vg.plan_variant(fmt, x_dtype, M, N, K))
+    cf, _ = _mean_counter(cfetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _mean_counter(cwrite_dir, "WRITE_SIZE", "copyBuffer")
+    if cf is None:
+        cf, _ = _mean_counter(cfetch_dir, "FETCH_SIZE", "")
+    if cw is None:
+        cw, _ = _mean_counter(cwrite_dir, "WRITE_SIZE", "")
+    nbytes = 256 << 20
+    fetch_factor = nbytes / (cf * 1024.0)
+    write_factor = nbytes / (cw * 1024.0)
+    kf, nf = _mean_counter(fetch_dir, "FETCH_SIZE", "vg::" + kern)
+    kw, nw = _mean_counter(write_dir, "WRITE_SIZE", "vg::" + kern)
+    if kf is None or kw is None:
+        print(f"no {kern} dispatches in the counter output", file=sys.stderr)
+        return 1
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        t = {}
+    t["note"] = ("HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per "
+                 "dispatch), each scaled by the factor the same counter shows for a 256 MiB device "
+                 "copy (bench.py --copy-calibration).  Keyed by variant/workload/M; valid only while "
+                 "the kernel sources hash to source_digest.")
+    t["calibration"] = {"copy_bytes": nbytes, "fetch_factor": fetch_factor, "write_factor": write_factor}
+    fb = kf * 1024.0 * fetch_factor
+    wb = kw * 1024.0 * write_factor
+    t.setdefault("kernels", {})[f"{kern}/{workload}/M{M}"] = {
+        "source_digest": kernel_source_digest(), "dispatches": [nf, nw],
+        "fetch_bytes": round(fb), "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+    print(json.dumps(t["kernels"][f"{kern}/{workload}/M{M}"]))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,7 +169,12 @@ def main() -> int:
     ap.add_argument("--table", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--m", default=None)
+    ap.add_argument("--ingest-counters", nargs=4, metavar="DIR", default=None)
     args = ap.parse_args()
+    if args.ingest_counters:
+        return ingest_counters(*args.ingest_counters, args.workload,
+                               int(args.m) if args.m else 8)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify GEMM runs on one device here; "
               "run it with --gpus 1.", file=sys.stderr)
@@ -138,6 +203,8 @@ def main() -> int:
     headline = None
     for name in names:
         fmt, K, N, x_dtype, Ms = WORKLOADS[name]
+        if args.m:
+            Ms = tuple(int(v) for v in args.m.split(","))
         case = workload_case(name, seed=0)
         pb = packed_bytes(case)
         ncopy = max(2, -(-POOL_BYTES // pb))
