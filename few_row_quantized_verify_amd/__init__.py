@@ -6,7 +6,8 @@ once inside the contraction.  All computation runs in the HIP library; this pack
 only marshals tensors and streams.
 """
 from .binding import (  # noqa: F401
-    DTYPES, FORMATS, VerifyGemmError, debug_unpack, force_variant, hadamard_rotate, lib,
-    plan_variant, variant_count, variant_name, verify_argmax_rows, verify_gemm,
+    DTYPES, FORMATS, VerifyGemmError, debug_unpack, force_ksplit, force_variant,
+    hadamard_rotate, lib, plan_ksplit, plan_variant, variant_count, variant_name,
+    verify_argmax_rows, verify_gemm,
     verify_gemm_affine2, verify_gemm_had2, verify_gemm_sign1,
 )

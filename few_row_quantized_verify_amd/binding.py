@@ -44,6 +44,8 @@ _SIGS = {
     "vg_variant_name": (ctypes.c_char_p, [_I]),
     "vg_force_variant": (_I, [_I]),
     "vg_variant_count": (_I, []),
+    "vg_plan_ksplit": (_I, [_I, _I, _I, _I, _I]),
+    "vg_force_ksplit": (_I, [_I]),
     "vg_debug_unpack_sign1": (_I, [_P, _I, _I, _P, _P]),
     "vg_debug_unpack_affine2": (_I, [_P, _I, _I, _P, _P]),
 }
@@ -182,3 +184,11 @@ def variant_count() -> int:
 
 def force_variant(v: int) -> None:
     _check(lib().vg_force_variant(v))
+
+
+def plan_ksplit(fmt: str, x_dtype: str, M: int, N: int, K: int) -> int:
+    return lib().vg_plan_ksplit(FORMATS[fmt], DTYPES[x_dtype], M, N, K)
+
+
+def force_ksplit(ks: int) -> None:
+    _check(lib().vg_force_ksplit(ks))

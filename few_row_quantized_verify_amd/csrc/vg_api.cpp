@@ -20,6 +20,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 int g_forced = -1;  // forced variant (-1: dispatch)
+int g_forced_ks = 0;  // forced K slices of the MFMA variants (0: dispatch)
 std::once_flag g_env_once;
 
 vg_status fail(vg_status s, const char* fmt, ...) {
@@ -89,22 +90,66 @@ int plan(int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev) {
   if (xt == VG_F32) return vg::VAR_VALU;
   if (K % kstep_of(fmt) != 0) return vg::VAR_VALU;
   const int var = M <= 4 ? vg::VAR_MFMA_Q : vg::VAR_MFMA_H;
-  const int tiles = (N + 15) / 16;
-  const int grid = tiles < dev.cu_count ? tiles : dev.cu_count;
-  int ws = 0;
-  vg::mfma_lds_bytes(fmt, var, M, K, N, grid, dev.max_lds, &ws);
-  return ws > 0 ? var : vg::VAR_VALU;
+  vg::MfmaPlan p;
+  return vg::plan_mfma(fmt, var, M, K, N, dev, g_forced_ks, &p) ? var : vg::VAR_VALU;
 }
 
 bool variant_supports(int var, int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev) {
   if (var == vg::VAR_VALU) return true;
   if (xt == VG_F32 || K % kstep_of(fmt) != 0) return false;
   if (var == vg::VAR_MFMA_Q && M > 4) return false;
-  const int tiles = (N + 15) / 16;
-  const int grid = tiles < dev.cu_count ? tiles : dev.cu_count;
-  int ws = 0;
-  vg::mfma_lds_bytes(fmt, var, M, K, N, grid, dev.max_lds, &ws);
-  return ws > 0;
+  vg::MfmaPlan p;
+  return vg::plan_mfma(fmt, var, M, K, N, dev, g_forced_ks, &p);
+}
+
+// Workspaces of the calls that split K across workgroups, one per (device, stream): the
+// partial outputs and one arrival counter per row group.  Allocated on the first such call
+// on a stream, grown when a larger call needs it, kept until the process ends.  The
+// kernels leave the counters at zero, so consecutive calls on one stream share them; calls
+// on different streams never share a workspace.
+struct Workspace {
+  int dev;
+  hipStream_t stream;
+  char* ptr;
+  size_t bytes;
+};
+std::mutex g_ws_mu;
+Workspace g_ws[64];
+int g_ws_count = 0;
+constexpr size_t kCounterBytes = 4096;   // >= 4 bytes per row group (<= 1024 groups)
+
+vg_status workspace(int dev, hipStream_t stream, size_t part_bytes, float** part, uint32_t** counters) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace* w = nullptr;
+  for (int k = 0; k < g_ws_count; ++k)
+    if (g_ws[k].dev == dev && g_ws[k].stream == stream) w = &g_ws[k];
+  if (!w) {
+    if (g_ws_count == 64) return fail(VG_ERR_HIP, "too many streams with split-K calls");
+    w = &g_ws[g_ws_count++];
+    *w = Workspace{dev, stream, nullptr, 0};
+  }
+  const size_t need = kCounterBytes + part_bytes;
+  if (w->bytes < need) {
+    if (w->ptr) {
+      // earlier calls on this stream may still read the old workspace
+      if (hipStreamSynchronize(stream) != hipSuccess || hipFree(w->ptr) != hipSuccess)
+        return fail(VG_ERR_HIP, "releasing the split-K workspace failed");
+      w->ptr = nullptr;
+      w->bytes = 0;
+    }
+    const size_t bytes = need + need / 2;
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return fail(VG_ERR_HIP, "split-K workspace allocation of %zu bytes failed", bytes);
+    if (hipMemsetAsync(p, 0, kCounterBytes, stream) != hipSuccess) {
+      (void)hipFree(p);
+      return fail(VG_ERR_HIP, "clearing the split-K counters failed");
+    }
+    w->ptr = static_cast<char*>(p);
+    w->bytes = bytes;
+  }
+  *counters = reinterpret_cast<uint32_t*>(w->ptr);
+  *part = reinterpret_cast<float*>(w->ptr + kCounterBytes);
+  return VG_OK;
 }
 
 vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint32_t* w,
@@ -120,7 +165,21 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
     var = g_forced;
   }
   vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, static_cast<hipStream_t>(stream)};
-  const hipError_t e = var == vg::VAR_VALU ? vg::launch_valu(c, dev) : vg::launch_mfma(c, var, dev);
+  hipError_t e;
+  if (var == vg::VAR_VALU) {
+    e = vg::launch_valu(c, dev);
+  } else {
+    vg::MfmaPlan p;
+    if (!vg::plan_mfma(fmt, var, M, K, N, dev, g_forced_ks, &p))
+      return fail(VG_ERR_UNSUPPORTED, "M=%d K=%d does not fit the MFMA staging", M, K);
+    float* part = nullptr;
+    uint32_t* counters = nullptr;
+    if (p.ks > 1) {
+      if (p.rg * 4 > static_cast<int>(kCounterBytes)) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
+      if (vg_status s = workspace(dev.id, c.stream, vg::mfma_workspace_bytes(M, N, p), &part, &counters)) return s;
+    }
+    e = vg::launch_mfma(c, var, p, part, counters, dev);
+  }
   if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return VG_OK;
@@ -219,6 +278,22 @@ vg_status vg_force_variant(int variant) {
 }
 
 int vg_variant_count(void) { return vg::VAR_COUNT; }
+
+vg_status vg_force_ksplit(int ksplit) {
+  if (ksplit < 0 || ksplit > 64) return fail(VG_ERR_ARG, "K slices %d outside 0..64", ksplit);
+  g_forced_ks = ksplit;
+  return VG_OK;
+}
+
+int vg_plan_ksplit(int format, int x_dtype, int M, int N, int K) {
+  const int var = vg_plan_variant(format, x_dtype, M, N, K);
+  if (var < 0) return -1;
+  if (var == vg::VAR_VALU) return 1;
+  vg::DeviceInfo dev;
+  if (device_info(&dev) != VG_OK) return -1;
+  vg::MfmaPlan p;
+  return vg::plan_mfma(format, var, M, K, N, dev, g_forced_ks, &p) ? p.ks : -1;
+}
 
 vg_status vg_debug_unpack_sign1(const uint32_t* wbits, int N, int K, uint8_t* codes, void* stream) {
   if (N < 1 || K < 32 || K % 32 != 0) return fail(VG_ERR_SHAPE, "bad shape N=%d K=%d", N, K);

@@ -82,6 +82,9 @@ struct MfmaArgs {
   int a_pitch;     // LDS bytes per activation row in a window
   uint32_t mask[6];   // code-extraction masks per bit position (see vg_device.h)
   uint32_t magic[6];  // fp16 magic pairs per bit position
+  int rg, ks;         // row groups x K slices; workgroup b takes row group b / ks, slice b % ks
+  float* part;        // ks > 1: partial outputs [ks][M][N]
+  uint32_t* counters; // ks > 1: arrivals per row group (zero between calls)
 };
 
 // LDS carve-up (byte offsets), computed identically on host and device.
@@ -91,7 +94,7 @@ struct MfmaArgs {
 //   xp: 2-bit formats: per (row, lane-group quad of GL groups) the group sums / 64 as
 //       fp16 hi parts then lo parts (16 bytes), rows 0..M-1 and a zero row M
 struct LdsLayout {
-  int a_off, e_off, xp_off, xp_pitch, ytile_off, slot_off, row_off, total;
+  int a_off, e_off, xp_off, xp_pitch, ytile_off, slot_off, row_off, flag_off, total;
   __host__ __device__ LdsLayout(int fmt, int M, int win_steps, int tiles_max) {
     const int groups = win_steps * fmt_gps(fmt);
     const int pitch = groups * fmt_gs(fmt) + 16;   // must equal MfmaArgs::a_pitch
@@ -102,7 +105,8 @@ struct LdsLayout {
     ytile_off = xp_off + (fmt == SIGN1 ? 0 : (M + 1) * xp_pitch);
     slot_off = ytile_off + tiles_max * MAXM * 16 * 4;
     row_off = slot_off + NW * 2 * MAXM * 16 * 4;
-    total = row_off + 2 * MAXM * 4;
+    flag_off = row_off + 2 * MAXM * 4;
+    total = flag_off + 16;
   }
 };
 
@@ -533,10 +537,11 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
-  const int P = gridDim.x, b = blockIdx.x;
-  const int r0 = (int)(((long long)A.N * b) / P), r1 = (int)(((long long)A.N * (b + 1)) / P);
+  const int rgi = blockIdx.x / A.ks, ksi = blockIdx.x - rgi * A.ks;
+  const int r0 = (int)(((long long)A.N * rgi) / A.rg), r1 = (int)(((long long)A.N * (rgi + 1)) / A.rg);
   const int T = (r1 - r0 + 15) / 16;
   const int S = A.K / KSTEP;
+  const int kb0 = (S * ksi) / A.ks, kb1 = (S * (ksi + 1)) / A.ks;   // this slice's K-steps
   const uint32_t wrow = (uint32_t)(A.K / F::WORD_K) * 4u;   // bytes of codes per row
   const uint32_t srow = (uint32_t)(A.K / F::G) * 2u;        // bytes of scales per row
   // masks stay in SGPRs, magics are moved into VGPRs once: v_and_or_b32 may read only one
@@ -576,8 +581,8 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   const char* sbase = reinterpret_cast<const char*>(A.scales) + (size_t)r0 * srow;
   const char* bbase = reinterpret_cast<const char*>(A.biases) + (size_t)r0 * srow;
 
-  for (int ws0 = 0; ws0 < S; ws0 += A.win_steps) {
-    const int ns = min(A.win_steps, S - ws0);
+  for (int ws0 = kb0; ws0 < kb1; ws0 += A.win_steps) {
+    const int ns = min(A.win_steps, kb1 - ws0);
     const int UW = T * ns;
     const int ua = (int)(((long long)UW * wid) / NW), ub = (int)(((long long)UW * (wid + 1)) / NW);
     const int nu = ub - ua;
@@ -687,10 +692,42 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
 
   // write y[m, r0 .. r1) from the tile accumulators
   const int nr = r1 - r0;
+  if (A.ks == 1) {
+    for (int e = tid; e < A.M * nr; e += NTHREADS) {
+      const int m = e / nr, rr = e - m * nr;
+      A.y[(size_t)m * A.N + r0 + rr] = ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)];
+    }
+    return;
+  }
+  // K split across workgroups: park this slice's partial, and let the last slice of the row
+  // group to arrive add all slices in slice order (the same order whichever arrives last).
+  // The partials and the arrival counter are agent-scope atomic accesses, which bypass the
+  // per-XCD L2 caches; a device-wide fence would instead write back and invalidate the
+  // whole L2 of the XCD under every other workgroup running there.
+  float* part = A.part + (size_t)ksi * A.M * A.N;
   for (int e = tid; e < A.M * nr; e += NTHREADS) {
     const int m = e / nr, rr = e - m * nr;
-    A.y[(size_t)m * A.N + r0 + rr] = ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)];
+    __hip_atomic_store(part + (size_t)m * A.N + r0 + rr, ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)],
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partials have landed
+  lds_barrier();
+  uint32_t* flag = reinterpret_cast<uint32_t*>(smem + L.flag_off);
+  if (tid == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(A.counters + rgi, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    flag[0] = before == (uint32_t)(A.ks - 1) ? 1u : 0u;
+  }
+  lds_barrier();
+  if (flag[0] == 0u) return;
+  for (int e = tid; e < A.M * nr; e += NTHREADS) {
+    const int m = e / nr, rr = e - m * nr;
+    const float* src = A.part + (size_t)m * A.N + r0 + rr;
+    float sum = 0.0f;
+    for (int k = 0; k < A.ks; ++k)
+      sum += __hip_atomic_load(src + (size_t)k * A.M * A.N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    A.y[(size_t)m * A.N + r0 + rr] = sum;
+  }
+  if (tid == 0) __hip_atomic_store(A.counters + rgi, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The kernel names carry the variant name, so a trace shows which variant ran.
@@ -707,29 +744,76 @@ __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
 
 // ---------------------------------------------------------------------------------------
 // Host side of the MFMA variants.
-static int pick_grid(int N, const DeviceInfo& dev) {
-  const int tiles = (N + 15) / 16;
-  return tiles < dev.cu_count ? tiles : dev.cu_count;
+// Packed-weight bytes of a call (codes, scales and biases).
+static double packed_bytes(int fmt, int K, int N) {
+  return fmt == SIGN1 ? (double)N * K / 8 + 2.0 * N * K / 128 : (double)N * K / 4 + 4.0 * N * K / 64;
 }
 
-size_t mfma_lds_bytes(int fmt, int variant, int M, int K, int N, int grid, int max_lds, int* win_steps) {
-  (void)variant;
-  const int S = K / KSTEP;
-  const int rows_max = (N + grid - 1) / grid + 1;
-  const int tiles_max = (rows_max + 15) / 16 + 1;
-  // largest window that fits, then balanced so windows have equal step counts
+// Largest staging window (in K-steps) whose LDS carve-up fits, balanced so the windows of
+// a slice of S K-steps have equal step counts; 0 when nothing fits.
+static int window_steps(int fmt, int M, int S, int tiles_max, int max_lds, size_t* lds) {
   int best = 0;
   // at most MAXT activation chunks of 32 K per thread: M * ws * KSTEP / 32 <= NTHREADS * MAXT
   const int ws_cap = (NTHREADS * MAXT * 32) / (M * KSTEP);
   for (int ws = S < ws_cap ? S : ws_cap; ws >= 1; --ws) {
-    const LdsLayout L(fmt, M, ws, tiles_max);
-    if (L.total <= max_lds) { best = ws; break; }
+    if (LdsLayout(fmt, M, ws, tiles_max).total <= max_lds) { best = ws; break; }
   }
-  if (best == 0) { *win_steps = 0; return 0; }
+  if (best == 0) return 0;
   const int nwin = (S + best - 1) / best;
   const int ws = (S + nwin - 1) / nwin;
-  *win_steps = ws;
-  return (size_t)LdsLayout(fmt, M, ws, tiles_max).total;
+  *lds = (size_t)LdsLayout(fmt, M, ws, tiles_max).total;
+  return ws;
+}
+
+bool plan_mfma(int fmt, int variant, int M, int K, int N, const DeviceInfo& dev, int force_ks, MfmaPlan* p) {
+  (void)variant;
+  const int tiles = (N + 15) / 16;
+  const int S = K / KSTEP;
+  const int cus = dev.cu_count;
+  // K slices: the count minimising a per-workgroup cost in bytes, which adds the weight
+  // units it streams (16-row tiles, so a short last tile costs a whole one), the activation
+  // bytes it stages at half weight (they come from L2) or full weight for the rotated
+  // format (the transform runs in every workgroup), and for a split the partial outputs
+  // written and read back plus a fixed cost for the reduction at the end.  Measured on
+  // MI355X against forced slice counts.
+  int ks = 1;
+  if (force_ks > 0) {
+    ks = force_ks < S ? force_ks : S;
+  } else {
+    const double unit_bytes = packed_bytes(fmt, KSTEP, 16);
+    const int ks_max = S < 16 ? S : 16;
+    double best = 0.0;
+    for (int k = 1; k <= ks_max; ++k) {
+      int g = cus / k;
+      if (g > tiles) g = tiles;
+      if (g < 1) g = 1;
+      const int rows = (N + g - 1) / g, steps = (S + k - 1) / k;
+      const double stage_weight = fmt == HAD2 ? 1.0 : 0.5;
+      double cost = (double)((rows + 15) / 16) * steps * unit_bytes + stage_weight * steps * M * KSTEP * 2.0;
+      if (k > 1) cost += 8.0 * k * M * rows + 20480.0;
+      if (k == 1 || cost < best) { best = cost; ks = k; }
+    }
+  }
+  int rg = cus / ks;
+  if (rg > tiles) rg = tiles;
+  if (rg < 1) rg = 1;
+  p->ks = ks;
+  p->rg = rg;
+  p->grid = rg * ks;
+  const int rows_max = (N + rg - 1) / rg + 1;
+  p->tiles_max = (rows_max + 15) / 16 + 1;
+  const int s_wg = (S + ks - 1) / ks;
+  p->win_steps = window_steps(fmt, M, s_wg, p->tiles_max, dev.max_lds, &p->lds);
+  // Units in flight per wave: one when each wave streams only a few units (the first
+  // loads then reach the compute sooner), two for long streams; the 1-bit format's units
+  // are half as large and always keep two.
+  const int units_per_wave = ((rows_max + 15) / 16) * s_wg / NW;
+  p->pref = fmt == SIGN1 ? 2 : (units_per_wave < 8 ? 1 : 2);
+  return p->win_steps > 0;
+}
+
+size_t mfma_workspace_bytes(int M, int N, const MfmaPlan& p) {
+  return p.ks > 1 ? (size_t)p.ks * M * N * sizeof(float) : 0;
 }
 
 // Raises a kernel's dynamic-LDS limit once per device.
@@ -743,53 +827,50 @@ static hipError_t allow_lds(void (*kern)(MfmaArgs), std::atomic<uint64_t>& done,
 }
 
 template <int FMT, int MODE, int XT, int PREF>
-static hipError_t launch_kern(const MfmaArgs& A, int grid, size_t lds, hipStream_t stream, const DeviceInfo& dev) {
+static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t stream, const DeviceInfo& dev) {
   void (*kern)(MfmaArgs) = MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT, PREF> : vg_mfma_h<FMT, XT, PREF>;
   static std::atomic<uint64_t> attr_done{0};
   const hipError_t e = allow_lds(kern, attr_done, dev);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHREADS), lds, stream, A);
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(NTHREADS), p.lds, stream, A);
   return hipGetLastError();
 }
 
 template <int FMT, int MODE, int XT>
-static hipError_t launch_one(const GemmCall& c, const DeviceInfo& dev) {
-  const int grid = pick_grid(c.N, dev);
-  int ws = 0;
-  const size_t lds = mfma_lds_bytes(FMT, MODE, c.M, c.K, c.N, grid, dev.max_lds, &ws);
-  if (ws == 0) return hipErrorInvalidValue;
+static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, uint32_t* counters,
+                             const DeviceInfo& dev) {
+  if (p.win_steps <= 0 || (p.ks > 1 && (part == nullptr || counters == nullptr))) return hipErrorInvalidValue;
   MfmaArgs A;
   A.x = c.x; A.w = c.w; A.scales = c.scales; A.biases = c.biases; A.y = c.y;
   A.M = c.M; A.K = c.K; A.N = c.N;
-  A.win_steps = ws;
-  const int rows_max = (c.N + grid - 1) / grid + 1;
-  A.tiles_max = (rows_max + 15) / 16 + 1;
-  A.a_pitch = ws * fmt_gps(FMT) * fmt_gs(FMT) + 16;
+  A.win_steps = p.win_steps;
+  A.tiles_max = p.tiles_max;
+  A.a_pitch = p.win_steps * fmt_gps(FMT) * fmt_gs(FMT) + 16;
+  A.rg = p.rg;
+  A.ks = p.ks;
+  A.part = part;
+  A.counters = counters;
   for (int k = 0; k < 6; ++k) {
     if (FMT == SIGN1) {
-      const int p = 5 + k;   // positions 5..10
-      A.mask[k] = (1u << p) | (1u << (p + 16));
-      A.magic[k] = half_magic_sign1(p) | (half_magic_sign1(p) << 16);
+      const int q = 5 + k;   // positions 5..10
+      A.mask[k] = (1u << q) | (1u << (q + 16));
+      A.magic[k] = half_magic_sign1(q) | (half_magic_sign1(q) << 16);
     } else {
-      const int p = 4 + 2 * (k < 3 ? k : 2);   // positions 4, 6, 8
-      A.mask[k] = (3u << p) | (3u << (p + 16));
-      A.magic[k] = half_magic_affine2(p) | (half_magic_affine2(p) << 16);
+      const int q = 4 + 2 * (k < 3 ? k : 2);   // positions 4, 6, 8
+      A.mask[k] = (3u << q) | (3u << (q + 16));
+      A.magic[k] = half_magic_affine2(q) | (half_magic_affine2(q) << 16);
     }
   }
-  // Units in flight per wave: one when each wave streams only a few units (the first
-  // loads then reach the compute sooner), two for long streams; the 1-bit format's units
-  // are half as large and always keep two.
-  if (FMT == SIGN1) return launch_kern<FMT, MODE, XT, 2>(A, grid, lds, c.stream, dev);
-  const int units_per_wave = ((rows_max + 15) / 16) * (c.K / KSTEP) / NW;
-  if (units_per_wave < 8) return launch_kern<FMT, MODE, XT, 1>(A, grid, lds, c.stream, dev);
-  return launch_kern<FMT, MODE, XT, 2>(A, grid, lds, c.stream, dev);
+  if (FMT == SIGN1 || p.pref == 2) return launch_kern<FMT, MODE, XT, 2>(A, p, c.stream, dev);
+  return launch_kern<FMT, MODE, XT, 1>(A, p, c.stream, dev);
 }
 
-hipError_t launch_mfma(const GemmCall& c, int variant, const DeviceInfo& dev) {
+hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float* part, uint32_t* counters,
+                       const DeviceInfo& dev) {
 #define VG_DISPATCH_XT(FMT, MODE)                                                   \
   switch (c.xt) {                                                                    \
-    case XF16: return launch_one<FMT, MODE, XF16>(c, dev);                           \
-    case XBF16: return launch_one<FMT, MODE, XBF16>(c, dev);                         \
+    case XF16: return launch_one<FMT, MODE, XF16>(c, p, part, counters, dev);        \
+    case XBF16: return launch_one<FMT, MODE, XBF16>(c, p, part, counters, dev);      \
     default: return hipErrorInvalidValue;                                            \
   }
 #define VG_DISPATCH_MODE(FMT)                                                       \

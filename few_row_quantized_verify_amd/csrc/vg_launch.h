@@ -32,17 +32,32 @@ struct DeviceInfo {
   int max_lds;        // bytes per workgroup
 };
 
+// Launch plan of the MFMA variants for one call.
+struct MfmaPlan {
+  int grid;        // workgroups = rg * ks
+  int rg, ks;      // row groups, K slices (ks > 1: partials reduced by the last slice)
+  int win_steps;   // K-steps per staging window (0: the call does not fit)
+  int tiles_max;   // 16-row tiles per workgroup, upper bound
+  int pref;        // units in flight per wave
+  size_t lds;      // dynamic LDS bytes
+};
+
+// Plans an MFMA call; force_ks > 0 imposes that many K slices (capped at K/1024).
+// Returns false when the call cannot be staged in LDS.
+bool plan_mfma(int fmt, int variant, int M, int K, int N, const DeviceInfo& dev, int force_ks,
+               MfmaPlan* p);
+// Device workspace a planned call needs (partial outputs; 0 when K is not split).
+size_t mfma_workspace_bytes(int M, int N, const MfmaPlan& p);
+
 // Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
-hipError_t launch_mfma(const GemmCall& c, int variant, const DeviceInfo& dev);
+// part / counters: the call's workspace when p.ks > 1 (counters zero on entry; the
+// kernel leaves them zero).
+hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float* part,
+                       uint32_t* counters, const DeviceInfo& dev);
 hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev);
 hipError_t launch_hadamard(const void* x, int xt, int M, int K, float* out, hipStream_t s);
 hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, hipStream_t s);
 hipError_t launch_debug_unpack(int fmt, const uint32_t* w, int N, int K, uint8_t* codes,
                                hipStream_t s);
-
-// LDS bytes the MFMA kernel needs for a call, and the K-steps per staging window it uses
-// (0 if the call does not fit in `max_lds`).
-size_t mfma_lds_bytes(int fmt, int variant, int M, int K, int N, int grid, int max_lds,
-                      int* win_steps);
 
 }  // namespace vg

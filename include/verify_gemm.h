@@ -15,8 +15,13 @@
  *   - Arguments are validated on the host before anything is enqueued.  On error the call
  *     returns a non-zero vg_status, enqueues nothing, and vg_last_error() returns a message
  *     (per calling thread).
- *   - The library allocates no device memory in these calls.  It keeps a small read-only
- *     per-device state (device attributes) created on first use.
+ *   - The library keeps a small read-only per-device state (device attributes) created on
+ *     first use.  The GEMM calls allocate no device memory, except that a call whose K
+ *     the dispatch splits across workgroups (see vg_plan_ksplit) uses a workspace owned by
+ *     the library: one per device and stream, allocated on the first such call on that
+ *     stream (hipMalloc), grown when a larger call needs it (after synchronizing that
+ *     stream) and kept until the process ends.  Calls on one stream are ordered by the
+ *     stream; calls on different streams use different workspaces.
  *   - Activations x are row-major [M, K] of dtype VG_F32, VG_F16 or VG_BF16 (raw IEEE bits);
  *     outputs y are row-major fp32 [M, N]; rows >= M are never read or written.
  *   - Packed weights, row-major over the N output rows, little-endian words, LSB first:
@@ -129,6 +134,21 @@ vg_status vg_force_variant(int variant);
 
 /* Number of variants; variant ids are 0 .. vg_variant_count()-1. */
 int vg_variant_count(void);
+
+/*
+ * K slices the MFMA variants split a call into (1: each workgroup runs the whole K range
+ * of its output rows), or -1 for an invalid shape.  A workgroup stages the activations of
+ * its K range once per call; when that staging would exceed the packed bytes it streams,
+ * K is split across workgroups, each stages its slice, and the last slice of a row group
+ * to finish adds the partial outputs in slice order, so results do not depend on timing.
+ */
+int vg_plan_ksplit(int format, int x_dtype, int M, int N, int K);
+
+/*
+ * Force the K slices of later MFMA calls in this process (tests and timing); 0 restores
+ * the dispatch.  Values above K/1024 are capped.  VG_ERR_ARG outside 0..64.
+ */
+vg_status vg_force_ksplit(int ksplit);
 
 /*
  * Debug: decode the packed codes on the GPU into one byte per weight, codes[N, K] uint8

@@ -22,7 +22,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("verify_gemm_sign1", "verify_gemm_affine2", "verify_gemm_had2", "hadamard_rotate",
                "verify_argmax_rows", "vg_last_error", "vg_plan_variant", "vg_variant_name",
-               "vg_force_variant", "vg_variant_count", "vg_debug_unpack_sign1", "vg_debug_unpack_affine2"):
+               "vg_force_variant", "vg_variant_count", "vg_debug_unpack_sign1", "vg_debug_unpack_affine2",
+               "vg_plan_ksplit", "vg_force_ksplit"):
         assert fn in names, fn
 
 
@@ -122,3 +123,13 @@ def test_python_binding_rejects_unknown_dtype():
     with pytest.raises(vgm.VerifyGemmError) as e:
         vgm.verify_gemm_sign1(x, x, x)
     assert e.value.status == B.VG_ERR_DTYPE
+
+
+def test_force_ksplit_validation():
+    with pytest.raises(vgm.VerifyGemmError) as e:
+        vgm.force_ksplit(-1)
+    assert e.value.status == B.VG_ERR_ARG
+    with pytest.raises(vgm.VerifyGemmError):
+        vgm.force_ksplit(65)
+    vgm.force_ksplit(0)
+    assert vgm.plan_ksplit("sign1", "f16", 0, 16, 1024) == -1

@@ -282,3 +282,48 @@ def test_long_row_ranges_deep_ring(vg, fmt, x_dtype):
     cols = sample_cols(N, k=300, seed=1)
     for M in (1, 3, 8):
         check(case, M, run(vg, case, M), cols=cols, label="deep-ring")
+
+
+# ----------------------------------------------------------------------------- K split across workgroups
+@pytest.fixture
+def ksplit(vg):
+    yield vg.force_ksplit
+    vg.force_ksplit(0)
+
+
+@pytest.mark.parametrize("fmt,K,N,x_dtype", [("sign1", 5120, 300, "bf16"), ("affine2", 4096, 100, "f16"),
+                                             ("had2", 3072, 77, "f16")])
+@pytest.mark.parametrize("ks", [2, 3, 5])
+def test_forced_k_split(vg, ksplit, fmt, K, N, x_dtype, ks):
+    """K split across workgroups (capped at K/1024 slices), ragged row groups, every row
+    count; the result is the same bits on a repeated call (fixed slice order)."""
+    ksplit(ks)
+    case = draw_case(fmt, K, N, x_dtype, seed=20 + ks)
+    assert vg.plan_ksplit(fmt, x_dtype, 8, N, K) == min(ks, K // 1024)
+    for M in (1, 4, 5, 8):
+        y1 = run(vg, case, M)
+        check(case, M, y1, label=f"ksplit{ks}")
+        assert np.array_equal(y1, run(vg, case, M)), "split-K result changed between identical calls"
+
+
+def test_k_split_counters_reset_across_calls_and_streams(vg, ksplit):
+    """Consecutive split-K calls of different shapes on one stream, then on a second
+    stream: the arrival counters must be back at zero after every call."""
+    ksplit(4)
+    cases = [draw_case("sign1", 4096, 200, "bf16", seed=30), draw_case("affine2", 5120, 64, "f16", seed=31)]
+    for rep in range(3):
+        for case in cases:
+            check(case, 8, run(vg, case, 8), label=f"ks-seq{rep}")
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        for case in cases:
+            x, w, s, b = case_tensors(case, 6)
+            y = vg.verify_gemm(case.fmt, x, w, s, b)
+            s2.synchronize()
+            check(case, 6, y.cpu().numpy().astype(np.float64), label="ks-stream2")
+
+
+def test_dispatch_splits_tall_k(vg):
+    assert vg.plan_ksplit("sign1", "bf16", 8, 5120, 17408) > 1
+    assert vg.plan_ksplit("affine2", "f16", 1, 17408, 5120) == 1
+    assert vg.plan_ksplit("affine2", "f16", 8, 151936, 5120) == 1
