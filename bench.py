@@ -16,6 +16,8 @@ t(M=8)/t(M=1), a roofline object for the dominant kernel and the CPU oracle base
 Options:
   --workload NAME    another named workload (see synthetic.inputs.WORKLOADS)
   --m LIST           only these row counts, e.g. "8" (for profiling one kernel)
+  --force-variant V  run every call on kernel variant V (vg_mfma_q, vg_mfma_h, vg_valu)
+                     instead of the per-shape dispatch, for A/B timing
   --table            also print one JSON line per workload and M (not the default)
   --no-cpu           skip the CPU oracle baseline leg
   --copy-calibration run only a device-to-device copy of known size (for HBM counters)
@@ -170,6 +172,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--m", default=None)
+    ap.add_argument("--force-variant", default=None)
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR", default=None)
     args = ap.parse_args()
     if args.ingest_counters:
@@ -186,6 +189,12 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.force_variant:
+        names_v = [vg.variant_name(i) for i in range(vg.variant_count())]
+        if args.force_variant not in names_v:
+            print(f"unknown variant {args.force_variant!r}; one of {names_v}", file=sys.stderr)
+            return 2
+        vg.force_variant(names_v.index(args.force_variant))
 
     if args.copy_calibration:
         nbytes = 256 << 20

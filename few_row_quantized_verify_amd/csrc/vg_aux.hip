@@ -46,13 +46,24 @@ __device__ void lds_fwht(float* xs, int M, int len) {
   }
 }
 
-// One thread per output row; exact fp32 dequantization, fp32 fused multiply-adds.
+// VALU kernel: exact fp32 dequantization and fp32 fused multiply-adds.  A workgroup takes
+// VALU_ROWS output rows; the VALU_PARTS threads of a row split its words round-robin (part
+// p takes words p, p + VALU_PARTS, ...), so neighbouring threads read neighbouring words of
+// a row and threads of equal part read the same activations (an LDS broadcast).  The parts
+// are added in part order through LDS, so results do not depend on timing.
+constexpr int VALU_PARTS = 8;
+constexpr int VALU_ROWS = VALU_THREADS / VALU_PARTS;
+
 template <int FMT>
 __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
   __shared__ float xs[MAXM * VALU_WK];
-  const int n = blockIdx.x * VALU_THREADS + threadIdx.x;
-  const bool live = n < A.N;
+  __shared__ float red[VALU_ROWS][VALU_PARTS][MAXM];
   constexpr int G = FMT == SIGN1 ? 128 : 64;
+  constexpr int WK = FMT == SIGN1 ? 32 : 16;   // K per word
+  const int part = threadIdx.x % VALU_PARTS, lr = threadIdx.x / VALU_PARTS;
+  const int n = blockIdx.x * VALU_ROWS + lr;
+  const bool live = n < A.N;
+  const size_t wrow = (size_t)n * (A.K / WK), grow = (size_t)n * (A.K / G);
   float acc[MAXM];
 #pragma unroll
   for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
@@ -70,42 +81,49 @@ __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
       __syncthreads();
     }
     if (live) {
-      if constexpr (FMT == SIGN1) {
-        for (int wi = 0; wi < len / 32; ++wi) {
-          const int k = k0 + 32 * wi;
-          const uint32_t word = A.w[(size_t)n * (A.K / 32) + k / 32];
-          const float s = h2f(A.scales[(size_t)n * (A.K / G) + k / G]);
+      for (int wi = part; wi < len / WK; wi += VALU_PARTS) {
+        const int k = k0 + WK * wi;
+        const uint32_t word = A.w[wrow + k / WK];
+        const size_t gi = grow + k / G;
+        const float sc = h2f(A.scales[gi]);
+        const float* xw = xs + WK * wi;
+        if constexpr (FMT == SIGN1) {
+#pragma unroll 4
           for (int bit = 0; bit < 32; ++bit) {
-            const float wv = ((word >> bit) & 1u) ? s : -s;
+            const float wv = ((word >> bit) & 1u) ? sc : -sc;
 #pragma unroll
             for (int m = 0; m < MAXM; ++m)
-              if (m < A.M) acc[m] = __builtin_fmaf(xs[m * len + 32 * wi + bit], wv, acc[m]);
+              if (m < A.M) acc[m] = __builtin_fmaf(xw[m * len + bit], wv, acc[m]);
           }
-        }
-      } else {
-        for (int wi = 0; wi < len / 16; ++wi) {
-          const int k = k0 + 16 * wi;
-          const uint32_t word = A.w[(size_t)n * (A.K / 16) + k / 16];
-          const size_t gi = (size_t)n * (A.K / G) + k / G;
-          const float s = h2f(A.scales[gi]), b = h2f(A.biases[gi]);
+        } else {
+          const float b = h2f(A.biases[gi]);
+#pragma unroll 4
           for (int c = 0; c < 16; ++c) {
-            const float wv = (float)((word >> (2 * c)) & 3u) * s + b;   // exact in fp32
+            const float wv = (float)((word >> (2 * c)) & 3u) * sc + b;   // exact in fp32
 #pragma unroll
             for (int m = 0; m < MAXM; ++m)
-              if (m < A.M) acc[m] = __builtin_fmaf(xs[m * len + 16 * wi + c], wv, acc[m]);
+              if (m < A.M) acc[m] = __builtin_fmaf(xw[m * len + c], wv, acc[m]);
           }
         }
       }
     }
   }
-  if (live)
-    for (int m = 0; m < A.M; ++m) A.y[(size_t)m * A.N + n] = acc[m];
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) red[lr][part][m] = acc[m];
+  __syncthreads();
+  if (part == 0 && live) {
+    for (int m = 0; m < A.M; ++m) {
+      float sum = 0.0f;
+      for (int q = 0; q < VALU_PARTS; ++q) sum += red[lr][q][m];
+      A.y[(size_t)m * A.N + n] = sum;
+    }
+  }
 }
 
 hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev) {
   (void)dev;
   ValuArgs A{c.x, c.xt, c.w, c.scales, c.biases, c.y, c.M, c.K, c.N};
-  const dim3 grid((c.N + VALU_THREADS - 1) / VALU_THREADS);
+  const dim3 grid((c.N + VALU_ROWS - 1) / VALU_ROWS);
   switch (c.fmt) {
     case SIGN1: hipLaunchKernelGGL(vg_valu<SIGN1>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
     case AFFINE2: hipLaunchKernelGGL(vg_valu<AFFINE2>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
