@@ -9,6 +9,9 @@ kernels run on), and cycles through a pool of >= 1 GiB of distinct weight copies
 256 MB Infinity Cache cannot serve repeated calls.  Inputs are resident in HBM before
 timing starts.
 
+For the output-head workload a call is the verify GEMM followed by the argmax of every row
+(the head's argmax step), so its per-M times include both kernels.
+
 Prints one JSON line: value = packed-weight bytes (codes + fp16 scales + fp16 biases)
 moved per second over all timed calls (GB/s, 1e9), plus per-M microseconds per call,
 t(M=8)/t(M=1), a roofline object for the dominant kernel and the CPU oracle baseline.
@@ -223,10 +226,14 @@ def main() -> int:
         b0 = f16_tensor(case.biases, dev) if case.biases is not None else None
         pool = [(w0.clone(), s0.clone(), None if b0 is None else b0.clone()) for _ in range(ncopy)]
         ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
+        head = name.startswith("head_")
+        idx = {M: torch.empty((M,), dtype=torch.int32, device=dev) for M in Ms}
 
         def call(M, j):
             w, s, b = pool[j % ncopy]
             vg.verify_gemm(fmt, x_all[M], w, s, b, y=ys[M])
+            if head:
+                vg.verify_argmax_rows(ys[M], idx=idx[M])
 
         for M in Ms:
             for j in range(args.warmup):

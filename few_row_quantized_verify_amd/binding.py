@@ -39,6 +39,7 @@ _SIGS = {
     "verify_gemm_had2": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P]),
     "hadamard_rotate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "verify_argmax_rows": (_I, [_P, _I, _I, _P, _P]),
+    "verify_accept_greedy": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "vg_last_error": (ctypes.c_char_p, []),
     "vg_plan_variant": (_I, [_I, _I, _I, _I, _I]),
     "vg_variant_name": (ctypes.c_char_p, [_I]),
@@ -158,6 +159,19 @@ def verify_argmax_rows(y, idx=None, stream=None):
         idx = torch.empty((M,), dtype=torch.int32, device=y.device)
     _check(lib().verify_argmax_rows(_ptr(y), M, N, _ptr(idx), _stream(stream)))
     return idx
+
+
+def verify_accept_greedy(y, draft, idx=None, accepted=None, stream=None):
+    """(idx, accepted): per-row argmax of the logits y [M, N] and the number of leading rows
+    whose argmax equals draft[m] (draft: int32 [M] on the device)."""
+    torch = _torch()
+    M, N = y.shape
+    if idx is None:
+        idx = torch.empty((M,), dtype=torch.int32, device=y.device)
+    if accepted is None:
+        accepted = torch.empty((1,), dtype=torch.int32, device=y.device)
+    _check(lib().verify_accept_greedy(_ptr(y), M, N, _ptr(draft), _ptr(idx), _ptr(accepted), _stream(stream)))
+    return idx, accepted
 
 
 def debug_unpack(fmt: str, w, K, codes=None, stream=None):

@@ -175,11 +175,36 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
     float* part = nullptr;
     uint32_t* counters = nullptr;
     if (p.ks > 1) {
-      if (p.rg * 4 > static_cast<int>(kCounterBytes)) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
+      if (p.rg > 768) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
       if (vg_status s = workspace(dev.id, c.stream, vg::mfma_workspace_bytes(M, N, p), &part, &counters)) return s;
     }
     e = vg::launch_mfma(c, var, p, part, counters, dev);
   }
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return VG_OK;
+}
+
+// Counters of the argmax kernel sit above those of the K-split reductions in the workspace.
+constexpr int kArgmaxCounterBase = 768;
+
+vg_status run_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
+                     void* stream) {
+  if (M < 1 || M > VG_MAX_ROWS) return fail(VG_ERR_SHAPE, "M=%d outside 1..%d", M, VG_MAX_ROWS);
+  if (N < 1) return fail(VG_ERR_SHAPE, "N=%d < 1", N);
+  if (!y) return fail(VG_ERR_ARG, "y is null");
+  if (reinterpret_cast<uintptr_t>(y) & 3u) return fail(VG_ERR_ALIGN, "y is not 4-byte aligned");
+  if (!idx) return fail(VG_ERR_ARG, "idx is null");
+  if ((draft == nullptr) != (accepted == nullptr)) return fail(VG_ERR_ARG, "draft and accepted go together");
+  vg::DeviceInfo dev;
+  if (vg_status s = device_info(&dev)) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t parts = (size_t)vg::argmax_chunks(N) * M;
+  float* part = nullptr;
+  uint32_t* counters = nullptr;
+  if (vg_status s = workspace(dev.id, st, parts * 8, &part, &counters)) return s;
+  const hipError_t e = vg::launch_argmax(y, M, N, idx, draft, accepted, part, reinterpret_cast<int32_t*>(part + parts),
+                                         counters + kArgmaxCounterBase, st);
   if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return VG_OK;
@@ -238,14 +263,13 @@ vg_status hadamard_rotate(const void* x, int x_dtype, int M, int K, int block, f
 }
 
 vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* stream) {
-  if (M < 1 || M > VG_MAX_ROWS) return fail(VG_ERR_SHAPE, "M=%d outside 1..%d", M, VG_MAX_ROWS);
-  if (N < 1) return fail(VG_ERR_SHAPE, "N=%d < 1", N);
-  if (vg_status s = check_ptr(y, "y")) return s;
-  if (vg_status s = check_ptr(idx, "idx")) return s;
-  const hipError_t e = vg::launch_argmax(y, M, N, idx, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  g_err[0] = '\0';
-  return VG_OK;
+  return run_argmax(y, M, N, idx, nullptr, nullptr, stream);
+}
+
+vg_status verify_accept_greedy(const float* y, int M, int N, const int32_t* draft, int32_t* idx,
+                               int32_t* accepted, void* stream) {
+  if (!draft || !accepted) return fail(VG_ERR_ARG, "draft or accepted is null");
+  return run_argmax(y, M, N, idx, draft, accepted, stream);
 }
 
 const char* vg_last_error(void) { return g_err; }

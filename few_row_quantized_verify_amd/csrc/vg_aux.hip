@@ -10,6 +10,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int VALU_THREADS = 256;
 constexpr int VALU_WK = 2048;   // K per LDS window (fp32 activations, 8 rows: 64 KB)
 constexpr int MAXM = 8;
+constexpr int VG_MAX_ROWS_DEV = 8;   // counters[0..7]: rows; counters[8]: finished rows
 
 __device__ __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 __device__ __forceinline__ float x_at(const void* x, int xt, size_t idx) {
@@ -175,37 +176,96 @@ hipError_t launch_hadamard(const void* x, int xt, int M, int K, float* out, hipS
 }
 
 // ---------------------------------------------------------------------------------------
-// Per-row argmax of fp32 logits, lowest index on ties, NaN never selected (a row of only
-// NaN gives index 0).  One workgroup per row.
-__global__ __launch_bounds__(1024) void vg_argmax_kernel(const float* y, int N, int32_t* idx) {
-  __shared__ float sv[1024];
-  __shared__ int si[1024];
-  const int m = blockIdx.x;
-  const float* row = y + (size_t)m * N;
-  float best = -INFINITY;
-  int bi = -1;
-  for (int n = threadIdx.x; n < N; n += 1024) {
-    const float v = row[n];
-    if (v > best || (bi < 0 && v == v)) { best = v; bi = n; }
-  }
-  sv[threadIdx.x] = best;
-  si[threadIdx.x] = bi;
+// Per-row argmax of fp32 logits over the whole chip, then (optionally) greedy acceptance of
+// a drafted block.  Block (c, m) scans columns [c*ARG_CHUNK, ...) of row m and parks its
+// (value, index); the last chunk of a row to arrive combines the row's chunks in chunk
+// order, and the last row to finish counts the leading rows whose argmax equals the
+// drafted token ("dflash-mlx-bonsai2" README, "Verify it yourself": greedy acceptance and
+// argmax parity).  Lowest index on ties; NaN is never selected (a row of only NaN gives 0).
+// The parked values and the counters are agent-scope atomic accesses (they bypass the
+// per-XCD L2 caches), so no device-wide fence is needed.
+constexpr int ARG_THREADS = 256;
+constexpr int ARG_PER_THREAD = 8;                          // loads in flight per thread
+constexpr int ARG_CHUNK = ARG_THREADS * ARG_PER_THREAD;    // columns per block
+
+__device__ __forceinline__ bool arg_better(float v2, int i2, float v1, int i1) {
+  return i2 >= 0 && (i1 < 0 || v2 > v1 || (v2 == v1 && i2 < i1));
+}
+
+// Block-wide (value, index) selection; the rule (larger value, then lower index, NaN and
+// empty never win) is order-independent, so the result does not depend on the tree shape.
+__device__ __forceinline__ void arg_block_reduce(float* sv, int* si, float v, int i) {
+  sv[threadIdx.x] = v;
+  si[threadIdx.x] = i;
   __syncthreads();
-  for (int off = 512; off > 0; off >>= 1) {
-    if (threadIdx.x < off) {
-      const float v2 = sv[threadIdx.x + off];
-      const int i2 = si[threadIdx.x + off];
-      const int i1 = si[threadIdx.x];
-      const bool take = i2 >= 0 && (i1 < 0 || v2 > sv[threadIdx.x] || (v2 == sv[threadIdx.x] && i2 < i1));
-      if (take) { sv[threadIdx.x] = v2; si[threadIdx.x] = i2; }
+  for (int off = ARG_THREADS / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < off && arg_better(sv[threadIdx.x + off], si[threadIdx.x + off], sv[threadIdx.x], si[threadIdx.x])) {
+      sv[threadIdx.x] = sv[threadIdx.x + off];
+      si[threadIdx.x] = si[threadIdx.x + off];
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) idx[m] = si[0] < 0 ? 0 : si[0];
 }
 
-hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, hipStream_t s) {
-  hipLaunchKernelGGL(vg_argmax_kernel, dim3(M), dim3(1024), 0, s, y, N, idx);
+__global__ __launch_bounds__(ARG_THREADS) void vg_argmax_kernel(const float* y, int M, int N, int32_t* idx,
+                                                              const int32_t* draft, int32_t* accepted,
+                                                              float* pval, int32_t* pidx, uint32_t* counters) {
+  __shared__ float sv[ARG_THREADS];
+  __shared__ int si[ARG_THREADS];
+  __shared__ uint32_t last;
+  const int c = blockIdx.x, m = blockIdx.y, C = gridDim.x;
+  const float* row = y + (size_t)m * N;
+  const int n0 = c * ARG_CHUNK + threadIdx.x;
+  float v[ARG_PER_THREAD];
+#pragma unroll
+  for (int e = 0; e < ARG_PER_THREAD; ++e) {
+    const int n = n0 + e * ARG_THREADS;
+    v[e] = n < N ? row[n] : __builtin_nanf("");
+  }
+  float best = -INFINITY;
+  int bi = -1;
+#pragma unroll
+  for (int e = 0; e < ARG_PER_THREAD; ++e)
+    if (v[e] > best || (bi < 0 && v[e] == v[e])) { best = v[e]; bi = n0 + e * ARG_THREADS; }
+  arg_block_reduce(sv, si, best, bi);
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(pval + m * C + c, sv[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(pidx + m * C + c, si[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial has landed
+    last = __hip_atomic_fetch_add(counters + m, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(C - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  // last chunk of row m to finish: select among the row's C partials
+  best = -INFINITY;
+  bi = -1;
+  for (int k = threadIdx.x; k < C; k += ARG_THREADS) {
+    const float pv = __hip_atomic_load(pval + m * C + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int pi = __hip_atomic_load(pidx + m * C + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (arg_better(pv, pi, best, bi)) { best = pv; bi = pi; }
+  }
+  arg_block_reduce(sv, si, best, bi);
+  if (threadIdx.x != 0) return;
+  const int32_t am = si[0] < 0 ? 0 : si[0];
+  __hip_atomic_store(idx + m, am, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(counters + m, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (draft == nullptr) return;
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (__hip_atomic_fetch_add(counters + VG_MAX_ROWS_DEV, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)(M - 1))
+    return;
+  // last row to finish: the drafted prefix the target agrees with
+  int L = 0;
+  while (L < M && __hip_atomic_load(idx + L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == draft[L]) ++L;
+  accepted[0] = L;
+  __hip_atomic_store(counters + VG_MAX_ROWS_DEV, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+int argmax_chunks(int N) { return (N + ARG_CHUNK - 1) / ARG_CHUNK; }
+
+hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
+                         float* pval, int32_t* pidx, uint32_t* counters, hipStream_t s) {
+  hipLaunchKernelGGL(vg_argmax_kernel, dim3(argmax_chunks(N), M), dim3(ARG_THREADS), 0, s, y, M, N, idx, draft,
+                     accepted, pval, pidx, counters);
   return hipGetLastError();
 }
 

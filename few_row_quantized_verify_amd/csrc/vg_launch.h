@@ -56,7 +56,12 @@ hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float*
                        uint32_t* counters, const DeviceInfo& dev);
 hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev);
 hipError_t launch_hadamard(const void* x, int xt, int M, int K, float* out, hipStream_t s);
-hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, hipStream_t s);
+// Argmax of each row over the whole chip; with draft/accepted non-null also the greedy
+// acceptance count.  pval/pidx: argmax_chunks(N) * M partials; counters: 9 zeroed words
+// (left zeroed).
+int argmax_chunks(int N);
+hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
+                         float* pval, int32_t* pidx, uint32_t* counters, hipStream_t s);
 hipError_t launch_debug_unpack(int fmt, const uint32_t* w, int N, int K, uint8_t* codes,
                                hipStream_t s);
 

@@ -17,11 +17,12 @@
  *     (per calling thread).
  *   - The library keeps a small read-only per-device state (device attributes) created on
  *     first use.  The GEMM calls allocate no device memory, except that a call whose K
- *     the dispatch splits across workgroups (see vg_plan_ksplit) uses a workspace owned by
- *     the library: one per device and stream, allocated on the first such call on that
- *     stream (hipMalloc), grown when a larger call needs it (after synchronizing that
- *     stream) and kept until the process ends.  Calls on one stream are ordered by the
- *     stream; calls on different streams use different workspaces.
+ *     the dispatch splits across workgroups (see vg_plan_ksplit), and the argmax and
+ *     acceptance calls, use a workspace owned by the library: one per device and stream,
+ *     allocated on the first such call on that stream (hipMalloc), grown when a larger
+ *     call needs it (after synchronizing that stream) and kept until the process ends.
+ *     Calls on one stream are ordered by the stream; calls on different streams use
+ *     different workspaces.
  *   - Activations x are row-major [M, K] of dtype VG_F32, VG_F16 or VG_BF16 (raw IEEE bits);
  *     outputs y are row-major fp32 [M, N]; rows >= M are never read or written.
  *   - Packed weights, row-major over the N output rows, little-endian words, LSB first:
@@ -108,11 +109,24 @@ vg_status hadamard_rotate(const void* x, int x_dtype, int M, int K, int block,
                           float* x_out, void* stream);
 
 /*
- * idx[m] = argmax_n y[m, n] for m < M (lowest n on ties; NaN never wins), for the output
- * head of a verify pass.  y is fp32 [M, N] row-major, idx is int32 [M].
- * Requires 1 <= M <= 8, N >= 1.
+ * idx[m] = argmax_n y[m, n] for m < M (lowest n on ties; NaN never wins; a row of only
+ * NaN gives 0), for the output head of a verify pass ("dflash-mlx-bonsai2" README, "Verify
+ * it yourself": the verify is checked by its argmax).  y is fp32 [M, N] row-major (4-byte
+ * aligned), idx is int32 [M].  Requires 1 <= M <= 8, N >= 1.  Uses the per-stream workspace
+ * described above (the argmax of each row is split over the whole chip).
  */
 vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* stream);
+
+/*
+ * Greedy acceptance of a drafted block: idx[m] = argmax_n y[m, n] as verify_argmax_rows,
+ * and accepted[0] = the number of leading rows m with idx[m] == draft[m] (0..M), i.e. the
+ * length of the drafted prefix the target model agrees with; when it is below M,
+ * idx[accepted[0]] is the target's own token at the first disagreement.  draft is int32
+ * [M] on the device; accepted is int32 [1] on the device.  Same requirements as
+ * verify_argmax_rows; draft and accepted must be non-null.
+ */
+vg_status verify_accept_greedy(const float* y, int M, int N, const int32_t* draft, int32_t* idx,
+                               int32_t* accepted, void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* vg_last_error(void);

@@ -233,6 +233,19 @@ def argmax_rows(y: np.ndarray):
     return idx.astype(np.int64), top2[:, 1] - top2[:, 0]
 
 
+def greedy_accept(y: np.ndarray, draft: np.ndarray):
+    """Greedy acceptance of a drafted block ("dflash-mlx-bonsai2" README, "Verify it
+    yourself": the verify keeps the drafted tokens the target's argmax agrees with).
+    Returns (argmax per row, L) with L the number of leading rows m whose argmax equals
+    draft[m]."""
+    idx, _ = argmax_rows(y)
+    draft = np.asarray(draft).reshape(-1)
+    L = 0
+    while L < len(idx) and idx[L] == draft[L]:
+        L += 1
+    return idx, L
+
+
 def normwise_rel_err(y_test: np.ndarray, y_ref: np.ndarray) -> float:
     """max over rows m of  max_n |y_test - y_ref| / max_n |y_ref|."""
     y_test = np.asarray(y_test, dtype=np.float64)

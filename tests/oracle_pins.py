@@ -394,8 +394,27 @@ def pin_magnitude(ref):
                   ref.verify("affine2", x, "f16", words, s, b), rtol=1e-13, atol=0)
 
 
+def pin_greedy_accept(ref):
+    """Leading-agreement count on planted logits: all rows agree, none agree, the first
+    disagreement in the middle, and a disagreement after it that must not count."""
+    rng = np.random.default_rng(15)
+    y = rng.standard_normal((6, 50))
+    top = np.array([3, 17, 17, 0, 49, 8])
+    y[np.arange(6), top] = 10.0
+    idx, L = ref.greedy_accept(y, top)
+    assert list(idx) == list(top) and L == 6
+    assert ref.greedy_accept(y, top + 1)[1] == 0
+    d = top.copy()
+    d[2] = 5
+    assert ref.greedy_accept(y, d)[1] == 2
+    d[4] = 0
+    assert ref.greedy_accept(y, d)[1] == 2
+    y[1, 20] = 10.0                      # tie in row 1: the lower index (17) still wins
+    assert ref.greedy_accept(y, top)[1] == 6
+
+
 ALL_PINS = [pin_decode, pin_unpack_hand_words, pin_pack_roundtrip, pin_golden,
             pin_sign1_closed_form, pin_affine2_known_codes, pin_rowsum_identity,
             pin_bruteforce_fraction, pin_hadamard_identities, pin_had2_weight_side,
             pin_mlx_1bit_encoding, pin_argmax, pin_columns_and_chunks, pin_normwise,
-            pin_magnitude]
+            pin_magnitude, pin_greedy_accept]

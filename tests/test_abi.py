@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     for fn in ("verify_gemm_sign1", "verify_gemm_affine2", "verify_gemm_had2", "hadamard_rotate",
                "verify_argmax_rows", "vg_last_error", "vg_plan_variant", "vg_variant_name",
                "vg_force_variant", "vg_variant_count", "vg_debug_unpack_sign1", "vg_debug_unpack_affine2",
-               "vg_plan_ksplit", "vg_force_ksplit"):
+               "vg_plan_ksplit", "vg_force_ksplit", "verify_accept_greedy"):
         assert fn in names, fn
 
 
@@ -133,3 +133,11 @@ def test_force_ksplit_validation():
         vgm.force_ksplit(65)
     vgm.force_ksplit(0)
     assert vgm.plan_ksplit("sign1", "f16", 0, 16, 1024) == -1
+
+
+def test_accept_greedy_validation():
+    L = B.lib()
+    assert L.verify_accept_greedy(ALIGNED, 2, 100, None, ALIGNED, ALIGNED, None) == B.VG_ERR_ARG
+    assert L.verify_accept_greedy(ALIGNED, 2, 100, ALIGNED, ALIGNED, None, None) == B.VG_ERR_ARG
+    assert L.verify_accept_greedy(ALIGNED, 9, 100, ALIGNED, ALIGNED, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.verify_accept_greedy(ALIGNED + 2, 2, 100, ALIGNED, ALIGNED, ALIGNED, None) == B.VG_ERR_ALIGN

@@ -327,3 +327,58 @@ def test_dispatch_splits_tall_k(vg):
     assert vg.plan_ksplit("sign1", "bf16", 8, 5120, 17408) > 1
     assert vg.plan_ksplit("affine2", "f16", 1, 17408, 5120) == 1
     assert vg.plan_ksplit("affine2", "f16", 8, 151936, 5120) == 1
+
+
+# ----------------------------------------------------------------------------- greedy acceptance
+def test_argmax_many_chunks_and_ties(vg):
+    """Rows longer than one chunk: the winner in a later chunk, a tie across chunks (the
+    lower index wins), NaN and -inf rows."""
+    rng = np.random.default_rng(40)
+    N = 70001
+    y = rng.standard_normal((8, N)).astype(np.float32)
+    y[0, 65000] = 9.0
+    y[1, 100] = y[1, 50000] = 9.0
+    y[2, :] = np.nan
+    y[3, :] = -np.inf
+    y[3, 40000] = np.nan
+    y[4, 16384] = 7.0
+    y[4, 16383] = 7.0
+    idx = vg.verify_argmax_rows(torch.from_numpy(y).cuda()).cpu().numpy()
+    assert idx[0] == 65000 and idx[1] == 100 and idx[2] == 0 and idx[4] == 16383
+    assert idx[3] == 0
+    yy = np.where(np.isnan(y), -np.inf, y)
+    assert list(idx[5:]) == list(np.argmax(yy[5:], axis=1))
+
+
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_accept_greedy_planted(vg, M):
+    rng = np.random.default_rng(41 + M)
+    N = 151936
+    y = rng.standard_normal((M, N)).astype(np.float32)
+    top = rng.integers(0, N, size=M)
+    y[np.arange(M), top] = 20.0
+    yt = torch.from_numpy(y).cuda()
+    for k in range(M + 1):
+        d = top.copy()
+        if k < M:
+            d[k] = (d[k] + 1) % N
+        idx, acc = vg.verify_accept_greedy(yt, torch.from_numpy(d.astype(np.int32)).cuda())
+        ref_idx, ref_L = oracle.greedy_accept(y, d)
+        assert list(idx.cpu().numpy()) == list(ref_idx)
+        assert int(acc.cpu().numpy()[0]) == ref_L == k
+
+
+def test_accept_greedy_on_head_logits(vg):
+    """The verify GEMM of the output head followed by greedy acceptance, against the
+    oracle's argmax of the same workload with a drafted block that diverges at row 3."""
+    with open(os.path.join(GOLDEN, "head_affine2_k5120_n151936_argmax.json")) as f:
+        gold = json.load(f)
+    case = workload_case(gold["workload"], seed=gold["seed"])
+    M = 7
+    x, w, s, b = case_tensors(case, M)
+    y = vg.verify_gemm_affine2(x, w, s, b)
+    draft = np.array(gold["argmax"][:M], dtype=np.int32)
+    draft[3] = (draft[3] + 5) % case.N
+    idx, acc = vg.verify_accept_greedy(y, torch.from_numpy(draft).cuda())
+    assert list(idx.cpu().numpy()) == gold["argmax"][:M]
+    assert int(acc.cpu().numpy()[0]) == 3

@@ -155,12 +155,19 @@ def _mut_magnitude_unrotated(m):
     m.magnitude_columns = magnitude_columns
 
 
+def _mut_accept_counts_all_matches(m):
+    def greedy_accept(y, draft):
+        idx, _ = m.argmax_rows(y)
+        return idx, int(np.sum(idx == np.asarray(draft).reshape(-1)))
+    m.greedy_accept = greedy_accept
+
+
 MUTATIONS = [_mut_sign1_msb_first, _mut_affine2_code_order, _mut_sign_polarity, _mut_drop_bias,
              _mut_sign1_group_size, _mut_affine2_group_index, _mut_hadamard_unnormalized,
              _mut_hadamard_wrong_recursion, _mut_hadamard_skipped, _mut_bf16_shift,
              _mut_f16_as_bf16, _mut_rows_reversed, _mut_chunk_offset, _mut_argmax_last_tie,
              _mut_normwise_elementwise, _mut_magnitude_signed_x,
-             _mut_magnitude_unrotated]
+             _mut_magnitude_unrotated, _mut_accept_counts_all_matches]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__[5:])
