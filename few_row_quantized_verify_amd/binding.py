@@ -17,8 +17,8 @@ VG_OK, VG_ERR_ARG, VG_ERR_SHAPE, VG_ERR_ALIGN, VG_ERR_DTYPE, VG_ERR_UNSUPPORTED,
 STATUS_NAMES = ["VG_OK", "VG_ERR_ARG", "VG_ERR_SHAPE", "VG_ERR_ALIGN", "VG_ERR_DTYPE",
                 "VG_ERR_UNSUPPORTED", "VG_ERR_HIP"]
 VG_F32, VG_F16, VG_BF16 = 0, 1, 2
-FMT_SIGN1, FMT_AFFINE2, FMT_HAD2 = 0, 1, 2
-FORMATS = {"sign1": FMT_SIGN1, "affine2": FMT_AFFINE2, "had2": FMT_HAD2}
+FMT_SIGN1, FMT_AFFINE2, FMT_HAD2, FMT_AFFINE1 = 0, 1, 2, 3
+FORMATS = {"sign1": FMT_SIGN1, "affine2": FMT_AFFINE2, "had2": FMT_HAD2, "affine1": FMT_AFFINE1}
 DTYPES = {"f32": VG_F32, "f16": VG_F16, "bf16": VG_BF16}
 
 
@@ -35,6 +35,7 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SIGS = {
     "verify_gemm_sign1": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P]),
+    "verify_gemm_affine1": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
     "verify_gemm_affine2": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
     "verify_gemm_had2": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P]),
     "hadamard_rotate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
@@ -123,6 +124,16 @@ def verify_gemm_affine2(x, wq, scales, biases, y=None, stream=None):
     return y
 
 
+def verify_gemm_affine1(x, wbits, scales, biases, y=None, stream=None):
+    """y[M, N] = x[M, K] @ W^T, W MLX 1-bit affine g128 (wbits int32 [N, K/32], scales/biases fp16 [N, K/128])."""
+    M, K = x.shape
+    N = wbits.shape[0]
+    y = _out(y, M, N, x.device)
+    _check(lib().verify_gemm_affine1(_ptr(x), _xdtype(x), M, K, _ptr(wbits), _ptr(scales),
+                                     _ptr(biases), N, _ptr(y), _stream(stream)))
+    return y
+
+
 def verify_gemm_had2(x, wq, scales, biases, had_block=128, y=None, stream=None):
     """y = (x @ blockdiag(H_128/sqrt(128))) @ W^T with W 2-bit affine g64."""
     M, K = x.shape
@@ -140,6 +151,8 @@ def verify_gemm(fmt: str, x, w, scales, biases=None, y=None, stream=None):
         return verify_gemm_affine2(x, w, scales, biases, y, stream)
     if fmt == "had2":
         return verify_gemm_had2(x, w, scales, biases, 128, y, stream)
+    if fmt == "affine1":
+        return verify_gemm_affine1(x, w, scales, biases, y, stream)
     raise ValueError(fmt)
 
 

@@ -224,6 +224,18 @@ vg_status verify_gemm_sign1(const void* x, int x_dtype, int M, int K, const uint
   return run_gemm(vg::SIGN1, x, x_dtype, M, K, wbits, scales, nullptr, N, y, stream);
 }
 
+vg_status verify_gemm_affine1(const void* x, int x_dtype, int M, int K, const uint32_t* wbits,
+                              const uint16_t* scales, const uint16_t* biases, int N, float* y,
+                              void* stream) {
+  if (vg_status s = check_common(x, x_dtype, M, K, N)) return s;
+  if (K % 128 != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of 128 (1-bit affine group)", K);
+  if (vg_status s = check_ptr(wbits, "wbits")) return s;
+  if (vg_status s = check_ptr(scales, "scales")) return s;
+  if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_ptr(y, "y")) return s;
+  return run_gemm(vg::AFFINE1, x, x_dtype, M, K, wbits, scales, biases, N, y, stream);
+}
+
 vg_status verify_gemm_affine2(const void* x, int x_dtype, int M, int K, const uint32_t* wq,
                               const uint16_t* scales, const uint16_t* biases, int N, float* y,
                               void* stream) {
@@ -275,9 +287,9 @@ vg_status verify_accept_greedy(const float* y, int M, int N, const int32_t* draf
 const char* vg_last_error(void) { return g_err; }
 
 int vg_plan_variant(int format, int x_dtype, int M, int N, int K) {
-  if (format < 0 || format > 2) return -1;
+  if (format < 0 || format > 3) return -1;
   if (x_dtype < 0 || x_dtype > 2 || M < 1 || M > VG_MAX_ROWS || N < 1 || K < 1) return -1;
-  if (K % (format == vg::SIGN1 || format == vg::HAD2 ? 128 : 64) != 0) return -1;
+  if (K % (format == vg::AFFINE2 ? 64 : 128) != 0) return -1;
   std::call_once(g_env_once, read_env);
   vg::DeviceInfo dev;
   if (device_info(&dev) != VG_OK) return -1;

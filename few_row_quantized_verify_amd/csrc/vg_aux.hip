@@ -59,8 +59,8 @@ template <int FMT>
 __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
   __shared__ float xs[MAXM * VALU_WK];
   __shared__ float red[VALU_ROWS][VALU_PARTS][MAXM];
-  constexpr int G = FMT == SIGN1 ? 128 : 64;
-  constexpr int WK = FMT == SIGN1 ? 32 : 16;   // K per word
+  constexpr int G = fmt_one_bit(FMT) ? 128 : 64;
+  constexpr int WK = fmt_one_bit(FMT) ? 32 : 16;   // K per word
   const int part = threadIdx.x % VALU_PARTS, lr = threadIdx.x / VALU_PARTS;
   const int n = blockIdx.x * VALU_ROWS + lr;
   const bool live = n < A.N;
@@ -88,10 +88,12 @@ __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
         const size_t gi = grow + k / G;
         const float sc = h2f(A.scales[gi]);
         const float* xw = xs + WK * wi;
-        if constexpr (FMT == SIGN1) {
+        if constexpr (fmt_one_bit(FMT)) {
+          const float b = FMT == AFFINE1 ? h2f(A.biases[gi]) : 0.0f;
 #pragma unroll 4
           for (int bit = 0; bit < 32; ++bit) {
-            const float wv = ((word >> bit) & 1u) ? sc : -sc;
+            const bool on = ((word >> bit) & 1u) != 0u;
+            const float wv = FMT == AFFINE1 ? (on ? sc + b : b) : (on ? sc : -sc);   // exact in fp32
 #pragma unroll
             for (int m = 0; m < MAXM; ++m)
               if (m < A.M) acc[m] = __builtin_fmaf(xw[m * len + bit], wv, acc[m]);
@@ -129,6 +131,7 @@ hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev) {
     case SIGN1: hipLaunchKernelGGL(vg_valu<SIGN1>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
     case AFFINE2: hipLaunchKernelGGL(vg_valu<AFFINE2>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
     case HAD2: hipLaunchKernelGGL(vg_valu<HAD2>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
+    case AFFINE1: hipLaunchKernelGGL(vg_valu<AFFINE1>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

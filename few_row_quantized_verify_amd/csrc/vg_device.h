@@ -25,7 +25,10 @@
 
 namespace vg {
 
-enum Format : int { SIGN1 = 0, AFFINE2 = 1, HAD2 = 2 };
+// AFFINE1: MLX's 1-bit affine codes (w = bit * s + b, one scale and bias per 128 weights),
+// decoded like the sign bits and finished like the 2-bit affine format.
+enum Format : int { SIGN1 = 0, AFFINE2 = 1, HAD2 = 2, AFFINE1 = 3 };
+__host__ __device__ constexpr bool fmt_one_bit(int fmt) { return fmt == SIGN1 || fmt == AFFINE1; }
 
 // ---- 1-bit sign format: 16 registers per 32-bit word ---------------------------------
 // Register b0 (0..15) holds the bits b0 and b0+16 of the word, taken at position p of a

@@ -53,21 +53,26 @@ template <> struct Fmt<SIGN1> {
   static constexpr int G = 128, WORD_K = 32, PAIRS = 16, NQ = 4, GL = 2;
   static constexpr int WB = 64;           // LDS bytes of one word's operand window
   static constexpr int GS = 4 * WB + 16;  // LDS bytes per group (+16 pad vs bank conflicts)
-  static constexpr bool AFFINE = false;
+  static constexpr bool AFFINE = false;   // a bias per group
+  static constexpr bool ONE_BIT = true;   // sign-bit decode (else 2-bit codes)
+};
+template <> struct Fmt<AFFINE1> : Fmt<SIGN1> {
+  static constexpr bool AFFINE = true;
 };
 template <> struct Fmt<AFFINE2> {
   static constexpr int G = 64, WORD_K = 16, PAIRS = 8, NQ = 2, GL = 4;
   static constexpr int WB = 32;
   static constexpr int GS = 4 * WB + 16;
   static constexpr bool AFFINE = true;
+  static constexpr bool ONE_BIT = false;
 };
 template <> struct Fmt<HAD2> : Fmt<AFFINE2> {};
 
-__host__ __device__ constexpr int fmt_group(int fmt) { return fmt == SIGN1 ? 128 : 64; }
-__host__ __device__ constexpr int fmt_gs(int fmt) { return fmt == SIGN1 ? 4 * 64 + 16 : 4 * 32 + 16; }
-__host__ __device__ constexpr int fmt_word_k(int fmt) { return fmt == SIGN1 ? 32 : 16; }
-__host__ __device__ constexpr int fmt_gps(int fmt) { return fmt == SIGN1 ? 8 : 16; }   // groups per K-step
-__host__ __device__ constexpr int fmt_gl(int fmt) { return fmt == SIGN1 ? 2 : 4; }     // Fmt<>::GL
+__host__ __device__ constexpr int fmt_group(int fmt) { return fmt_one_bit(fmt) ? 128 : 64; }
+__host__ __device__ constexpr int fmt_gs(int fmt) { return fmt_one_bit(fmt) ? 4 * 64 + 16 : 4 * 32 + 16; }
+__host__ __device__ constexpr int fmt_word_k(int fmt) { return fmt_one_bit(fmt) ? 32 : 16; }
+__host__ __device__ constexpr int fmt_gps(int fmt) { return fmt_one_bit(fmt) ? 8 : 16; }   // groups per K-step
+__host__ __device__ constexpr int fmt_gl(int fmt) { return fmt_one_bit(fmt) ? 2 : 4; }     // Fmt<>::GL
 constexpr int KSTEP = 1024;   // K per unit, both formats
 
 struct MfmaArgs {
@@ -102,7 +107,7 @@ struct LdsLayout {
     e_off = a_off + (M + 1) * pitch;
     xp_off = e_off + groups * MAXM * 4;
     xp_pitch = (groups / fmt_gl(fmt)) * 16 + 16;
-    ytile_off = xp_off + (fmt == SIGN1 ? 0 : (M + 1) * xp_pitch);
+    ytile_off = xp_off + (fmt == SIGN1 ? 0 : (M + 1) * xp_pitch);   // every other format has biases
     slot_off = ytile_off + tiles_max * MAXM * 16 * 4;
     row_off = slot_off + NW * 2 * MAXM * 16 * 4;
     flag_off = row_off + 2 * MAXM * 4;
@@ -291,22 +296,46 @@ __device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L,
 
     // pair dwords, sums, LDS writes
     char* arow = smem + L.a_off + m * pitch;
-    if constexpr (FMT == SIGN1) {
-      // chunk = one word window (32 K) = word (c % 4) of group (c / 4)
+    if constexpr (F::ONE_BIT) {
+      // chunk = one word window (32 K) = word (c % 4) of group (c / 4).  The offset sum is
+      // sum a (BETA + 1) for signs (the decoded half is BETA + 2 bit = BETA + 1 + sign) and
+      // sum a BETA for 1-bit affine codes (BETA + 2 bit = BETA + 2 code).
       uint32_t pd[16];
-      float e = 0.0f;
+      float e = 0.0f, xsum = 0.0f;
 #pragma unroll
       for (int b0 = 0; b0 < 16; ++b0) {
         pd[b0] = hv[b0] | (hv[b0 + 16] << 16);
-        const _Float16 cf = (_Float16)(sign1_beta(b0) + 1.0f);
-        e = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pd[b0]), f16x2{cf, cf}, e, false);
+        const _Float16 cf = (_Float16)(sign1_beta(b0) + (FMT == SIGN1 ? 1.0f : 0.0f));
+        const f16x2 ph = __builtin_bit_cast(f16x2, pd[b0]);
+        e = __builtin_amdgcn_fdot2(ph, f16x2{cf, cf}, e, false);
+        if constexpr (F::AFFINE) xsum = __builtin_amdgcn_fdot2(ph, f16x2{(_Float16)1.0f, (_Float16)1.0f}, xsum, false);
       }
       u32x4* dst = reinterpret_cast<u32x4*>(arow + (c >> 2) * F::GS + (c & 3) * F::WB);
 #pragma unroll
       for (int q = 0; q < 4; ++q) dst[q] = u32x4{pd[4 * q], pd[4 * q + 1], pd[4 * q + 2], pd[4 * q + 3]};
       e += __shfl_xor(e, 1);
       e += __shfl_xor(e, 2);
-      if ((c & 3) == 0) reinterpret_cast<float*>(smem + L.e_off)[(c >> 2) * MAXM + m] = -e;
+      if constexpr (F::AFFINE) {
+        xsum += __shfl_xor(xsum, 1);
+        xsum += __shfl_xor(xsum, 2);
+      }
+      if ((c & 3) == 0) {
+        const int grp = c >> 2;
+        reinterpret_cast<float*>(smem + L.e_off)[grp * MAXM + m] = -e;
+        if constexpr (F::AFFINE) {
+          // group sum / 128 as fp16 hi and lo parts; a quad holds GL = 2 groups, its unused
+          // halves are cleared by the quad's first group
+          const float xm = xsum * (1.0f / F::G);
+          const _Float16 hi = (_Float16)xm;
+          const _Float16 lo = (_Float16)(xm - (float)hi);
+          _Float16* xp = reinterpret_cast<_Float16*>(smem + L.xp_off + m * L.xp_pitch + (grp / F::GL) * 16);
+          xp[grp % F::GL] = hi;
+          xp[4 + grp % F::GL] = lo;
+          if (grp % F::GL == 0) {
+            xp[2] = xp[3] = xp[6] = xp[7] = (_Float16)0.0f;
+          }
+        }
+      }
     } else {
       // chunk = two word windows (16 K each) = words 2(c%2), 2(c%2)+1 of group c/2
       float r = 0.0f, xsum = 0.0f;
@@ -332,7 +361,7 @@ __device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L,
         reinterpret_cast<float*>(smem + L.e_off)[grp * MAXM + m] = -r;
         // the group sum enters the bias product as an exact-enough fp16 pair: X/64 is
         // bounded by the largest activation, so neither part can overflow
-        const float xm = xsum * 0.015625f;
+        const float xm = xsum * (1.0f / F::G);
         const _Float16 hi = (_Float16)xm;
         const _Float16 lo = (_Float16)(xm - (float)hi);
         _Float16* xp = reinterpret_cast<_Float16*>(smem + L.xp_off + m * L.xp_pitch + (grp / F::GL) * 16);
@@ -361,7 +390,7 @@ __device__ __forceinline__ float half_of(uint32_t pair, int hi) {
 // operand register; as literals the compiler would split it into an AND and an OR).
 template <int FMT>
 __device__ __forceinline__ void unpack_word_rt(uint32_t w, uint32_t* out, const uint32_t* mk, const uint32_t* mg) {
-  if constexpr (FMT == SIGN1) {
+  if constexpr (Fmt<FMT>::ONE_BIT) {
     const uint32_t src[3] = {w, w << 5, w >> 6};
 #pragma unroll
     for (int b0 = 0; b0 < 16; ++b0) {
@@ -405,6 +434,8 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
   constexpr int NPAIR = MODE == VAR_MFMA_Q ? GL / 2 : GL;
   constexpr int WPP = MODE == VAR_MFMA_Q ? 4 : 2;   // words per group and pair member
   constexpr int NSTEP = NPAIR * WPP;
+  // 1-bit affine codes decode to BETA + 2 code, so their accumulators hold twice the sum
+  constexpr float SCALE_MUL = FMT == AFFINE1 ? 0.5f : 1.0f;
 
   uint32_t wa[NPAIR][WPP], wb[NPAIR][WPP];
   float sa[NPAIR], sb[NPAIR];
@@ -417,8 +448,8 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
         wa[pi][w] = U.w[2 * pi][w];
         wb[pi][w] = U.w[2 * pi + 1][w];
       }
-      sa[pi] = half_of(U.s[pi], 0);
-      sb[pi] = half_of(U.s[pi], 1);
+      sa[pi] = half_of(U.s[pi], 0) * SCALE_MUL;
+      sb[pi] = half_of(U.s[pi], 1) * SCALE_MUL;
       ga[pi] = 2 * pi;
       gb[pi] = 2 * pi + 1;
     }
@@ -441,8 +472,8 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
       wa[h][1] = s13[0];
       wb[h][0] = s02[1];
       wb[h][1] = s13[1];
-      sa[h] = half_of(sc[0][h >> 1], h & 1);
-      sb[h] = half_of(sc[1][h >> 1], h & 1);
+      sa[h] = half_of(sc[0][h >> 1], h & 1) * SCALE_MUL;
+      sb[h] = half_of(sc[1][h >> 1], h & 1) * SCALE_MUL;
       ga[h] = h;
       gb[h] = GL + h;
     }
@@ -486,10 +517,13 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
     }
   }
   if constexpr (F::AFFINE) {
-    static_assert(GL == 4, "bias product takes four groups per lane");
+    // K slots: the lane-group's GL group sums as hi parts (halves 0..3), then lo parts
+    // (halves 4..7); with GL = 2 the unused halves are zero on both sides
     const f16x8 xa = *reinterpret_cast<const f16x8*>(smem + xp_lane);
-    const f16x8 bv = __builtin_bit_cast(f16x8, u32x4{U.b[0], U.b[1], U.b[0], U.b[1]});
-    yb = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bv, yb, 0, 0, 0);
+    u32x4 bw;
+    if constexpr (GL == 4) bw = u32x4{U.b[0], U.b[1], U.b[0], U.b[1]};
+    else bw = u32x4{U.b[0], 0u, U.b[0], 0u};
+    yb = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, __builtin_bit_cast(f16x8, bw), yb, 0, 0, 0);
   } else {
     (void)xp_lane;
     (void)yb;
@@ -508,7 +542,7 @@ __device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    v[r] = (Fmt<FMT>::AFFINE ? __builtin_fmaf(64.0f, yb[r], yacc[r]) : yacc[r]) * invf[m0 + r];
+    v[r] = (Fmt<FMT>::AFFINE ? __builtin_fmaf((float)Fmt<FMT>::G, yb[r], yacc[r]) : yacc[r]) * invf[m0 + r];
     if constexpr (MODE == VAR_MFMA_Q) {
       const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[r]), __float_as_uint(v[r]), false, false);
       v[r] = __uint_as_float(p[0]) + __uint_as_float(p[1]);   // rows 0+1 and 2+3
@@ -746,7 +780,9 @@ __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
 // Host side of the MFMA variants.
 // Packed-weight bytes of a call (codes, scales and biases).
 static double packed_bytes(int fmt, int K, int N) {
-  return fmt == SIGN1 ? (double)N * K / 8 + 2.0 * N * K / 128 : (double)N * K / 4 + 4.0 * N * K / 64;
+  if (fmt == SIGN1) return (double)N * K / 8 + 2.0 * N * K / 128;
+  if (fmt == AFFINE1) return (double)N * K / 8 + 4.0 * N * K / 128;
+  return (double)N * K / 4 + 4.0 * N * K / 64;
 }
 
 // Largest staging window (in K-steps) whose LDS carve-up fits, balanced so the windows of
@@ -808,7 +844,7 @@ bool plan_mfma(int fmt, int variant, int M, int K, int N, const DeviceInfo& dev,
   // loads then reach the compute sooner), two for long streams; the 1-bit format's units
   // are half as large and always keep two.
   const int units_per_wave = ((rows_max + 15) / 16) * s_wg / NW;
-  p->pref = fmt == SIGN1 ? 2 : (units_per_wave < 8 ? 1 : 2);
+  p->pref = fmt_one_bit(fmt) ? 2 : (units_per_wave < 8 ? 1 : 2);
   return p->win_steps > 0;
 }
 
@@ -851,7 +887,7 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.part = part;
   A.counters = counters;
   for (int k = 0; k < 6; ++k) {
-    if (FMT == SIGN1) {
+    if (fmt_one_bit(FMT)) {
       const int q = 5 + k;   // positions 5..10
       A.mask[k] = (1u << q) | (1u << (q + 16));
       A.magic[k] = half_magic_sign1(q) | (half_magic_sign1(q) << 16);
@@ -861,7 +897,7 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
       A.magic[k] = half_magic_affine2(q) | (half_magic_affine2(q) << 16);
     }
   }
-  if (FMT == SIGN1 || p.pref == 2) return launch_kern<FMT, MODE, XT, 2>(A, p, c.stream, dev);
+  if (fmt_one_bit(FMT) || p.pref == 2) return launch_kern<FMT, MODE, XT, 2>(A, p, c.stream, dev);
   return launch_kern<FMT, MODE, XT, 1>(A, p, c.stream, dev);
 }
 
@@ -880,6 +916,7 @@ hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float*
     case SIGN1: VG_DISPATCH_MODE(SIGN1)
     case AFFINE2: VG_DISPATCH_MODE(AFFINE2)
     case HAD2: VG_DISPATCH_MODE(HAD2)
+    case AFFINE1: VG_DISPATCH_MODE(AFFINE1)
     default: return hipErrorInvalidValue;
   }
 #undef VG_DISPATCH_MODE

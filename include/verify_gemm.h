@@ -58,7 +58,7 @@ typedef enum {
 
 typedef enum { VG_F32 = 0, VG_F16 = 1, VG_BF16 = 2 } vg_dtype;
 
-typedef enum { VG_FMT_SIGN1 = 0, VG_FMT_AFFINE2 = 1, VG_FMT_HAD2 = 2 } vg_format;
+typedef enum { VG_FMT_SIGN1 = 0, VG_FMT_AFFINE2 = 1, VG_FMT_HAD2 = 2, VG_FMT_AFFINE1 = 3 } vg_format;
 
 /* Maximum drafted rows per call (verify blocks of up to 8 rows are padded to 8:
    "dflash-mlx-bonsai2" README, "What this fork adds"). */
@@ -73,6 +73,19 @@ typedef enum { VG_FMT_SIGN1 = 0, VG_FMT_AFFINE2 = 1, VG_FMT_HAD2 = 2 } vg_format
 vg_status verify_gemm_sign1(const void* x, int x_dtype, int M, int K,
                             const uint32_t* wbits, const uint16_t* scales, int N,
                             float* y, void* stream);
+
+/*
+ * y[M, N] = x[M, K] * W^T with W MLX's 1-bit affine weights: w = c*s + b with a 1-bit code
+ * c (0/1) and one fp16 scale s and fp16 bias b per 128 weights (1.25 bits per weight).
+ * wbits[N, K/32] packed like the sign bits; scales and biases [N, K/128] fp16.  The sign
+ * format is the special case s = 2*s_sign, b = -s_sign.
+ * Requires 1 <= M <= 8, N >= 1, K >= 128, K % 128 == 0.
+ * Source: "Bonsai-27B-mlx-1bit" model card, MLX paragraph (MLX stores the binary weights
+ * as 1-bit affine codes with scale 2s and bias -s per group of 128).
+ */
+vg_status verify_gemm_affine1(const void* x, int x_dtype, int M, int K,
+                              const uint32_t* wbits, const uint16_t* scales,
+                              const uint16_t* biases, int N, float* y, void* stream);
 
 /*
  * y[M, N] = x[M, K] * W^T with W the 2-bit affine g64 weights, w = q*s + b.

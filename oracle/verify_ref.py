@@ -21,6 +21,10 @@ Formats:
             fp16 bias b per 64 consecutive weights (MLX's grouped affine format,
             which stores a scale and a bias per group: same model card, MLX paragraph;
             "Ishizuki" README, MLX affine codes).
+  affine1 -- MLX's 1-bit affine codes: one bit c per weight, w = c*s + b with one fp16
+            scale and one fp16 bias per 128 consecutive weights; the sign format is the
+            case s = 2*s_sign, b = -s_sign ("Bonsai-27B-mlx-1bit" model card, MLX
+            paragraph).  Bits are packed exactly like the sign bits.
   had2   -- the 2-bit affine format applied to activations first multiplied by a
             block-diagonal normalized Sylvester Hadamard matrix with block 128
             ("dflash-mlx-bonsai2" README, "What this fork adds": Hadamard-rotated 2-bit
@@ -118,6 +122,13 @@ def dequant_affine2(codes: np.ndarray, scales: np.ndarray, biases: np.ndarray) -
     return codes.astype(np.float64) * decode_f16(scales)[:, g] + decode_f16(biases)[:, g]
 
 
+def dequant_affine1(bits: np.ndarray, scales: np.ndarray, biases: np.ndarray) -> np.ndarray:
+    """w[n, k] = bit[n, k] * s[n, k // 128] + b[n, k // 128]   (fp64, exact for fp16 s, b)."""
+    K = bits.shape[1]
+    g = np.arange(K) // 128
+    return bits.astype(np.float64) * decode_f16(scales)[:, g] + decode_f16(biases)[:, g]
+
+
 # ----------------------------------------------------------------------------- Hadamard
 def sylvester_hadamard(n: int) -> np.ndarray:
     """H_1 = [1],  H_2m = [[H_m, H_m], [H_m, -H_m]]  (integer matrix, n a power of two)."""
@@ -165,6 +176,16 @@ def verify_affine2(x: np.ndarray, x_dtype: str, words: np.ndarray, scales: np.nd
                                                         scales[a:b], biases[a:b]))
 
 
+def verify_affine1(x: np.ndarray, x_dtype: str, words: np.ndarray, scales: np.ndarray,
+                   biases: np.ndarray) -> np.ndarray:
+    """y[M, N] = x[M, K] @ W^T with W the dequantized 1-bit affine weights (fp64)."""
+    x64 = activations(x, x_dtype)
+    K = x64.shape[1]
+    return _matmul_chunked(x64, words.shape[0],
+                           lambda a, b: dequant_affine1(unpack_sign1(words[a:b], K),
+                                                        scales[a:b], biases[a:b]))
+
+
 def verify_had2(x: np.ndarray, x_dtype: str, words: np.ndarray, scales: np.ndarray,
                 biases: np.ndarray, block: int = 128) -> np.ndarray:
     """Unfused reference: rotate the activations, then the 2-bit affine product."""
@@ -188,6 +209,8 @@ def verify_columns(fmt: str, x: np.ndarray, x_dtype: str, words: np.ndarray,
         return verify_affine2(x, x_dtype, w, s, b)
     if fmt == "had2":
         return verify_had2(x, x_dtype, w, s, b)
+    if fmt == "affine1":
+        return verify_affine1(x, x_dtype, w, s, b)
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -198,6 +221,8 @@ def verify(fmt: str, x, x_dtype, words, scales, biases=None) -> np.ndarray:
         return verify_affine2(x, x_dtype, words, scales, biases)
     if fmt == "had2":
         return verify_had2(x, x_dtype, words, scales, biases)
+    if fmt == "affine1":
+        return verify_affine1(x, x_dtype, words, scales, biases)
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -216,6 +241,9 @@ def magnitude_columns(fmt: str, x: np.ndarray, x_dtype: str, words: np.ndarray,
     w, s = words[cols], scales[cols]
     if fmt == "sign1":
         dense = lambda a, b: dequant_sign1(unpack_sign1(w[a:b], K), s[a:b])
+    elif fmt == "affine1":
+        b1 = biases[cols]
+        dense = lambda a, b: dequant_affine1(unpack_sign1(w[a:b], K), s[a:b], b1[a:b])
     elif fmt in ("affine2", "had2"):
         bb = biases[cols]
         dense = lambda a, b: dequant_affine2(unpack_affine2(w[a:b], K), s[a:b], bb[a:b])

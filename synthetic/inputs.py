@@ -11,8 +11,9 @@ Recipe (fixed draw order, one ``numpy.random.default_rng(seed)`` per case):
      2-bit codes (2-bit format), so no packing step is needed here;
   2. one scale per group, drawn in float64 from U(lo, hi) and rounded to fp16
      (round to nearest even);
-  3. 2-bit format only: one bias per group, drawn from U(-2s, -s) using the
-     already rounded scale s, then rounded to fp16;
+  3. formats with biases: one bias per group, drawn using the already rounded scale s
+     and then rounded to fp16: U(-2s, -s) for the 2-bit formats (centred codes), U(-s, 0)
+     for the 1-bit affine format (weights b and s + b on both sides of zero);
   4. activations: an [8, K] block of N(0, 1) float64 samples, rounded to the
      activation dtype (fp16: nearest even; bf16: first to fp32, then nearest even
      on the fp32 bit pattern; fp32: nearest).  A call with M rows uses the first M
@@ -25,9 +26,10 @@ from dataclasses import dataclass
 import numpy as np
 
 # K-elements per group and per uint32 word for each packed format.
-GROUP = {"sign1": 128, "affine2": 64, "had2": 64}
-WORD_K = {"sign1": 32, "affine2": 16, "had2": 16}
-SCALE_RANGE = {"sign1": (0.01, 0.1), "affine2": (0.005, 0.05), "had2": (0.005, 0.05)}
+GROUP = {"sign1": 128, "affine2": 64, "had2": 64, "affine1": 128}
+WORD_K = {"sign1": 32, "affine2": 16, "had2": 16, "affine1": 32}
+SCALE_RANGE = {"sign1": (0.01, 0.1), "affine2": (0.005, 0.05), "had2": (0.005, 0.05),
+               "affine1": (0.02, 0.2)}
 X_DTYPES = ("f32", "f16", "bf16")
 M_MAX = 8
 
@@ -39,6 +41,7 @@ WORKLOADS = {
     "mlp_down_sign1_k17408_n5120": ("sign1", 17408, 5120, "bf16", tuple(range(1, 9))),
     "attn_had2_k5120_n6144": ("had2", 5120, 6144, "f16", tuple(range(1, 9))),
     "head_affine2_k5120_n151936": ("affine2", 5120, 151936, "f16", (1, 5, 6, 7, 8)),
+    "mlp_up_affine1_k5120_n17408": ("affine1", 5120, 17408, "bf16", tuple(range(1, 9))),
 }
 
 
@@ -97,6 +100,9 @@ def draw_case(fmt: str, K: int, N: int, x_dtype: str, seed: int = 0,
     if fmt in ("affine2", "had2"):
         s = s16.view(np.float16).astype(np.float64)
         biases = f16_bits(rng.uniform(-2.0 * s, -s))
+    elif fmt == "affine1":
+        s = s16.view(np.float16).astype(np.float64)
+        biases = f16_bits(rng.uniform(-s, 0.0))
     x_all = draw_x(rng, K, x_dtype)
     return Case(fmt, K, N, x_dtype, words, s16, biases, x_all)
 

@@ -311,6 +311,38 @@ def pin_mlx_1bit_encoding(ref):
     assert np.array_equal(w_sign, w_aff)
 
 
+def pin_affine1(ref):
+    """1-bit affine: the MLX encoding of the sign format reproduces the sign GEMM; all-ones
+    and all-zeros bits give the per-group closed forms; exact rational brute force with
+    an independent bit decoder."""
+    rng = np.random.default_rng(16)
+    M, K, N = 3, 384, 5
+    words, s, _, x = _rand_case(rng, "sign1", M, K, N, "bf16")
+    s64 = s.view(np.float16).astype(np.float64)
+    s2 = (2 * s64).astype(np.float16).view(np.uint16)          # exact: doubling an fp16
+    bm = (-s64).astype(np.float16).view(np.uint16)
+    assert _close(ref.verify_affine1(x, "bf16", words, s2, bm), ref.verify_sign1(x, "bf16", words, s),
+                  rtol=1e-13, atol=1e-13)
+    b = (-rng.uniform(0.0, 1.0, size=s64.shape) * s64).astype(np.float16).view(np.uint16)
+    x64 = ref.decode_bf16(x)
+    gsum = x64.reshape(M, K // 128, 128).sum(axis=2)                  # [M, groups]
+    sv, bv = ref.decode_f16(s), ref.decode_f16(b)
+    ones = np.full_like(words, 0xFFFFFFFF)
+    assert _close(ref.verify_affine1(x, "bf16", ones, s, b), gsum @ (sv + bv).T)
+    assert _close(ref.verify_affine1(x, "bf16", np.zeros_like(words), s, b), gsum @ bv.T)
+    y = ref.verify_affine1(x, "bf16", words, s, b)
+    xf = [[_bf16_fraction(int(v)) for v in row] for row in x]
+    for n in range(2):
+        w = []
+        for k in range(K):
+            bit = (int(words[n, k // 32]) >> (k % 32)) & 1
+            w.append(bit * _f16_fraction(int(s[n, k // 128])) + _f16_fraction(int(b[n, k // 128])))
+        for m in range(M):
+            exact = sum(xf[m][k] * w[k] for k in range(K))
+            bound = K * 2.0 ** -52 * float(sum(abs(xf[m][k] * w[k]) for k in range(K)))
+            assert abs(y[m, n] - float(exact)) <= bound + 1e-300, (m, n)
+
+
 def pin_argmax(ref):
     rng = np.random.default_rng(10)
     M, K, N = 3, 128, 64
@@ -417,4 +449,4 @@ ALL_PINS = [pin_decode, pin_unpack_hand_words, pin_pack_roundtrip, pin_golden,
             pin_sign1_closed_form, pin_affine2_known_codes, pin_rowsum_identity,
             pin_bruteforce_fraction, pin_hadamard_identities, pin_had2_weight_side,
             pin_mlx_1bit_encoding, pin_argmax, pin_columns_and_chunks, pin_normwise,
-            pin_magnitude, pin_greedy_accept]
+            pin_magnitude, pin_greedy_accept, pin_affine1]

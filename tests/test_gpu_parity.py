@@ -98,7 +98,7 @@ def test_debug_unpack_is_bit_exact(vg, fmt, K):
 # ----------------------------------------------------------------------------- small shapes
 # K a multiple of the 1024-wide K-step of the MFMA variants (fp16/bf16 take them), N not
 # a multiple of the 16-row tile.
-SMALL = [("sign1", 2048, 100), ("affine2", 3072, 100), ("had2", 2048, 100)]
+SMALL = [("sign1", 2048, 100), ("affine2", 3072, 100), ("had2", 2048, 100), ("affine1", 2048, 100)]
 VALU = 2
 
 
@@ -113,7 +113,7 @@ def test_small_all_rows(vg, fmt, K, N, x_dtype):
         check(case, M, run(vg, case, M), label=f"small[{vg.variant_name(var)}]")
 
 
-@pytest.mark.parametrize("fmt,K", [("sign1", 1024), ("affine2", 1024), ("had2", 1024)])
+@pytest.mark.parametrize("fmt,K", [("sign1", 1024), ("affine2", 1024), ("had2", 1024), ("affine1", 1024)])
 @pytest.mark.parametrize("N", [1, 17, 33, 257])
 def test_ragged_n(vg, fmt, K, N):
     case = draw_case(fmt, K, N, "f16", seed=2)
@@ -235,6 +235,7 @@ def sample_cols(N, k=384, seed=0):
     ("mlp_down_sign1_k17408_n5120", (1, 5, 8)),
     ("attn_had2_k5120_n6144", (1, 3, 8)),
     ("tiny_sign1_k512_n256", tuple(range(1, 9))),
+    ("mlp_up_affine1_k5120_n17408", (1, 4, 8)),
 ])
 def test_full_workload_sampled(vg, name, Ms):
     case = workload_case(name, seed=0)
@@ -292,7 +293,7 @@ def ksplit(vg):
 
 
 @pytest.mark.parametrize("fmt,K,N,x_dtype", [("sign1", 5120, 300, "bf16"), ("affine2", 4096, 100, "f16"),
-                                             ("had2", 3072, 77, "f16")])
+                                             ("had2", 3072, 77, "f16"), ("affine1", 4096, 90, "bf16")])
 @pytest.mark.parametrize("ks", [2, 3, 5])
 def test_forced_k_split(vg, ksplit, fmt, K, N, x_dtype, ks):
     """K split across workgroups (capped at K/1024 slices), ragged row groups, every row
@@ -382,3 +383,21 @@ def test_accept_greedy_on_head_logits(vg):
     idx, acc = vg.verify_accept_greedy(y, torch.from_numpy(draft).cuda())
     assert list(idx.cpu().numpy()) == gold["argmax"][:M]
     assert int(acc.cpu().numpy()[0]) == 3
+
+
+# ----------------------------------------------------------------------------- 1-bit affine
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16", "f32"])
+def test_affine1_mlx_encoding_matches_sign1(vg, x_dtype):
+    """The sign weights written as MLX 1-bit affine codes (scale 2s, bias -s) give the sign
+    GEMM's result on the GPU too, through a different decode and epilogue."""
+    case = draw_case("sign1", 3072, 200, x_dtype, seed=50)
+    s64 = case.scales.view(np.float16).astype(np.float64)
+    s2 = (2 * s64).astype(np.float16).view(np.uint16)
+    bm = (-s64).astype(np.float16).view(np.uint16)
+    from synthetic.torch_io import f16_tensor
+    for M in (1, 6):
+        x, w, s, _ = case_tensors(case, M)
+        y_sign = vg.verify_gemm_sign1(x, w, s).cpu().numpy().astype(np.float64)
+        y_aff = vg.verify_gemm_affine1(x, w, f16_tensor(s2), f16_tensor(bm)).cpu().numpy().astype(np.float64)
+        check(case, M, y_aff, label=f"affine1-as-sign1[{x_dtype}]")
+        assert oracle.normwise_rel_err(y_aff, y_sign) < 1e-5

@@ -162,12 +162,29 @@ def _mut_accept_counts_all_matches(m):
     m.greedy_accept = greedy_accept
 
 
+def _mut_affine1_group_64(m):
+    def dequant_affine1(bits, scales, biases):
+        K = bits.shape[1]
+        g = np.minimum(np.arange(K) // 64, scales.shape[1] - 1)
+        return bits.astype(np.float64) * m.decode_f16(scales)[:, g] + m.decode_f16(biases)[:, g]
+    m.dequant_affine1 = dequant_affine1
+
+
+def _mut_affine1_bias_on_set_bits_only(m):
+    def dequant_affine1(bits, scales, biases):
+        K = bits.shape[1]
+        g = np.arange(K) // 128
+        return bits.astype(np.float64) * (m.decode_f16(scales)[:, g] + m.decode_f16(biases)[:, g])
+    m.dequant_affine1 = dequant_affine1
+
+
 MUTATIONS = [_mut_sign1_msb_first, _mut_affine2_code_order, _mut_sign_polarity, _mut_drop_bias,
              _mut_sign1_group_size, _mut_affine2_group_index, _mut_hadamard_unnormalized,
              _mut_hadamard_wrong_recursion, _mut_hadamard_skipped, _mut_bf16_shift,
              _mut_f16_as_bf16, _mut_rows_reversed, _mut_chunk_offset, _mut_argmax_last_tie,
              _mut_normwise_elementwise, _mut_magnitude_signed_x,
-             _mut_magnitude_unrotated, _mut_accept_counts_all_matches]
+             _mut_magnitude_unrotated, _mut_accept_counts_all_matches, _mut_affine1_group_64,
+             _mut_affine1_bias_on_set_bits_only]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__[5:])
