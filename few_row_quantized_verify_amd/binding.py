@@ -36,6 +36,8 @@ _I = ctypes.c_int
 _SIGS = {
     "verify_gemm_sign1": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P]),
     "verify_gemm_affine1": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "verify_gemm_had2_signed": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "hadamard_rotate_signed": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "verify_gemm_affine2": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
     "verify_gemm_had2": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P]),
     "hadamard_rotate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
@@ -134,13 +136,20 @@ def verify_gemm_affine1(x, wbits, scales, biases, y=None, stream=None):
     return y
 
 
-def verify_gemm_had2(x, wq, scales, biases, had_block=128, y=None, stream=None):
-    """y = (x @ blockdiag(H_128/sqrt(128))) @ W^T with W 2-bit affine g64."""
+def verify_gemm_had2(x, wq, scales, biases, had_block=128, y=None, stream=None, signs=None):
+    """y = ((x * D) @ blockdiag(H_B/sqrt(B))) @ W^T with W 2-bit affine g64, B = had_block;
+    D = diag(+-1) from the sign bits `signs` (int32 [K/32], bit set: negate), or the
+    identity when signs is None."""
     M, K = x.shape
     N = wq.shape[0]
     y = _out(y, M, N, x.device)
-    _check(lib().verify_gemm_had2(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
-                                  _ptr(biases), N, had_block, _ptr(y), _stream(stream)))
+    if signs is None:
+        _check(lib().verify_gemm_had2(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
+                                      _ptr(biases), N, had_block, _ptr(y), _stream(stream)))
+    else:
+        _check(lib().verify_gemm_had2_signed(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
+                                             _ptr(biases), N, had_block, _ptr(signs), _ptr(y),
+                                             _stream(stream)))
     return y
 
 
@@ -156,12 +165,16 @@ def verify_gemm(fmt: str, x, w, scales, biases=None, y=None, stream=None):
     raise ValueError(fmt)
 
 
-def hadamard_rotate(x, block=128, out=None, stream=None):
+def hadamard_rotate(x, block=128, out=None, stream=None, signs=None):
     torch = _torch()
     M, K = x.shape
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=x.device)
-    _check(lib().hadamard_rotate(_ptr(x), _xdtype(x), M, K, block, _ptr(out), _stream(stream)))
+    if signs is None:
+        _check(lib().hadamard_rotate(_ptr(x), _xdtype(x), M, K, block, _ptr(out), _stream(stream)))
+    else:
+        _check(lib().hadamard_rotate_signed(_ptr(x), _xdtype(x), M, K, block, _ptr(signs), _ptr(out),
+                                            _stream(stream)))
     return out
 
 

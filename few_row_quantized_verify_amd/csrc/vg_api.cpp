@@ -153,7 +153,8 @@ vg_status workspace(int dev, hipStream_t stream, size_t part_bytes, float** part
 }
 
 vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint32_t* w,
-                   const uint16_t* scales, const uint16_t* biases, int N, float* y, void* stream) {
+                   const uint16_t* scales, const uint16_t* biases, int N, float* y, void* stream,
+                   int had_block = 128, const uint32_t* signs = nullptr) {
   std::call_once(g_env_once, read_env);
   vg::DeviceInfo dev;
   if (vg_status s = device_info(&dev)) return s;
@@ -164,7 +165,8 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
                   vg_variant_name(g_forced), fmt, x_dtype, M, K);
     var = g_forced;
   }
-  vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, static_cast<hipStream_t>(stream)};
+  vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, static_cast<hipStream_t>(stream),
+                 had_block, signs};
   hipError_t e;
   if (var == vg::VAR_VALU) {
     e = vg::launch_valu(c, dev);
@@ -248,30 +250,45 @@ vg_status verify_gemm_affine2(const void* x, int x_dtype, int M, int K, const ui
   return run_gemm(vg::AFFINE2, x, x_dtype, M, K, wq, scales, biases, N, y, stream);
 }
 
-vg_status verify_gemm_had2(const void* x, int x_dtype, int M, int K, const uint32_t* wq,
-                           const uint16_t* scales, const uint16_t* biases, int N, int had_block,
-                           float* y, void* stream) {
-  if (had_block != 128)
-    return fail(VG_ERR_UNSUPPORTED, "Hadamard block %d is not supported (only 128)", had_block);
+vg_status verify_gemm_had2_signed(const void* x, int x_dtype, int M, int K, const uint32_t* wq,
+                                  const uint16_t* scales, const uint16_t* biases, int N, int had_block,
+                                  const uint32_t* signs, float* y, void* stream) {
+  if (had_block != 64 && had_block != 128 && had_block != 256)
+    return fail(VG_ERR_UNSUPPORTED, "Hadamard block %d is not supported (64, 128 or 256)", had_block);
   if (vg_status s = check_common(x, x_dtype, M, K, N)) return s;
-  if (K % 128 != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of the Hadamard block 128", K);
+  if (K % 128 != 0 || K % had_block != 0)
+    return fail(VG_ERR_SHAPE, "K=%d is not a multiple of 128 and of the Hadamard block %d", K, had_block);
   if (vg_status s = check_ptr(wq, "wq")) return s;
   if (vg_status s = check_ptr(scales, "scales")) return s;
   if (vg_status s = check_ptr(biases, "biases")) return s;
   if (vg_status s = check_ptr(y, "y")) return s;
-  return run_gemm(vg::HAD2, x, x_dtype, M, K, wq, scales, biases, N, y, stream);
+  if (signs && (reinterpret_cast<uintptr_t>(signs) & 3u)) return fail(VG_ERR_ALIGN, "signs is not 4-byte aligned");
+  return run_gemm(vg::HAD2, x, x_dtype, M, K, wq, scales, biases, N, y, stream, had_block, signs);
+}
+
+vg_status verify_gemm_had2(const void* x, int x_dtype, int M, int K, const uint32_t* wq,
+                           const uint16_t* scales, const uint16_t* biases, int N, int had_block,
+                           float* y, void* stream) {
+  return verify_gemm_had2_signed(x, x_dtype, M, K, wq, scales, biases, N, had_block, nullptr, y, stream);
+}
+
+vg_status hadamard_rotate_signed(const void* x, int x_dtype, int M, int K, int block, const uint32_t* signs,
+                                 float* x_out, void* stream) {
+  if (block != 64 && block != 128 && block != 256)
+    return fail(VG_ERR_UNSUPPORTED, "Hadamard block %d is not supported (64, 128 or 256)", block);
+  if (vg_status s = check_common(x, x_dtype, M, K, 1)) return s;
+  if (K % block != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of the Hadamard block %d", K, block);
+  if (vg_status s = check_ptr(x_out, "x_out")) return s;
+  if (signs && (reinterpret_cast<uintptr_t>(signs) & 3u)) return fail(VG_ERR_ALIGN, "signs is not 4-byte aligned");
+  const hipError_t e = vg::launch_hadamard(x, x_dtype, M, K, block, signs, x_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return VG_OK;
 }
 
 vg_status hadamard_rotate(const void* x, int x_dtype, int M, int K, int block, float* x_out,
                           void* stream) {
-  if (block != 128) return fail(VG_ERR_UNSUPPORTED, "Hadamard block %d is not supported (only 128)", block);
-  if (vg_status s = check_common(x, x_dtype, M, K, 1)) return s;
-  if (K % 128 != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of the Hadamard block 128", K);
-  if (vg_status s = check_ptr(x_out, "x_out")) return s;
-  const hipError_t e = vg::launch_hadamard(x, x_dtype, M, K, x_out, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  g_err[0] = '\0';
-  return VG_OK;
+  return hadamard_rotate_signed(x, x_dtype, M, K, block, nullptr, x_out, stream);
 }
 
 vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* stream) {

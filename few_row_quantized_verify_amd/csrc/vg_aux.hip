@@ -27,18 +27,24 @@ struct ValuArgs {
   const uint16_t* biases;
   float* y;
   int M, K, N;
+  int had_block;            // rotated format: 64, 128 or 256
+  const uint32_t* signs;    // rotated format: optional sign bits [K/32]
 };
 
-// In-place unnormalized Walsh-Hadamard transform of 128-blocks of an LDS buffer
-// [MAXM][len] (len a multiple of 128), butterfly stage by stage.
-__device__ void lds_fwht(float* xs, int M, int len) {
-  const int pairs = M * len / 2;
-  for (int h = 1; h < 128; h <<= 1) {
+__device__ __forceinline__ float had_norm(int block) {
+  return block == 64 ? 0.125f : (block == 256 ? 0.0625f : 0.08838834764831845f);   // 1/sqrt(block)
+}
+
+// In-place unnormalized Walsh-Hadamard transform of the `block`-blocks of an LDS buffer
+// [MAXM][len] (len a multiple of block), butterfly stage by stage.
+__device__ void lds_fwht(float* xs, int M, int len, int block) {
+  const int pairs = M * len / 2, half = block / 2;
+  for (int h = 1; h < block; h <<= 1) {
     for (int p = threadIdx.x; p < pairs; p += blockDim.x) {
       const int m = p / (len / 2), q = p - m * (len / 2);
-      const int blk = q / 64, r = q - blk * 64;              // 64 butterflies per block
+      const int blk = q / half, r = q - blk * half;          // block/2 butterflies per block
       const int lo = (r / h) * (2 * h) + (r % h);
-      float* b = xs + m * len + blk * 128;
+      float* b = xs + m * len + blk * block;
       const float a0 = b[lo], a1 = b[lo + h];
       b[lo] = a0 + a1;
       b[lo + h] = a0 - a1;
@@ -77,8 +83,16 @@ __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
     }
     __syncthreads();
     if constexpr (FMT == HAD2) {
-      lds_fwht(xs, A.M, len);
-      for (int e = threadIdx.x; e < A.M * len; e += VALU_THREADS) xs[e] *= 0.08838834764831845f;
+      if (A.signs) {
+        for (int e = threadIdx.x; e < A.M * len; e += VALU_THREADS) {
+          const int k = k0 + e % len;
+          if ((A.signs[k >> 5] >> (k & 31)) & 1u) xs[e] = -xs[e];
+        }
+        __syncthreads();
+      }
+      lds_fwht(xs, A.M, len, A.had_block);
+      const float nrm = had_norm(A.had_block);
+      for (int e = threadIdx.x; e < A.M * len; e += VALU_THREADS) xs[e] *= nrm;
       __syncthreads();
     }
     if (live) {
@@ -125,7 +139,7 @@ __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
 
 hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev) {
   (void)dev;
-  ValuArgs A{c.x, c.xt, c.w, c.scales, c.biases, c.y, c.M, c.K, c.N};
+  ValuArgs A{c.x, c.xt, c.w, c.scales, c.biases, c.y, c.M, c.K, c.N, c.had_block, c.signs};
   const dim3 grid((c.N + VALU_ROWS - 1) / VALU_ROWS);
   switch (c.fmt) {
     case SIGN1: hipLaunchKernelGGL(vg_valu<SIGN1>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
@@ -146,35 +160,52 @@ __device__ __forceinline__ float dpp_quad_aux(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-__global__ __launch_bounds__(256) void vg_hadamard_kernel(const void* x, int xt, int M, int K, float* out) {
+__global__ __launch_bounds__(256) void vg_hadamard_kernel(const void* x, int xt, int M, int K, int block,
+                                                         const uint32_t* signs, float* out) {
+  const int lanes = block / 32, stages = lanes == 2 ? 1 : (lanes == 4 ? 2 : 3);
   const int gt = blockIdx.x * 256 + threadIdx.x;
-  const int nquads = M * (K / 128);
-  const int quad = gt >> 2, ql = gt & 3;
-  if (quad >= nquads) return;          // whole quads leave together (4 | 256)
-  const int m = quad / (K / 128), blk = quad - m * (K / 128);
-  const size_t base = (size_t)m * K + blk * 128 + ql * 32;
+  const int nblocks = M * (K / block);
+  const int bid = gt / lanes, bl = gt % lanes;
+  if (bid >= nblocks) return;          // whole blocks leave together (lanes | 256)
+  const int m = bid / (K / block), blk = bid - m * (K / block);
+  const int k0 = blk * block + bl * 32;
+  const size_t base = (size_t)m * K + k0;
   float v[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) v[e] = x_at(x, xt, base + e);
+  if (signs) {
+    const uint32_t sw = signs[k0 >> 5];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((sw >> e) & 1u) << 31));
+  }
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1)
 #pragma unroll
     for (int e = 0; e < 32; ++e)
       if ((e & h) == 0) { const float a = v[e], b = v[e + h]; v[e] = a + b; v[e + h] = a - b; }
-  const float c1 = (ql & 1) ? -1.0f : 1.0f, c2 = (ql & 2) ? -1.0f : 1.0f;
+  // cross-lane stages, upper results negated (the final sign is the parity of bl)
+  const float c1 = (bl & 1) ? -1.0f : 1.0f, c2 = (bl & 2) ? -1.0f : 1.0f, c3 = (bl & 4) ? -1.0f : 1.0f;
 #pragma unroll
   for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c1, dpp_quad_aux<0xB1>(v[e]), v[e]);
+  if (stages >= 2) {
 #pragma unroll
-  for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c2, dpp_quad_aux<0x4E>(v[e]), v[e]);
-  const float sg = (((ql & 1) ^ ((ql >> 1) & 1)) != 0) ? -1.0f : 1.0f;
-  const float sc = sg * 0.08838834764831845f;
+    for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c2, dpp_quad_aux<0x4E>(v[e]), v[e]);
+  }
+  if (stages >= 3) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      v[e] = __builtin_fmaf(c3, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v[e]), 0x101F)), v[e]);
+  }
+  const float sg = (__builtin_popcount(bl) & 1) ? -1.0f : 1.0f;
+  const float sc = sg * had_norm(block);
 #pragma unroll
   for (int e = 0; e < 32; ++e) out[base + e] = v[e] * sc;
 }
 
-hipError_t launch_hadamard(const void* x, int xt, int M, int K, float* out, hipStream_t s) {
-  const int threads = 4 * M * (K / 128);
-  hipLaunchKernelGGL(vg_hadamard_kernel, dim3((threads + 255) / 256), dim3(256), 0, s, x, xt, M, K, out);
+hipError_t launch_hadamard(const void* x, int xt, int M, int K, int block, const uint32_t* signs, float* out,
+                           hipStream_t s) {
+  const int threads = (block / 32) * M * (K / block);
+  hipLaunchKernelGGL(vg_hadamard_kernel, dim3((threads + 255) / 256), dim3(256), 0, s, x, xt, M, K, block, signs, out);
   return hipGetLastError();
 }
 

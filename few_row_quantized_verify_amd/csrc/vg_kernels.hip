@@ -88,6 +88,9 @@ struct MfmaArgs {
   uint32_t mask[6];   // code-extraction masks per bit position (see vg_device.h)
   uint32_t magic[6];  // fp16 magic pairs per bit position
   int rg, ks;         // row groups x K slices; workgroup b takes row group b / ks, slice b % ks
+  int had_stages;     // rotated format: log2(block / 32) cross-lane butterfly stages
+  float had_scale;    // 1 / sqrt(block)
+  const uint32_t* signs;  // rotated format: optional sign bits [K/32] (bit set: negate x[:, k])
   float* part;        // ks > 1: partial outputs [ks][M][N]
   uint32_t* counters; // ks > 1: arrivals per row group (zero between calls)
 };
@@ -129,13 +132,19 @@ __device__ __forceinline__ float dpp_quad(float v) {
                                                                CTRL, 0xF, 0xF, false));
 }
 
-// Fast Walsh-Hadamard transform of a 128-block held by 4 consecutive lanes (a quad), 32
-// fp32 values per lane, lane l holding block elements 32l .. 32l+31.  Five butterfly
-// stages run inside each lane's registers, two across the quad.  The cross-lane stages
-// use one fused multiply-add each and leave the upper results negated; the known final
-// sign of each lane is returned so the caller can fold it into its scale.  Unnormalized:
-// out[k] = sign * sum_j (-1)^popcount(k & j) in[j].
-__device__ __forceinline__ float fwht128_quad(float v[32], int quad_lane) {
+// Lane l ^ 4 within groups of 32 lanes (ds_swizzle, bit-mask mode: and 0x1f, xor 4).
+__device__ __forceinline__ float swizzle_xor4(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x101F));
+}
+
+// Fast Walsh-Hadamard transform of a block of 32 * 2^stages elements (64, 128 or 256) held
+// by 2^stages consecutive lanes, 32 fp32 values per lane, lane b of the block holding
+// block elements 32b .. 32b+31.  Five butterfly stages run inside each lane's registers,
+// `stages` across lanes (partners b ^ 1, b ^ 2 by DPP, b ^ 4 by swizzle).  Each cross-lane
+// stage is one fused multiply-add that leaves the upper results negated; the final sign of
+// each lane, (-1)^popcount(b), is returned so the caller can fold it into its scale.
+// Unnormalized: out[k] = sign * sum_j (-1)^popcount(k & j) in[j].
+__device__ __forceinline__ float fwht_lanes(float v[32], int block_lane, int stages) {
 #pragma unroll
   for (int h = 1; h < 32; h <<= 1) {
 #pragma unroll
@@ -147,13 +156,22 @@ __device__ __forceinline__ float fwht128_quad(float v[32], int quad_lane) {
       }
     }
   }
-  const float c1 = (quad_lane & 1) ? -1.0f : 1.0f;
-  const float c2 = (quad_lane & 2) ? -1.0f : 1.0f;
+  if (stages >= 1) {
+    const float c1 = (block_lane & 1) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c1, dpp_quad<0xB1>(v[e]), v[e]);
+    for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c1, dpp_quad<0xB1>(v[e]), v[e]);
+  }
+  if (stages >= 2) {
+    const float c2 = (block_lane & 2) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c2, dpp_quad<0x4E>(v[e]), v[e]);
-  return (((quad_lane & 1) ^ ((quad_lane >> 1) & 1)) != 0) ? -1.0f : 1.0f;
+    for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c2, dpp_quad<0x4E>(v[e]), v[e]);
+  }
+  if (stages >= 3) {
+    const float c3 = (block_lane & 4) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) v[e] = __builtin_fmaf(c3, swizzle_xor4(v[e]), v[e]);
+  }
+  return (__builtin_popcount(block_lane & ((1 << stages) - 1)) & 1) ? -1.0f : 1.0f;
 }
 
 // Workgroup barrier for hand-offs through LDS.  The fences order LDS accesses only, so a
@@ -233,7 +251,7 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
 }
 
 template <int FMT, int XT>
-__device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L, int WK, const XStage& xs) {
+__device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L, int k0, int WK, const XStage& xs) {
   using F = Fmt<FMT>;
   constexpr bool HAD = FMT == HAD2;
   constexpr bool NORM = HAD || XT == XBF16;
@@ -267,7 +285,7 @@ __device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L,
       float f = 1.0f;
       if (mx > 0.0f && mx == mx) {
         frexpf(mx, &ex);                      // mx < 2^ex
-        int e = 14 - ex - (HAD ? 4 : 0);      // rotated values are below sqrt(128) * max < 16 * max
+        int e = 14 - ex - (HAD ? 4 : 0);      // rotated values are below sqrt(256) * max = 16 * max
         e = e < -120 ? -120 : (e > 120 ? 120 : e);
         f = ldexpf(1.0f, e);
       }
@@ -280,7 +298,7 @@ __device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L,
 #pragma unroll
   for (int j = 0; j < MAXT; ++j) {
     const int t = tid + j * NTHREADS;
-    if (t >= ntask) continue;   // whole quads skip together (ntask and NTHREADS are multiples of 4)
+    if (t >= ntask) continue;   // whole blocks of 8 lanes skip together (32 | ntask, 64 | NTHREADS)
     const int m = t / nchunks, c = t - m * nchunks;
     uint32_t hv[32];  // fp16 bits, natural K order within the chunk
     chunk_halves(xs, j, hv);
@@ -289,7 +307,14 @@ __device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L,
 #pragma unroll
       for (int e = 0; e < 32; ++e) v[e] = half_bits_to_f32<XT>(hv[e]);
       float scale = rowf[m];
-      if constexpr (HAD) scale *= fwht128_quad(v, c & 3) * 0.08838834764831845f;  // 1/sqrt(128)
+      if constexpr (HAD) {
+        if (A.signs) {
+          const uint32_t sw = A.signs[(k0 >> 5) + c];   // the chunk's 32 sign bits
+#pragma unroll
+          for (int e = 0; e < 32; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((sw >> e) & 1u) << 31));
+        }
+        scale *= fwht_lanes(v, c & ((1 << A.had_stages) - 1), A.had_stages) * A.had_scale;
+      }
 #pragma unroll
       for (int e = 0; e < 32; ++e) hv[e] = f32_to_f16_bits(v[e] * scale);
     }
@@ -664,7 +689,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     XStage xs;
     stage_load<XT>(A, ws0 * KSTEP, ns * KSTEP, xs);
     lds_barrier();  // previous window's readers are done with the LDS
-    stage_compute<FMT, XT>(A, smem, L, ns * KSTEP, xs);
+    stage_compute<FMT, XT>(A, smem, L, ws0 * KSTEP, ns * KSTEP, xs);
     Unit<FMT> ring[PREF];
     if (nu > 0) {
 #pragma unroll
@@ -886,6 +911,9 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.ks = p.ks;
   A.part = part;
   A.counters = counters;
+  A.had_stages = c.had_block == 64 ? 1 : (c.had_block == 256 ? 3 : 2);
+  A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
+  A.signs = c.signs;
   for (int k = 0; k < 6; ++k) {
     if (fmt_one_bit(FMT)) {
       const int q = 5 + k;   // positions 5..10

@@ -24,6 +24,8 @@ struct GemmCall {
   const uint16_t* biases;  // null for the 1-bit format
   float* y;
   hipStream_t stream;
+  int had_block;            // rotated format: 64, 128 or 256
+  const uint32_t* signs;    // rotated format: optional sign bits [K/32]
 };
 
 struct DeviceInfo {
@@ -55,7 +57,8 @@ size_t mfma_workspace_bytes(int M, int N, const MfmaPlan& p);
 hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float* part,
                        uint32_t* counters, const DeviceInfo& dev);
 hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev);
-hipError_t launch_hadamard(const void* x, int xt, int M, int K, float* out, hipStream_t s);
+hipError_t launch_hadamard(const void* x, int xt, int M, int K, int block, const uint32_t* signs, float* out,
+                           hipStream_t s);
 // Argmax of each row over the whole chip; with draft/accepted non-null also the greedy
 // acceptance count.  pval/pidx: argmax_chunks(N) * M partials; counters: 9 zeroed words
 // (left zeroed).

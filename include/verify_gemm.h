@@ -100,13 +100,14 @@ vg_status verify_gemm_affine2(const void* x, int x_dtype, int M, int K,
 
 /*
  * y[M, N] = (x[M, K] * H_bd) * W^T with H_bd block-diagonal, each block the normalized
- * Sylvester Hadamard H_128 / sqrt(128), and W 2-bit affine g64 as above.  The rotation
- * runs inside the GEMM's prologue on each workgroup's activations; no rotated copy of x
- * is written.  had_block must be 128 (anything else -> VG_ERR_UNSUPPORTED).
- * Requires 1 <= M <= 8, N >= 1, K >= 128, K % 128 == 0.
+ * Sylvester Hadamard H_B / sqrt(B), B = had_block, and W 2-bit affine g64 as above.  The
+ * rotation runs inside the GEMM's prologue on each workgroup's activations; no rotated
+ * copy of x is written.  had_block must be 64, 128 or 256 (anything else ->
+ * VG_ERR_UNSUPPORTED: a transform that cannot be applied is refused, never run as the plain
+ * format).  Requires 1 <= M <= 8, N >= 1, K % 128 == 0 and K % had_block == 0.
  * Source: "dflash-mlx-bonsai2" README, "What this fork adds" (Hadamard-rotated 2-bit pack,
- * verify GEMM with the Hadamard fused into its prep); "Ishizuki" README (a pack declaring
- * a transform that cannot be applied is refused, not loaded as plain affine).
+ * verify GEMM with the Hadamard fused into its prep; the block of the test packs is 128);
+ * "Ishizuki" README (a pack declaring a transform that cannot be applied is refused).
  */
 vg_status verify_gemm_had2(const void* x, int x_dtype, int M, int K,
                            const uint32_t* wq, const uint16_t* scales,
@@ -114,12 +115,29 @@ vg_status verify_gemm_had2(const void* x, int x_dtype, int M, int K,
                            void* stream);
 
 /*
- * x_out[M, K] (fp32) = x[M, K] * H_bd, the same block-128 normalized Sylvester rotation
- * as verify_gemm_had2, as a standalone call.  block must be 128.  Requires 1 <= M <= 8,
- * K % 128 == 0.
+ * As verify_gemm_had2 with a random sign flip before the rotation:
+ * y = ((x * D) * H_bd) * W^T, D = diag(d_k), d_k = -1 where bit k%32 of signs[k/32] is set,
+ * +1 elsewhere.  signs is a device array of K/32 uint32 (4-byte aligned), or NULL for
+ * verify_gemm_had2.  Source: "dflash-mlx-bonsai2" README, "What this fork adds" (the fused
+ * prep names a sign step next to the Hadamard; the pages do not define it, and this
+ * diagonal-before-rotation form is the usual randomized Hadamard).
+ */
+vg_status verify_gemm_had2_signed(const void* x, int x_dtype, int M, int K,
+                                  const uint32_t* wq, const uint16_t* scales,
+                                  const uint16_t* biases, int N, int had_block,
+                                  const uint32_t* signs, float* y, void* stream);
+
+/*
+ * x_out[M, K] (fp32) = x[M, K] * H_bd, the same block-B normalized Sylvester rotation as
+ * verify_gemm_had2 (B = block: 64, 128 or 256), as a standalone call.  Requires
+ * 1 <= M <= 8, K % block == 0.
  */
 vg_status hadamard_rotate(const void* x, int x_dtype, int M, int K, int block,
                           float* x_out, void* stream);
+
+/* hadamard_rotate with the sign flip of verify_gemm_had2_signed first (signs may be NULL). */
+vg_status hadamard_rotate_signed(const void* x, int x_dtype, int M, int K, int block,
+                                 const uint32_t* signs, float* x_out, void* stream);
 
 /*
  * idx[m] = argmax_n y[m, n] for m < M (lowest n on ties; NaN never wins; a row of only

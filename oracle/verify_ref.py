@@ -140,11 +140,19 @@ def sylvester_hadamard(n: int) -> np.ndarray:
     return H
 
 
-def hadamard_rotate(x64: np.ndarray, block: int = 128) -> np.ndarray:
-    """x' = x @ blockdiag(H_block / sqrt(block)), applied to each aligned block of K."""
+def hadamard_rotate(x64: np.ndarray, block: int = 128, signs: np.ndarray | None = None) -> np.ndarray:
+    """x' = (x D) @ blockdiag(H_block / sqrt(block)), applied to each aligned block of K, with
+    D = diag(d_k), d_k = -1 where bit k % 32 of signs[k // 32] is set (D = I if signs is None).
+    The sign step is the plainest reading of the "sign" in the fused prep of the
+    "dflash-mlx-bonsai2" README ("What this fork adds"): a diagonal of +-1 before the
+    rotation."""
     M, K = x64.shape
     if K % block:
         raise ValueError("K must be a multiple of the Hadamard block")
+    if signs is not None:
+        k = np.arange(K)
+        neg = (np.asarray(signs, dtype=np.uint32)[k // 32] >> (k % 32).astype(np.uint32)) & 1
+        x64 = x64 * np.where(neg.astype(bool), -1.0, 1.0)
     Hn = sylvester_hadamard(block).astype(np.float64) / np.sqrt(float(block))
     return (x64.reshape(M, K // block, block) @ Hn).reshape(M, K)
 
@@ -187,9 +195,10 @@ def verify_affine1(x: np.ndarray, x_dtype: str, words: np.ndarray, scales: np.nd
 
 
 def verify_had2(x: np.ndarray, x_dtype: str, words: np.ndarray, scales: np.ndarray,
-                biases: np.ndarray, block: int = 128) -> np.ndarray:
-    """Unfused reference: rotate the activations, then the 2-bit affine product."""
-    x64 = hadamard_rotate(activations(x, x_dtype), block)
+                biases: np.ndarray, block: int = 128, signs: np.ndarray | None = None) -> np.ndarray:
+    """Unfused reference: rotate the activations (optionally sign-flipped first), then the
+    2-bit affine product."""
+    x64 = hadamard_rotate(activations(x, x_dtype), block, signs)
     K = x64.shape[1]
     return _matmul_chunked(x64, words.shape[0],
                            lambda a, b: dequant_affine2(unpack_affine2(words[a:b], K),
@@ -197,8 +206,10 @@ def verify_had2(x: np.ndarray, x_dtype: str, words: np.ndarray, scales: np.ndarr
 
 
 def verify_columns(fmt: str, x: np.ndarray, x_dtype: str, words: np.ndarray,
-                   scales: np.ndarray, biases: np.ndarray | None, cols: np.ndarray) -> np.ndarray:
-    """The oracle restricted to a sample of output columns: y[:, cols]."""
+                   scales: np.ndarray, biases: np.ndarray | None, cols: np.ndarray,
+                   block: int = 128, signs: np.ndarray | None = None) -> np.ndarray:
+    """The oracle restricted to a sample of output columns: y[:, cols] (block and signs:
+    the rotation of the had2 format)."""
     cols = np.asarray(cols)
     w = words[cols]
     s = scales[cols]
@@ -208,7 +219,7 @@ def verify_columns(fmt: str, x: np.ndarray, x_dtype: str, words: np.ndarray,
     if fmt == "affine2":
         return verify_affine2(x, x_dtype, w, s, b)
     if fmt == "had2":
-        return verify_had2(x, x_dtype, w, s, b)
+        return verify_had2(x, x_dtype, w, s, b, block, signs)
     if fmt == "affine1":
         return verify_affine1(x, x_dtype, w, s, b)
     raise ValueError(f"unknown format {fmt!r}")
@@ -227,7 +238,8 @@ def verify(fmt: str, x, x_dtype, words, scales, biases=None) -> np.ndarray:
 
 
 def magnitude_columns(fmt: str, x: np.ndarray, x_dtype: str, words: np.ndarray,
-                      scales: np.ndarray, biases: np.ndarray | None, cols=None) -> np.ndarray:
+                      scales: np.ndarray, biases: np.ndarray | None, cols=None,
+                      block: int = 128, signs: np.ndarray | None = None) -> np.ndarray:
     """mag[m, n] = sum_k |a[m, k]| * |w[n, k]|, the sum of the magnitudes of the terms of
     y[m, n] (a = the activations, rotated for had2; w = the dequantized weights), for the
     columns `cols` (all if None).  Bounds how far any summation order and any rounding of
@@ -236,7 +248,7 @@ def magnitude_columns(fmt: str, x: np.ndarray, x_dtype: str, words: np.ndarray,
     cols = np.arange(words.shape[0]) if cols is None else np.asarray(cols)
     x64 = activations(x, x_dtype)
     if fmt == "had2":
-        x64 = hadamard_rotate(x64, 128)
+        x64 = hadamard_rotate(x64, block, signs)
     K = x64.shape[1]
     w, s = words[cols], scales[cols]
     if fmt == "sign1":

@@ -111,3 +111,9 @@ def workload_case(name: str, seed: int = 0, N: int | None = None) -> Case:
     """Draw a named workload; ``N`` may shrink the output width for quick checks."""
     fmt, K, N0, x_dtype, _ = WORKLOADS[name]
     return draw_case(fmt, K, N0 if N is None else N, x_dtype, seed)
+
+
+def draw_signs(K: int, seed: int = 0) -> np.ndarray:
+    """Sign bits of a randomized rotation: uint32 [K/32], each bit uniform (bit set: -1)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 1 << 32, size=(K // 32,), dtype=np.uint64).astype(np.uint32)

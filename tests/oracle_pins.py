@@ -270,6 +270,32 @@ def pin_hadamard_identities(ref):
                                                                [1, 1, -1, -1], [1, -1, -1, 1]]))
 
 
+def pin_hadamard_blocks_and_signs(ref):
+    """Blocks 64 and 256: H H^T = n I, the independent FWHT, the ones image; the signed
+    rotation equals the explicit product x D H_bd / sqrt(B), is orthogonal, and undoes to x
+    by rotating again and flipping the same signs."""
+    rng = np.random.default_rng(17)
+    for B in (64, 256):
+        H = ref.sylvester_hadamard(B)
+        assert np.array_equal(H @ H.T, B * np.eye(B, dtype=H.dtype))
+        x = rng.standard_normal((2, 2 * B))
+        xr = ref.hadamard_rotate(x, B)
+        assert np.allclose(_fwht(x.reshape(2, 2, B)).reshape(2, 2 * B) / math.sqrt(B), xr, atol=1e-13)
+        ones = ref.hadamard_rotate(np.ones((1, B)), B)[0]
+        assert abs(ones[0] - math.sqrt(B)) < 1e-12 and np.abs(ones[1:]).max() < 1e-12
+    K, B = 512, 128
+    signs = rng.integers(0, 1 << 32, size=(K // 32,), dtype=np.uint64).astype(np.uint32)
+    x = rng.standard_normal((3, K))
+    assert np.array_equal(ref.hadamard_rotate(x, B, np.zeros(K // 32, np.uint32)), ref.hadamard_rotate(x, B))
+    d = np.array([-1.0 if (int(signs[k // 32]) >> (k % 32)) & 1 else 1.0 for k in range(K)])
+    Hbd = np.kron(np.eye(K // B), ref.sylvester_hadamard(B).astype(np.float64)) / math.sqrt(B)
+    xs = ref.hadamard_rotate(x, B, signs)
+    assert np.allclose(xs, (x * d) @ Hbd, atol=1e-13)
+    assert np.allclose(np.linalg.norm(xs, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    assert np.allclose(ref.hadamard_rotate(xs, B) * d, x, atol=1e-13)
+    assert not np.allclose(xs, ref.hadamard_rotate(x, B))
+
+
 def pin_had2_weight_side(ref):
     """(x Hn) W^T == x (W Hn)^T: rotating the dense weights instead of the activations."""
     rng = np.random.default_rng(8)
@@ -449,4 +475,4 @@ ALL_PINS = [pin_decode, pin_unpack_hand_words, pin_pack_roundtrip, pin_golden,
             pin_sign1_closed_form, pin_affine2_known_codes, pin_rowsum_identity,
             pin_bruteforce_fraction, pin_hadamard_identities, pin_had2_weight_side,
             pin_mlx_1bit_encoding, pin_argmax, pin_columns_and_chunks, pin_normwise,
-            pin_magnitude, pin_greedy_accept, pin_affine1]
+            pin_magnitude, pin_greedy_accept, pin_affine1, pin_hadamard_blocks_and_signs]

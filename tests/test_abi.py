@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
     for fn in ("verify_gemm_sign1", "verify_gemm_affine2", "verify_gemm_had2", "hadamard_rotate",
                "verify_argmax_rows", "vg_last_error", "vg_plan_variant", "vg_variant_name",
                "vg_force_variant", "vg_variant_count", "vg_debug_unpack_sign1", "vg_debug_unpack_affine2",
-               "vg_plan_ksplit", "vg_force_ksplit", "verify_accept_greedy"):
+               "vg_plan_ksplit", "vg_force_ksplit", "verify_accept_greedy", "verify_gemm_affine1",
+               "verify_gemm_had2_signed", "hadamard_rotate_signed"):
         assert fn in names, fn
 
 
@@ -86,7 +87,7 @@ def test_misaligned_pointers(which):
     assert st == B.VG_ERR_ALIGN and "aligned" in _err()
 
 
-@pytest.mark.parametrize("block", [0, 64, 256, 127])
+@pytest.mark.parametrize("block", [0, 32, 512, 127])
 def test_unsupported_hadamard_block_is_refused(block):
     L = B.lib()
     st = L.verify_gemm_had2(ALIGNED, B.VG_F16, 1, 256, ALIGNED, ALIGNED, ALIGNED, 8, block, ALIGNED, None)
@@ -141,3 +142,12 @@ def test_accept_greedy_validation():
     assert L.verify_accept_greedy(ALIGNED, 2, 100, ALIGNED, ALIGNED, None, None) == B.VG_ERR_ARG
     assert L.verify_accept_greedy(ALIGNED, 9, 100, ALIGNED, ALIGNED, ALIGNED, None) == B.VG_ERR_SHAPE
     assert L.verify_accept_greedy(ALIGNED + 2, 2, 100, ALIGNED, ALIGNED, ALIGNED, None) == B.VG_ERR_ALIGN
+
+
+def test_hadamard_block_must_divide_k_and_signs_aligned():
+    L = B.lib()
+    assert L.verify_gemm_had2(ALIGNED, B.VG_F16, 1, 384, ALIGNED, ALIGNED, ALIGNED, 8, 256, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.hadamard_rotate(ALIGNED, B.VG_F16, 1, 192, 128, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.verify_gemm_had2_signed(ALIGNED, B.VG_F16, 1, 256, ALIGNED, ALIGNED, ALIGNED, 8, 64, ALIGNED + 2,
+                                     ALIGNED, None) == B.VG_ERR_ALIGN
+    assert L.hadamard_rotate_signed(ALIGNED, B.VG_F16, 1, 256, 64, ALIGNED + 1, ALIGNED, None) == B.VG_ERR_ALIGN

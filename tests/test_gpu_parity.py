@@ -39,7 +39,7 @@ def run(vg, case, M, y=None):
     return out.cpu().numpy().astype(np.float64)
 
 
-def check(case, M, y_gpu, cols=None, tol=TOL, label=""):
+def check(case, M, y_gpu, cols=None, tol=TOL, label="", had=None):
     """Two bars, both against the fp64 oracle on the same inputs.
 
     Componentwise, every output: |y - y_ref| <= (2^-11 + K 2^-24) * mag + slack, with
@@ -53,14 +53,15 @@ def check(case, M, y_gpu, cols=None, tol=TOL, label=""):
     args = (case.fmt, case.x(M), case.x_dtype, case.words, case.scales, case.biases)
     if cols is None:
         cols = np.arange(case.N)
-    y_ref = oracle.verify_columns(*args, cols)
-    mag = oracle.magnitude_columns(*args, cols)
+    had = had or {}
+    y_ref = oracle.verify_columns(*args, cols, **had)
+    mag = oracle.magnitude_columns(*args, cols, **had)
     got = y_gpu[:, cols]
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"
     K = case.K
     a = oracle.activations(case.x(M), case.x_dtype)
     if case.fmt == "had2":
-        a = oracle.hadamard_rotate(a, 128)
+        a = oracle.hadamard_rotate(a, had.get("block", 128), had.get("signs"))
     sc = oracle.decode_f16(case.scales[cols])
     if case.fmt == "sign1":
         wmax = float(sc.max())
@@ -401,3 +402,41 @@ def test_affine1_mlx_encoding_matches_sign1(vg, x_dtype):
         y_aff = vg.verify_gemm_affine1(x, w, f16_tensor(s2), f16_tensor(bm)).cpu().numpy().astype(np.float64)
         check(case, M, y_aff, label=f"affine1-as-sign1[{x_dtype}]")
         assert oracle.normwise_rel_err(y_aff, y_sign) < 1e-5
+
+
+# ----------------------------------------------------------------------------- other rotations
+@pytest.mark.parametrize("block", [64, 128, 256])
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16", "f32"])
+def test_hadamard_rotate_blocks_and_signs(vg, block, x_dtype):
+    from synthetic import draw_signs
+    case = draw_case("had2", 1024, 1, x_dtype, seed=60)
+    signs = draw_signs(1024, seed=61)
+    for M in (1, 8):
+        x = x_tensor(case.x(M), x_dtype)
+        a = oracle.activations(case.x(M), x_dtype)
+        for sg in (None, signs):
+            st = None if sg is None else torch.from_numpy(sg.view(np.int32)).cuda()
+            out = vg.hadamard_rotate(x, block, signs=st).cpu().numpy().astype(np.float64)
+            ref = oracle.hadamard_rotate(a, block, sg)
+            assert np.max(np.abs(out - ref)) / np.max(np.abs(ref)) < 1e-6
+
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+@pytest.mark.parametrize("K,N,x_dtype", [(2048, 100, "f16"), (3072, 37, "bf16"), (1536, 50, "f16"),
+                                         (1024, 40, "f32")])
+def test_had2_blocks_and_signs(vg, block, K, N, x_dtype):
+    """Rotations of block 64, 128 and 256, with and without a random sign flip, on the
+    MFMA path (K a multiple of 1024) and the VALU path (fp32, or K = 1536)."""
+    from synthetic import draw_signs
+    if K % block:
+        pytest.skip("K not a multiple of the block")
+    case = draw_case("had2", K, N, x_dtype, seed=62 + block)
+    signs = draw_signs(K, seed=63)
+    st = torch.from_numpy(signs.view(np.int32)).cuda()
+    for M in (1, 4, 8):
+        x, w, s, b = case_tensors(case, M)
+        for sg, stt in ((None, None), (signs, st)):
+            y = vg.verify_gemm_had2(x, w, s, b, had_block=block, signs=stt)
+            torch.cuda.synchronize()
+            check(case, M, y.cpu().numpy().astype(np.float64), had={"block": block, "signs": sg},
+                  label=f"had{block}{'s' if sg is not None else ''}")

@@ -68,8 +68,17 @@ def _mut_affine2_group_index(m):
     m.dequant_affine2 = dequant_affine2
 
 
+def _signed(x64, signs):
+    if signs is None:
+        return x64
+    k = np.arange(x64.shape[1])
+    neg = (np.asarray(signs, dtype=np.uint32)[k // 32] >> (k % 32).astype(np.uint32)) & 1
+    return x64 * np.where(neg.astype(bool), -1.0, 1.0)
+
+
 def _mut_hadamard_unnormalized(m):
-    def hadamard_rotate(x64, block=128):
+    def hadamard_rotate(x64, block=128, signs=None):
+        x64 = _signed(x64, signs)
         M, K = x64.shape
         H = m.sylvester_hadamard(block).astype(np.float64)
         return (x64.reshape(M, K // block, block) @ H).reshape(M, K)
@@ -86,7 +95,7 @@ def _mut_hadamard_wrong_recursion(m):
 
 
 def _mut_hadamard_skipped(m):
-    m.hadamard_rotate = lambda x64, block=128: x64
+    m.hadamard_rotate = lambda x64, block=128, signs=None: _signed(x64, signs)
 
 
 def _mut_bf16_shift(m):
@@ -178,13 +187,26 @@ def _mut_affine1_bias_on_set_bits_only(m):
     m.dequant_affine1 = dequant_affine1
 
 
+def _mut_signs_after_rotation(m):
+    orig = m.hadamard_rotate
+
+    def hadamard_rotate(x64, block=128, signs=None):
+        y = orig(x64, block)
+        if signs is None:
+            return y
+        k = np.arange(x64.shape[1])
+        neg = (np.asarray(signs, dtype=np.uint32)[k // 32] >> (k % 32).astype(np.uint32)) & 1
+        return y * np.where(neg.astype(bool), -1.0, 1.0)
+    m.hadamard_rotate = hadamard_rotate
+
+
 MUTATIONS = [_mut_sign1_msb_first, _mut_affine2_code_order, _mut_sign_polarity, _mut_drop_bias,
              _mut_sign1_group_size, _mut_affine2_group_index, _mut_hadamard_unnormalized,
              _mut_hadamard_wrong_recursion, _mut_hadamard_skipped, _mut_bf16_shift,
              _mut_f16_as_bf16, _mut_rows_reversed, _mut_chunk_offset, _mut_argmax_last_tie,
              _mut_normwise_elementwise, _mut_magnitude_signed_x,
              _mut_magnitude_unrotated, _mut_accept_counts_all_matches, _mut_affine1_group_64,
-             _mut_affine1_bias_on_set_bits_only]
+             _mut_affine1_bias_on_set_bits_only, _mut_signs_after_rotation]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__[5:])
