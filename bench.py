@@ -12,6 +12,12 @@ timing starts.
 For the output-head workload a call is the verify GEMM followed by the argmax of every row
 (the head's argmax step), so its per-M times include both kernels.
 
+For a routed-expert workload (synthetic.inputs.EXPERT_WORKLOADS) a call is one grouped
+expert verify of M rows, each routed to topk of the E experts; the calls cycle through 64
+seeded routings and the weight pool.  value counts the packed bytes of the distinct experts
+each call routes to (each read once), and the line also gives the time of the same work as
+one plain verify call per (row, slot), which reads an expert once per row routed to it.
+
 Prints one JSON line: value = packed-weight bytes (codes + fp16 scales + fp16 biases)
 moved per second over all timed calls (GB/s, 1e9), plus per-M microseconds per call,
 t(M=8)/t(M=1), a roofline object for the dominant kernel and the CPU oracle baseline.
@@ -45,7 +51,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from synthetic import WORKLOADS, workload_case  # noqa: E402
+from synthetic import EXPERT_WORKLOADS, WORKLOADS, draw_experts, draw_route, workload_case  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 POOL_BYTES = 1 << 30
@@ -98,6 +104,134 @@ def cpu_baseline(case) -> dict:
             "sample": f"M=8, first {ncols} of {case.N} output columns of {case.fmt} K={case.K}, "
                       f"{reps} reps, {dt * 1e3:.1f} ms/rep; us/call-equivalent "
                       f"{dt / frac * 1e6:.0f}"}
+
+
+def cpu_baseline_experts(ec, routes) -> dict:
+    """The oracle's routed-expert verify on the host, on a bounded sample of columns."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    M = routes[0].shape[0]
+    ncols = min(ec.N, 128)
+    cols = np.arange(ncols)
+    per_expert = (ec.words[0].nbytes + ec.scales[0].nbytes +
+                  (ec.biases[0].nbytes if ec.biases is not None else 0))
+    t0 = time.perf_counter()
+    reps = 0
+    nbytes = 0.0
+    while True:
+        r = routes[reps % len(routes)]
+        oracle.verify_experts(ec.fmt, ec.x(M), ec.x_dtype, r, ec.words, ec.scales, ec.biases, rows=cols)
+        nbytes += len(np.unique(r)) * per_expert * ncols / ec.N
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 20:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"M={M}, first {ncols} of {ec.N} output columns of every routed slot, "
+                      f"{reps} routings, {dt / reps * 1e3:.1f} ms/routing"}
+
+
+def bench_experts(args, vg, torch, dev) -> dict:
+    from synthetic.torch_io import case_tensors, f16_tensor, words_tensor
+    name = args.workload
+    fmt, K, N, E, topk, x_dtype = EXPERT_WORKLOADS[name]
+    Ms = tuple(int(v) for v in args.m.split(",")) if args.m else (1, 2, 4, 8)
+    ec = draw_experts(fmt, K, N, E, x_dtype, seed=0)
+    per_expert = (ec.words[0].nbytes + ec.scales[0].nbytes +
+                  (ec.biases[0].nbytes if ec.biases is not None else 0))
+    ncopy = max(2, -(-POOL_BYTES // (per_expert * E)))
+    w0, s0 = words_tensor(ec.words, dev), f16_tensor(ec.scales, dev)
+    b0 = f16_tensor(ec.biases, dev) if ec.biases is not None else None
+    pool = [(w0.clone(), s0.clone(), None if b0 is None else b0.clone()) for _ in range(ncopy)]
+    NR = 64
+    routes = {M: [draw_route(M, topk, E, seed=1000 * M + r) for r in range(NR)] for M in Ms}
+    rdev = {M: [torch.from_numpy(r).to(dev) for r in routes[M]] for M in Ms}
+    uniq = {M: [len(np.unique(r)) for r in routes[M]] for M in Ms}
+    x_all = {M: case_tensors(ec, M, dev)[0] for M in Ms}
+    ys = {M: torch.empty((M, topk, N), dtype=torch.float32, device=dev) for M in Ms}
+
+    def call(M, j):
+        w, s, b = pool[j % ncopy]
+        vg.verify_gemm_experts(fmt, x_all[M], rdev[M][j % NR], w, s, b, y=ys[M])
+
+    for M in Ms:
+        for j in range(args.warmup):
+            call(M, j)
+    torch.cuda.synchronize()
+    ev = {M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
+    t_wall = time.perf_counter()
+    nbytes = {M: 0 for M in Ms}
+    j = 0
+    for M in Ms:
+        ev[M][0].record()
+        for i in range(args.steps):
+            call(M, j)
+            nbytes[M] += uniq[M][j % NR] * per_expert
+            j += 1
+        ev[M][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    us = {M: ev[M][0].elapsed_time(ev[M][1]) * 1e3 / args.steps for M in Ms}
+
+    # the same routed products as one plain verify call per (row, slot), on routing 0
+    Mtop = max(Ms)
+    rt0 = routes[Mtop][0]
+    xs = [x_all[Mtop][m:m + 1].contiguous() for m in range(Mtop)]
+    y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+
+    def per_slot(j):
+        w, s, b = pool[j % ncopy]
+        for m in range(Mtop):
+            for sl in range(topk):
+                e = int(rt0[m, sl])
+                vg.verify_gemm(fmt, xs[m], w[e], s[e], None if b is None else b[e], y=y1)
+
+    for j in range(3):
+        per_slot(j)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(5, args.steps // 10)
+    e0.record()
+    for j in range(reps):
+        per_slot(j)
+    e1.record()
+    torch.cuda.synchronize()
+    per_slot_us = e0.elapsed_time(e1) * 1e3 / reps
+
+    total_s = sum(us.values()) * args.steps * 1e-6
+    value = sum(nbytes.values()) / total_s / 1e9
+    per_m = {str(M): {"us_per_call": round(us[M], 3),
+                      "distinct_experts_mean": round(float(np.mean(uniq[M])), 2),
+                      "gbs": round(nbytes[M] / args.steps / (us[M] * 1e-6) / 1e9, 1),
+                      "pct_hbm_peak": round(100 * nbytes[M] / args.steps / (us[M] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+             for M in Ms}
+    algo = nbytes[Mtop] / args.steps + x_bytes(ec, Mtop) + Mtop * topk * N * 4
+    achieved = algo / (us[Mtop] * 1e-6) / 1e9
+    kern = vg.variant_name(0 if Mtop <= 4 else 1)
+    line = {
+        "metric": "µs/call and routed packed-weight GB/s (% of HBM peak) of the grouped expert verify",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sum(us.values()) * 1e-3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if x_dtype != "f32" else "f32", "data": "synthetic",
+        "config": {"workload": name, "format": fmt, "K": K, "N": N, "E": E, "topk": topk,
+                   "x_dtype": x_dtype, "M": list(Ms), "packed_bytes_per_expert": per_expert,
+                   "routings": NR, "weight_pool_copies": ncopy},
+        "per_m": per_m,
+        "per_slot_calls_us": {"M": Mtop, "us": round(per_slot_us, 2),
+                              "grouped_speedup": round(per_slot_us / us[Mtop], 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": kern, "M": Mtop, "algorithmic_bytes_per_launch": round(algo)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_experts(ec, routes[Mtop])
+    return line
 
 
 def load_traffic(kernel: str, digest: str):
@@ -210,6 +344,9 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}))
         return 0
 
+    if args.workload in EXPERT_WORKLOADS:
+        print(json.dumps(bench_experts(args, vg, torch, dev)))
+        return 0
     names = list(WORKLOADS) if args.table else [args.workload]
     lines = []
     headline = None

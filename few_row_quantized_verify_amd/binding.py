@@ -43,6 +43,7 @@ _SIGS = {
     "hadamard_rotate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "verify_argmax_rows": (_I, [_P, _I, _I, _P, _P]),
     "verify_accept_greedy": (_I, [_P, _I, _I, _P, _P, _P, _P]),
+    "verify_gemm_experts": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P]),
     "vg_last_error": (ctypes.c_char_p, []),
     "vg_plan_variant": (_I, [_I, _I, _I, _I, _I]),
     "vg_variant_name": (ctypes.c_char_p, [_I]),
@@ -163,6 +164,23 @@ def verify_gemm(fmt: str, x, w, scales, biases=None, y=None, stream=None):
     if fmt == "affine1":
         return verify_gemm_affine1(x, w, scales, biases, y, stream)
     raise ValueError(fmt)
+
+
+def verify_gemm_experts(fmt: str, x, route, w, scales, biases=None, y=None, stream=None):
+    """Grouped routed-expert verify: y[m, s] = x[m] @ W_e^T with e = route[m, s] (int32
+    [M, topk] on the device, values outside 0..E-1 mark unused slots, whose rows of y are
+    not written).  w, scales, biases: the E experts' packed weights stacked on dim 0.
+    Returns y, fp32 [M, topk, N]."""
+    torch = _torch()
+    M, K = x.shape
+    topk = route.shape[1]
+    E, N = w.shape[0], w.shape[1]
+    if y is None:
+        y = torch.empty((M, topk, N), dtype=torch.float32, device=x.device)
+    b = ctypes.c_void_p(0) if biases is None else _ptr(biases)
+    _check(lib().verify_gemm_experts(FORMATS[fmt], _ptr(x), _xdtype(x), M, K, E, topk, _ptr(route),
+                                     _ptr(w), _ptr(scales), b, N, _ptr(y), _stream(stream)))
+    return y
 
 
 def hadamard_rotate(x, block=128, out=None, stream=None, signs=None):

@@ -187,6 +187,52 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   return VG_OK;
 }
 
+// Grouped expert verify: one MFMA launch whose workgroups each group the routing by expert
+// and take one row group of one job.  Mode Q (jobs of up to 4 rows) when the call has up to 4 rows, else mode H (up to 8);
+// the plan depends only on (format, dtype, M, topk, E, K, N), so a row's result does not
+// depend on which other rows are routed with it.
+vg_status run_experts(int fmt, const void* x, int x_dtype, int M, int K, int E, int topk, const int32_t* route,
+                      const uint32_t* w, const uint16_t* scales, const uint16_t* biases, int N, float* y,
+                      void* stream) {
+  if (vg_status s = check_common(x, x_dtype, M, K, N)) return s;
+  if (E < 1) return fail(VG_ERR_SHAPE, "E=%d < 1", E);
+  if (topk < 1 || topk > VG_MAX_ROWS) return fail(VG_ERR_SHAPE, "topk=%d outside 1..%d", topk, VG_MAX_ROWS);
+  if (x_dtype == VG_F32)
+    return fail(VG_ERR_UNSUPPORTED, "grouped expert verify takes fp16 or bf16 activations");
+  if (K % kstep_of(fmt) != 0) return fail(VG_ERR_UNSUPPORTED, "grouped expert verify needs K a multiple of 1024 (K=%d)", K);
+  if (!route) return fail(VG_ERR_ARG, "route is null");
+  if (reinterpret_cast<uintptr_t>(route) & 3u) return fail(VG_ERR_ALIGN, "route is not 4-byte aligned");
+  if (vg_status s = check_ptr(w, "w")) return s;
+  if (vg_status s = check_ptr(scales, "scales")) return s;
+  if (fmt != vg::SIGN1)
+    if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_ptr(y, "y")) return s;
+  std::call_once(g_env_once, read_env);
+  vg::DeviceInfo dev;
+  if (vg_status s = device_info(&dev)) return s;
+  const int var = M <= 4 ? vg::VAR_MFMA_Q : vg::VAR_MFMA_H;
+  const int cap = M <= 4 ? 4 : 8;
+  const int n = M * topk;
+  const int rows_max = n < cap ? n : cap;   // rows of one job
+  // most jobs a routing can make: each holds at least one entry, and the experts' jobs
+  // number sum ceil(count / cap) <= (experts used) + n / cap
+  const long long jobs_e = (long long)E + n / cap;
+  const int jobs = jobs_e < n ? (int)jobs_e : n;
+  vg::MfmaPlan p;
+  if (!vg::plan_mfma_grouped(fmt, rows_max, K, N, jobs, dev, &p))
+    return fail(VG_ERR_UNSUPPORTED, "M=%d K=%d does not fit the MFMA staging", M, K);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool two_bit = fmt == vg::AFFINE2 || fmt == vg::HAD2;
+  const long long words = (long long)N * (K / (two_bit ? 16 : 32));
+  const long long groups = (long long)N * (K / (two_bit ? 64 : 128));
+  vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, st, 128, nullptr,
+                 route, topk, E, cap, words * 4, groups * 2};
+  const hipError_t e = vg::launch_mfma(c, var, p, nullptr, nullptr, dev);
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return VG_OK;
+}
+
 // Counters of the argmax kernel sit above those of the K-split reductions in the workspace.
 constexpr int kArgmaxCounterBase = 768;
 
@@ -299,6 +345,13 @@ vg_status verify_accept_greedy(const float* y, int M, int N, const int32_t* draf
                                int32_t* accepted, void* stream) {
   if (!draft || !accepted) return fail(VG_ERR_ARG, "draft or accepted is null");
   return run_argmax(y, M, N, idx, draft, accepted, stream);
+}
+
+vg_status verify_gemm_experts(int format, const void* x, int x_dtype, int M, int K, int E, int topk,
+                              const int32_t* route, const uint32_t* w, const uint16_t* scales,
+                              const uint16_t* biases, int N, float* y, void* stream) {
+  if (format < VG_FMT_SIGN1 || format > VG_FMT_AFFINE1) return fail(VG_ERR_ARG, "unknown format %d", format);
+  return run_experts(format, x, x_dtype, M, K, E, topk, route, w, scales, biases, N, y, stream);
 }
 
 const char* vg_last_error(void) { return g_err; }

@@ -93,6 +93,15 @@ struct MfmaArgs {
   const uint32_t* signs;  // rotated format: optional sign bits [K/32] (bit set: negate x[:, k])
   float* part;        // ks > 1: partial outputs [ks][M][N]
   uint32_t* counters; // ks > 1: arrivals per row group (zero between calls)
+  // Grouped expert verify (route non-null, ks = 1): route [M, topk] names the expert of
+  // each (row, slot); values outside 0..E-1 mark unused slots.  Each workgroup groups the
+  // routing by expert into jobs of at most cap rows and takes one row group of one job
+  // (find_job); rg is then the fewest row groups per job the plan sized the LDS for.
+  // Expert e's codes start e * w_estride bytes into w, its scales and biases e * s_estride
+  // bytes into scales and biases; y is [M * topk, N].
+  const int32_t* route;
+  int topk, E, cap;
+  long long w_estride, s_estride;
 };
 
 // LDS carve-up (byte offsets), computed identically on host and device.
@@ -101,12 +110,14 @@ struct MfmaArgs {
 //   e:  fp32 per-(group, row) offset sums, the accumulators' initial values
 //   xp: 2-bit formats: per (row, lane-group quad of GL groups) the group sums / 64 as
 //       fp16 hi parts then lo parts (16 bytes), rows 0..M-1 and a zero row M
+//   job (first 128 bytes): grouped expert verify, the workgroup's job (find_job)
+constexpr int JOB_BYTES = 128;
 struct LdsLayout {
   int a_off, e_off, xp_off, xp_pitch, ytile_off, slot_off, row_off, flag_off, total;
   __host__ __device__ LdsLayout(int fmt, int M, int win_steps, int tiles_max) {
     const int groups = win_steps * fmt_gps(fmt);
     const int pitch = groups * fmt_gs(fmt) + 16;   // must equal MfmaArgs::a_pitch
-    a_off = 0;
+    a_off = JOB_BYTES;
     e_off = a_off + (M + 1) * pitch;
     xp_off = e_off + groups * MAXM * 4;
     xp_pitch = (groups / fmt_gl(fmt)) * 16 + 16;
@@ -221,14 +232,15 @@ struct XStage {
 };
 
 template <int XT>
-__device__ __forceinline__ void stage_load(const MfmaArgs& A, int k0, int WK, XStage& xs) {
-  const int nchunks = WK / 32, ntask = A.M * nchunks;
+// xmap: the x row of each row (grouped expert verify), or null for x rows 0..M-1.
+__device__ __forceinline__ void stage_load(const MfmaArgs& A, int M, const int* xmap, int k0, int WK, XStage& xs) {
+  const int nchunks = WK / 32, ntask = M * nchunks;
 #pragma unroll
   for (int j = 0; j < MAXT; ++j) {
     const int t = threadIdx.x + j * NTHREADS;
     if (t < ntask) {
       const int m = t / nchunks, c = t - m * nchunks;
-      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.x) + (size_t)m * A.K + k0 + 32 * c);
+      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.x) + (size_t)(xmap ? xmap[m] : m) * A.K + k0 + 32 * c);
 #pragma unroll
       for (int q = 0; q < 4; ++q) xs.d[j][q] = p[q];
     }
@@ -251,12 +263,12 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
 }
 
 template <int FMT, int XT>
-__device__ void stage_compute(const MfmaArgs& A, char* smem, const LdsLayout& L, int k0, int WK, const XStage& xs) {
+__device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLayout& L, int k0, int WK,
+                              const XStage& xs) {
   using F = Fmt<FMT>;
   constexpr bool HAD = FMT == HAD2;
   constexpr bool NORM = HAD || XT == XBF16;
   const int tid = threadIdx.x;
-  const int M = A.M;
   const int nchunks = WK / 32;
   const int ntask = M * nchunks;
   const int pitch = A.a_pitch;
@@ -587,17 +599,102 @@ __device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t
   }
 }
 
+// Grouped expert verify: this workgroup's job, derived from the routing by every workgroup
+// alike.  Entry l = m * topk + s (row m, slot s) is routed to expert route[l] when that is
+// in 0..E-1.  Each expert's entries, in order of l, fill jobs of at most cap rows; jobs
+// are numbered by expert, then by position.  With J jobs each takes rg = max(rg_min,
+// grid / J) row groups (at most one per 16-row tile), and workgroup b takes row group
+// b % rg of job b / rg (J * rg <= grid: the grid holds rg_min row groups of the most jobs
+// a routing can make).  The job's x rows (job[0..7]), y rows (job[8..15]), J (job[16]),
+// expert (job[17]) and row count (job[18]) are left in LDS; the 64-entry scratch after
+// them lies in the activation area, which is written only after the last barrier here.
+// Returns false when the workgroup has no job.
+__device__ bool find_job(const MfmaArgs& A, char* smem, int& M, int& expert, int& rgi, int& rg) {
+  int* job = reinterpret_cast<int*>(smem);
+  int* key = job + JOB_BYTES / 4;   // [64] expert of each entry, -1 when unused
+  int* starts = key + 64;           // [64] jobs begun by each expert's first entry
+  const int tid = threadIdx.x;
+  const int n = A.M * A.topk, cap = A.cap;
+  if (tid < 64) {
+    const int v = tid < n ? A.route[tid] : -1;
+    key[tid] = (v >= 0 && v < A.E) ? v : -1;
+  }
+  lds_barrier();
+  int e = -1, pos = 0, cnt = 0;
+  if (tid < 64) {
+    e = key[tid];
+#pragma unroll 8
+    for (int t = 0; t < 64; ++t) {
+      const int kt = key[t];
+      cnt += kt == e ? 1 : 0;
+      pos += (kt == e && t < tid) ? 1 : 0;
+    }
+    starts[tid] = (e >= 0 && pos == 0) ? (cnt + cap - 1) / cap : 0;
+  }
+  lds_barrier();
+  const int tiles = (A.N + 15) / 16;
+  if (tid < 64) {
+    int before = 0, total = 0;
+#pragma unroll 8
+    for (int t = 0; t < 64; ++t) {
+      const int jt = starts[t];
+      total += jt;
+      before += key[t] < e ? jt : 0;
+    }
+    if (tid == 0) job[16] = total;
+    if (e >= 0 && total > 0) {
+      const int r_dyn = min(tiles, max(A.rg, (int)gridDim.x / total));
+      const int mine = before + pos / cap, r = pos - (pos / cap) * cap;
+      if (mine == (int)blockIdx.x / r_dyn) {
+        job[r] = tid / A.topk;
+        job[MAXM + r] = tid;
+        if (r == 0) {
+          job[17] = e;
+          job[18] = min(cap, cnt - pos);
+        }
+      }
+    }
+  }
+  lds_barrier();
+  const int total = job[16];
+  if (total == 0) return false;
+  rg = min(tiles, max(A.rg, (int)gridDim.x / total));
+  const int j = (int)blockIdx.x / rg;
+  if (j >= total) return false;
+  rgi = (int)blockIdx.x - j * rg;
+  expert = job[17];
+  M = job[18];
+  return true;
+}
+
 template <int FMT, int MODE, int XT, int PREF>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, GPS = 4 * GL;
   constexpr bool NORM = FMT == HAD2 || XT == XBF16;
-  const LdsLayout L(FMT, A.M, A.win_steps, A.tiles_max);
+  // The workgroup's job: row group and K slice of the call, or for a grouped expert verify
+  // a row group of one job, whose rows are gathered from x and scattered to y.
+  int M = A.M, rgi, ksi = 0, rg = A.rg;
+  const uint32_t* wq = A.w;
+  const uint16_t* sc = A.scales;
+  const uint16_t* bi = A.biases;
+  const int* xmap = nullptr;   // grouped: x row of each row, then y row of each row
+  if (A.route) {
+    int e;
+    if (!find_job(A, smem, M, e, rgi, rg)) return;
+    xmap = reinterpret_cast<const int*>(smem);
+    wq = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(wq) + e * A.w_estride);
+    sc = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(sc) + e * A.s_estride);
+    if (bi) bi = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(bi) + e * A.s_estride);
+  } else {
+    rgi = blockIdx.x / A.ks;
+    ksi = blockIdx.x - rgi * A.ks;
+  }
+  const LdsLayout L(FMT, M, A.win_steps, A.tiles_max);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
-  const int rgi = blockIdx.x / A.ks, ksi = blockIdx.x - rgi * A.ks;
-  const int r0 = (int)(((long long)A.N * rgi) / A.rg), r1 = (int)(((long long)A.N * (rgi + 1)) / A.rg);
+  const int r0 = (int)(((long long)A.N * rgi) / rg), r1 = (int)(((long long)A.N * (rgi + 1)) / rg);
   const int T = (r1 - r0 + 15) / 16;
   const int S = A.K / KSTEP;
   const int kb0 = (S * ksi) / A.ks, kb1 = (S * (ksi + 1)) / A.ks;   // this slice's K-steps
@@ -615,8 +712,8 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   // this lane's operand row: a drafted row, or the zero row M when the lane's A row
   // carries none (rows of other row-blocks must read zeros in this lane's K slots)
   const int am = MODE == VAR_MFMA_Q ? i - 4 * g : (g < 2 ? i : i - 8);
-  const bool av = am >= 0 && am < A.M && (MODE == VAR_MFMA_H || am < 4);
-  const int arow = av ? am : A.M;
+  const bool av = am >= 0 && am < M && (MODE == VAR_MFMA_H || am < 4);
+  const int arow = av ? am : M;
   const int m0 = MODE == VAR_MFMA_Q ? 0 : 4 * (g & 1);
   const uint32_t a_lane0 = L.a_off + (uint32_t)arow * A.a_pitch +
                            (MODE == VAR_MFMA_Q ? GL * g * F::GS : 2 * (g >> 1) * GL * F::GS + 2 * (g & 1) * F::WB);
@@ -627,18 +724,18 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   for (int e = tid; e < T * MAXM * 16; e += NTHREADS) ytile[e] = 0.0f;
   {
     // the zero rows: never written by the staging, so cleared once per launch
-    uint32_t* za = reinterpret_cast<uint32_t*>(smem + L.a_off + A.M * A.a_pitch);
+    uint32_t* za = reinterpret_cast<uint32_t*>(smem + L.a_off + M * A.a_pitch);
     for (int e = tid; e < A.a_pitch / 4; e += NTHREADS) za[e] = 0u;
     if constexpr (F::AFFINE) {
-      uint32_t* zx = reinterpret_cast<uint32_t*>(smem + L.xp_off + A.M * L.xp_pitch);
+      uint32_t* zx = reinterpret_cast<uint32_t*>(smem + L.xp_off + M * L.xp_pitch);
       for (int e = tid; e < L.xp_pitch / 4; e += NTHREADS) zx[e] = 0u;
     }
   }
   if (!NORM && tid < MAXM) reinterpret_cast<float*>(smem + L.row_off)[MAXM + tid] = 1.0f;
 
-  const char* wbase = reinterpret_cast<const char*>(A.w) + (size_t)r0 * wrow;
-  const char* sbase = reinterpret_cast<const char*>(A.scales) + (size_t)r0 * srow;
-  const char* bbase = reinterpret_cast<const char*>(A.biases) + (size_t)r0 * srow;
+  const char* wbase = reinterpret_cast<const char*>(wq) + (size_t)r0 * wrow;
+  const char* sbase = reinterpret_cast<const char*>(sc) + (size_t)r0 * srow;
+  const char* bbase = reinterpret_cast<const char*>(bi) + (size_t)r0 * srow;
 
   for (int ws0 = kb0; ws0 < kb1; ws0 += A.win_steps) {
     const int ns = min(A.win_steps, kb1 - ws0);
@@ -687,9 +784,9 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     // and a wave stalls at issue once the memory queues are full, so weight loads issued
     // first would hold back the staging (and every MFMA after it) by the whole burst.
     XStage xs;
-    stage_load<XT>(A, ws0 * KSTEP, ns * KSTEP, xs);
+    stage_load<XT>(A, M, xmap, ws0 * KSTEP, ns * KSTEP, xs);
     lds_barrier();  // previous window's readers are done with the LDS
-    stage_compute<FMT, XT>(A, smem, L, ws0 * KSTEP, ns * KSTEP, xs);
+    stage_compute<FMT, XT>(A, M, smem, L, ws0 * KSTEP, ns * KSTEP, xs);
     Unit<FMT> ring[PREF];
     if (nu > 0) {
 #pragma unroll
@@ -752,9 +849,9 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   // write y[m, r0 .. r1) from the tile accumulators
   const int nr = r1 - r0;
   if (A.ks == 1) {
-    for (int e = tid; e < A.M * nr; e += NTHREADS) {
+    for (int e = tid; e < M * nr; e += NTHREADS) {
       const int m = e / nr, rr = e - m * nr;
-      A.y[(size_t)m * A.N + r0 + rr] = ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)];
+      A.y[(size_t)(xmap ? xmap[MAXM + m] : m) * A.N + r0 + rr] = ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)];
     }
     return;
   }
@@ -763,8 +860,8 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   // The partials and the arrival counter are agent-scope atomic accesses, which bypass the
   // per-XCD L2 caches; a device-wide fence would instead write back and invalidate the
   // whole L2 of the XCD under every other workgroup running there.
-  float* part = A.part + (size_t)ksi * A.M * A.N;
-  for (int e = tid; e < A.M * nr; e += NTHREADS) {
+  float* part = A.part + (size_t)ksi * M * A.N;
+  for (int e = tid; e < M * nr; e += NTHREADS) {
     const int m = e / nr, rr = e - m * nr;
     __hip_atomic_store(part + (size_t)m * A.N + r0 + rr, ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)],
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -778,12 +875,12 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   }
   lds_barrier();
   if (flag[0] == 0u) return;
-  for (int e = tid; e < A.M * nr; e += NTHREADS) {
+  for (int e = tid; e < M * nr; e += NTHREADS) {
     const int m = e / nr, rr = e - m * nr;
     const float* src = A.part + (size_t)m * A.N + r0 + rr;
     float sum = 0.0f;
     for (int k = 0; k < A.ks; ++k)
-      sum += __hip_atomic_load(src + (size_t)k * A.M * A.N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sum += __hip_atomic_load(src + (size_t)k * M * A.N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     A.y[(size_t)m * A.N + r0 + rr] = sum;
   }
   if (tid == 0) __hip_atomic_store(A.counters + rgi, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -826,6 +923,24 @@ static int window_steps(int fmt, int M, int S, int tiles_max, int max_lds, size_
   return ws;
 }
 
+// The rest of a plan once the row groups and K slices are fixed: tile bound, staging
+// window and units in flight.
+static bool finish_plan(int fmt, int M, int K, int N, int rg, int ks, const DeviceInfo& dev, MfmaPlan* p) {
+  const int S = K / KSTEP;
+  p->ks = ks;
+  p->rg = rg;
+  const int rows_max = (N + rg - 1) / rg + 1;
+  p->tiles_max = (rows_max + 15) / 16 + 1;
+  const int s_wg = (S + ks - 1) / ks;
+  p->win_steps = window_steps(fmt, M, s_wg, p->tiles_max, dev.max_lds, &p->lds);
+  // Units in flight per wave: one when each wave streams only a few units (the first
+  // loads then reach the compute sooner), two for long streams; the 1-bit format's units
+  // are half as large and always keep two.
+  const int units_per_wave = ((rows_max + 15) / 16) * s_wg / NW;
+  p->pref = fmt_one_bit(fmt) ? 2 : (units_per_wave < 8 ? 1 : 2);
+  return p->win_steps > 0;
+}
+
 bool plan_mfma(int fmt, int variant, int M, int K, int N, const DeviceInfo& dev, int force_ks, MfmaPlan* p) {
   (void)variant;
   const int tiles = (N + 15) / 16;
@@ -858,19 +973,18 @@ bool plan_mfma(int fmt, int variant, int M, int K, int N, const DeviceInfo& dev,
   int rg = cus / ks;
   if (rg > tiles) rg = tiles;
   if (rg < 1) rg = 1;
-  p->ks = ks;
-  p->rg = rg;
   p->grid = rg * ks;
-  const int rows_max = (N + rg - 1) / rg + 1;
-  p->tiles_max = (rows_max + 15) / 16 + 1;
-  const int s_wg = (S + ks - 1) / ks;
-  p->win_steps = window_steps(fmt, M, s_wg, p->tiles_max, dev.max_lds, &p->lds);
-  // Units in flight per wave: one when each wave streams only a few units (the first
-  // loads then reach the compute sooner), two for long streams; the 1-bit format's units
-  // are half as large and always keep two.
-  const int units_per_wave = ((rows_max + 15) / 16) * s_wg / NW;
-  p->pref = fmt_one_bit(fmt) ? 2 : (units_per_wave < 8 ? 1 : 2);
-  return p->win_steps > 0;
+  return finish_plan(fmt, M, K, N, rg, ks, dev, p);
+}
+
+bool plan_mfma_grouped(int fmt, int M, int K, int N, int jobs, const DeviceInfo& dev, MfmaPlan* p) {
+  // One workgroup per CU (the kernels hold one per CU): at least rg_min row groups for
+  // each of the most jobs a routing can make, more when the routing makes fewer.
+  const int tiles = (N + 15) / 16;
+  int rg_min = (dev.cu_count + jobs - 1) / jobs;
+  if (rg_min > tiles) rg_min = tiles;
+  p->grid = jobs * rg_min;
+  return finish_plan(fmt, M, K, N, rg_min, 1, dev, p);
 }
 
 size_t mfma_workspace_bytes(int M, int N, const MfmaPlan& p) {
@@ -911,6 +1025,12 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.ks = p.ks;
   A.part = part;
   A.counters = counters;
+  A.route = c.route;
+  A.topk = c.topk;
+  A.E = c.E;
+  A.cap = c.cap;
+  A.w_estride = c.w_estride;
+  A.s_estride = c.s_estride;
   A.had_stages = c.had_block == 64 ? 1 : (c.had_block == 256 ? 3 : 2);
   A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
   A.signs = c.signs;

@@ -26,6 +26,11 @@ struct GemmCall {
   hipStream_t stream;
   int had_block;            // rotated format: 64, 128 or 256
   const uint32_t* signs;    // rotated format: optional sign bits [K/32]
+  // grouped expert verify: the routing [M, topk] over E experts, the most rows of a job,
+  // and the byte strides between consecutive experts' codes and scales (biases)
+  const int32_t* route;
+  int topk, E, cap;
+  long long w_estride, s_estride;
 };
 
 struct DeviceInfo {
@@ -48,6 +53,8 @@ struct MfmaPlan {
 // Returns false when the call cannot be staged in LDS.
 bool plan_mfma(int fmt, int variant, int M, int K, int N, const DeviceInfo& dev, int force_ks,
                MfmaPlan* p);
+// Plans a grouped expert verify of up to `jobs` jobs of at most M rows each (one K slice).
+bool plan_mfma_grouped(int fmt, int M, int K, int N, int jobs, const DeviceInfo& dev, MfmaPlan* p);
 // Device workspace a planned call needs (partial outputs; 0 when K is not split).
 size_t mfma_workspace_bytes(int M, int N, const MfmaPlan& p);
 

@@ -159,6 +159,30 @@ vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* s
 vg_status verify_accept_greedy(const float* y, int M, int N, const int32_t* draft, int32_t* idx,
                                int32_t* accepted, void* stream);
 
+/*
+ * Grouped routed-expert verify: for a mixture-of-experts layer whose M drafted rows are
+ * each routed to topk of E experts, y[m, s, :] = x[m, :] * W_e^T with e = route[m, s], for
+ * every routed slot, in one call that reads each routed expert's packed weights once
+ * however many rows it serves, and whose output for a slot is bit-identical whichever
+ * other rows are routed with it ("Ijah" README, "What's new (v0.2)": grouped routed-expert
+ * verify kernels).
+ *   format  VG_FMT_SIGN1, VG_FMT_AFFINE2, VG_FMT_HAD2 (block 128, unsigned) or
+ *           VG_FMT_AFFINE1; the weights of each expert as in that format's call.
+ *   x       activations [M, K], VG_F16 or VG_BF16 (VG_F32 is refused: VG_ERR_UNSUPPORTED).
+ *   route   int32 [M, topk] on the device: the expert of each (row, slot); a value outside
+ *           0..E-1 marks an unused slot.  Read by the device, so it is not validated on
+ *           the host; the call never reads or writes out of bounds whatever it holds.
+ *   w, scales, biases  the E experts' packed weights stacked expert-major: w[E, N, words
+ *           per row], scales and biases [E, N, groups per row] (biases unused and may be
+ *           NULL for VG_FMT_SIGN1).
+ *   y       fp32 [M, topk, N]; the rows of unused slots are not written.
+ * Requires 1 <= M <= 8, 1 <= topk <= 8, E >= 1, N >= 1, K a multiple of 1024.  One kernel
+ * launch; no workspace.
+ */
+vg_status verify_gemm_experts(int format, const void* x, int x_dtype, int M, int K, int E, int topk,
+                              const int32_t* route, const uint32_t* w, const uint16_t* scales,
+                              const uint16_t* biases, int N, float* y, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* vg_last_error(void);
 

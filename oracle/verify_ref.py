@@ -264,6 +264,31 @@ def magnitude_columns(fmt: str, x: np.ndarray, x_dtype: str, words: np.ndarray,
     return _matmul_chunked(np.abs(x64), len(cols), lambda a, b: np.abs(dense(a, b)))
 
 
+def verify_experts(fmt: str, x: np.ndarray, x_dtype: str, route: np.ndarray, words: np.ndarray,
+                   scales: np.ndarray, biases: np.ndarray | None, rows=None) -> np.ndarray:
+    """Routed-expert verify ("Ijah" README, "What's new (v0.2)": rows verified together
+    are routed to experts, and each expert's weights serve every row routed to it).
+
+    route int [M, topk]: the expert of each (row, slot), a value outside 0..E-1 marking an
+    unused slot; words, scales, biases: the E experts' packed weights stacked on axis 0.
+    Returns y[M, topk, N] (or only the output columns `rows`) with
+    y[m, s] = x[m] @ W_route[m, s]^T in fp64 and NaN in unused slots.  Grouping the rows
+    by expert changes which rows share a weight read, not what any row computes, so this
+    is the per-(row, slot) product of the format written out."""
+    route = np.asarray(route)
+    M, topk = route.shape
+    E = words.shape[0]
+    cols = np.arange(words.shape[1]) if rows is None else np.asarray(rows)
+    y = np.full((M, topk, len(cols)), np.nan)
+    for m in range(M):
+        for s in range(topk):
+            e = int(route[m, s])
+            if 0 <= e < E:
+                b = None if biases is None else biases[e]
+                y[m, s] = verify_columns(fmt, x[m:m + 1], x_dtype, words[e], scales[e], b, cols)[0]
+    return y
+
+
 # ----------------------------------------------------------------------------- head + checks
 def argmax_rows(y: np.ndarray):
     """Per-row argmax (first index on ties) and the gap between the top two values."""

@@ -113,6 +113,46 @@ def workload_case(name: str, seed: int = 0, N: int | None = None) -> Case:
     return draw_case(fmt, K, N0 if N is None else N, x_dtype, seed)
 
 
+@dataclass
+class ExpertsCase:
+    fmt: str
+    K: int
+    N: int
+    E: int
+    x_dtype: str
+    words: np.ndarray          # uint32 [E, N, K / WORD_K]
+    scales: np.ndarray         # uint16 fp16 bits [E, N, K / GROUP]
+    biases: np.ndarray | None  # uint16 fp16 bits [E, N, K / GROUP]
+    x_all: np.ndarray          # [8, K]
+
+    def x(self, M: int) -> np.ndarray:
+        return np.ascontiguousarray(self.x_all[:M])
+
+
+def draw_experts(fmt: str, K: int, N: int, E: int, x_dtype: str, seed: int = 0) -> ExpertsCase:
+    """E experts of one layer, each drawn as ``draw_case`` draws one matrix (expert e with
+    seed (seed, e)); the activation rows come from expert 0's draw."""
+    cases = [draw_case(fmt, K, N, x_dtype, seed=seed * 1000 + e) for e in range(E)]
+    biases = None if cases[0].biases is None else np.stack([c.biases for c in cases])
+    return ExpertsCase(fmt, K, N, E, x_dtype, np.stack([c.words for c in cases]),
+                       np.stack([c.scales for c in cases]), biases, cases[0].x_all)
+
+
+def draw_route(M: int, topk: int, E: int, seed: int = 0) -> np.ndarray:
+    """Router output int32 [M, topk]: each row's topk distinct experts, uniform over the E
+    (a mixture-of-experts router picks distinct experts per token)."""
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.choice(E, size=topk, replace=False) for _ in range(M)]).astype(np.int32)
+
+
+# Named routed-expert workloads: (format, K, N, E, topk, activation dtype).  The shape is
+# a fine-grained mixture-of-experts layer's fused gate and up projection (hidden 2048,
+# expert width 768, so N = 2 * 768), 128 experts, 8 routed per token.
+EXPERT_WORKLOADS = {
+    "moe_gate_up_affine2_e128_top8_k2048_n1536": ("affine2", 2048, 1536, 128, 8, "f16"),
+}
+
+
 def draw_signs(K: int, seed: int = 0) -> np.ndarray:
     """Sign bits of a randomized rotation: uint32 [K/32], each bit uniform (bit set: -1)."""
     rng = np.random.default_rng(seed)

@@ -471,8 +471,54 @@ def pin_greedy_accept(ref):
     assert ref.greedy_accept(y, top)[1] == 6
 
 
+def pin_experts(ref):
+    """Routed-expert verify.  Closed form: expert e holds all-ones sign bits with the exact
+    scale (e + 1) / 8, so y[m, s, n] = (route[m, s] + 1) / 8 * sum_k x[m, k]; unused slots
+    (route outside 0..E-1) are NaN.  Special case: every slot on one expert reduces to
+    the plain product.  Invariant: renumbering the experts (and the route with them)
+    changes nothing."""
+    E, M, topk, K, N = 4, 3, 3, 256, 5
+    words = np.full((E, N, K // 32), 0xFFFFFFFF, dtype=np.uint32)
+    scales = np.empty((E, N, K // 128), dtype=np.uint16)
+    for e in range(E):
+        scales[e] = np.float16((e + 1) / 8).view(np.uint16)
+    rng = np.random.default_rng(16)
+    x = _raw_x(rng.integers(-8, 9, size=(M, K)).astype(np.float64) / 4, "f16")
+    route = np.array([[2, 0, -1], [1, 1, 3], [E, 3, 0]])
+    y = ref.verify_experts("sign1", x, "f16", route, words, scales, None)
+    assert y.shape == (M, topk, N), y.shape
+    xs = ref.decode_f16(x).sum(axis=1)
+    for m in range(M):
+        for sl in range(topk):
+            e = route[m, sl]
+            if 0 <= e < E:
+                assert np.all(y[m, sl] == (e + 1) / 8 * xs[m]), (m, sl, y[m, sl])
+            else:
+                assert np.all(np.isnan(y[m, sl])), (m, sl)
+    # random weights: one expert everywhere is the plain product; a renumbering is invisible
+    fmt = "affine2"
+    wr, sr, br = [], [], []
+    for e in range(E):
+        w1, s1, b1, _ = _rand_case(rng, fmt, 1, K, N)
+        wr.append(w1), sr.append(s1), br.append(b1)
+    wr, sr, br = np.stack(wr), np.stack(sr), np.stack(br)
+    x2 = _raw_x(rng.standard_normal((M, K)), "f16")
+    one = ref.verify_experts(fmt, x2, "f16", np.full((M, 2), 2), wr, sr, br)
+    plain = ref.verify(fmt, x2, "f16", wr[2], sr[2], br[2])
+    assert _close(one[:, 0], plain) and _close(one[:, 1], plain)
+    route2 = np.array([[0, 3], [2, 1], [3, 3]])
+    perm = np.array([2, 0, 3, 1])                   # new expert i is old expert perm[i]
+    inv = np.argsort(perm)
+    a = ref.verify_experts(fmt, x2, "f16", route2, wr, sr, br)
+    b = ref.verify_experts(fmt, x2, "f16", inv[route2], wr[perm], sr[perm], br[perm])
+    assert np.array_equal(a, b)
+    cols = np.array([4, 0, 2])
+    assert np.array_equal(ref.verify_experts(fmt, x2, "f16", route2, wr, sr, br, rows=cols), a[:, :, cols])
+
+
 ALL_PINS = [pin_decode, pin_unpack_hand_words, pin_pack_roundtrip, pin_golden,
             pin_sign1_closed_form, pin_affine2_known_codes, pin_rowsum_identity,
             pin_bruteforce_fraction, pin_hadamard_identities, pin_had2_weight_side,
             pin_mlx_1bit_encoding, pin_argmax, pin_columns_and_chunks, pin_normwise,
-            pin_magnitude, pin_greedy_accept, pin_affine1, pin_hadamard_blocks_and_signs]
+            pin_magnitude, pin_greedy_accept, pin_affine1, pin_hadamard_blocks_and_signs,
+            pin_experts]

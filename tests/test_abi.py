@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
                "verify_argmax_rows", "vg_last_error", "vg_plan_variant", "vg_variant_name",
                "vg_force_variant", "vg_variant_count", "vg_debug_unpack_sign1", "vg_debug_unpack_affine2",
                "vg_plan_ksplit", "vg_force_ksplit", "verify_accept_greedy", "verify_gemm_affine1",
-               "verify_gemm_had2_signed", "hadamard_rotate_signed"):
+               "verify_gemm_had2_signed", "hadamard_rotate_signed", "verify_gemm_experts"):
         assert fn in names, fn
 
 
@@ -151,3 +151,32 @@ def test_hadamard_block_must_divide_k_and_signs_aligned():
     assert L.verify_gemm_had2_signed(ALIGNED, B.VG_F16, 1, 256, ALIGNED, ALIGNED, ALIGNED, 8, 64, ALIGNED + 2,
                                      ALIGNED, None) == B.VG_ERR_ALIGN
     assert L.hadamard_rotate_signed(ALIGNED, B.VG_F16, 1, 256, 64, ALIGNED + 1, ALIGNED, None) == B.VG_ERR_ALIGN
+
+
+def test_experts_validation():
+    L = B.lib()
+    A = ALIGNED
+
+    def call(fmt=B.FMT_AFFINE2, x=A, xt=B.VG_F16, M=2, K=2048, E=8, topk=4, route=A, w=A, s=A, b=A, N=64, y=A):
+        return L.verify_gemm_experts(fmt, x, xt, M, K, E, topk, route, w, s, b, N, y, None)
+
+    assert call(fmt=4) == B.VG_ERR_ARG and "format" in _err()
+    assert call(fmt=-1) == B.VG_ERR_ARG
+    assert call(M=0) == B.VG_ERR_SHAPE
+    assert call(M=9) == B.VG_ERR_SHAPE
+    assert call(E=0) == B.VG_ERR_SHAPE
+    assert call(topk=0) == B.VG_ERR_SHAPE
+    assert call(topk=9) == B.VG_ERR_SHAPE
+    assert call(N=0) == B.VG_ERR_SHAPE
+    assert call(xt=B.VG_F32) == B.VG_ERR_UNSUPPORTED and "fp16 or bf16" in _err()
+    assert call(xt=7) == B.VG_ERR_DTYPE
+    assert call(K=1536) == B.VG_ERR_UNSUPPORTED and "1024" in _err()
+    assert call(route=None) == B.VG_ERR_ARG and "route" in _err()
+    assert call(route=A + 2) == B.VG_ERR_ALIGN
+    assert call(w=None) == B.VG_ERR_ARG
+    assert call(s=A + 4) == B.VG_ERR_ALIGN
+    assert call(b=None) == B.VG_ERR_ARG and "biases" in _err()
+    assert call(fmt=B.FMT_HAD2, b=None) == B.VG_ERR_ARG
+    assert call(fmt=B.FMT_AFFINE1, b=None) == B.VG_ERR_ARG
+    assert call(y=A + 8) == B.VG_ERR_ALIGN
+    assert call(x=None) == B.VG_ERR_ARG

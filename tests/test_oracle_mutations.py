@@ -200,13 +200,50 @@ def _mut_signs_after_rotation(m):
     m.hadamard_rotate = hadamard_rotate
 
 
+def _experts_mutant(m, pick):
+    """An explicit routed-expert verify whose (row, slot) -> (x row, expert, output) map
+    is `pick(route, m, s, E)` -> (x row, expert or None)."""
+    def verify_experts(fmt, x, x_dtype, route, words, scales, biases, rows=None):
+        route = np.asarray(route)
+        M, topk = route.shape
+        E = words.shape[0]
+        cols = np.arange(words.shape[1]) if rows is None else np.asarray(rows)
+        y = np.full((M, topk, len(cols)), np.nan)
+        for r in range(M):
+            for sl in range(topk):
+                xr, e = pick(route, r, sl, E)
+                if e is not None:
+                    b = None if biases is None else biases[e]
+                    y[r, sl] = m.verify_columns(fmt, x[xr:xr + 1], x_dtype, words[e], scales[e], b, cols)[0]
+        return y
+    m.verify_experts = verify_experts
+
+
+def _mut_experts_first_slot_only(m):
+    _experts_mutant(m, lambda rt, r, sl, E: (r, int(rt[r, 0]) if 0 <= rt[r, 0] < E else None))
+
+
+def _mut_experts_slot_as_row(m):
+    _experts_mutant(m, lambda rt, r, sl, E: (sl % rt.shape[0], int(rt[r, sl]) if 0 <= rt[r, sl] < E else None))
+
+
+def _mut_experts_wraps_out_of_range(m):
+    _experts_mutant(m, lambda rt, r, sl, E: (r, int(rt[r, sl]) % E))
+
+
+def _mut_experts_off_by_one(m):
+    _experts_mutant(m, lambda rt, r, sl, E: (r, (int(rt[r, sl]) + 1) % E if 0 <= rt[r, sl] < E else None))
+
+
 MUTATIONS = [_mut_sign1_msb_first, _mut_affine2_code_order, _mut_sign_polarity, _mut_drop_bias,
              _mut_sign1_group_size, _mut_affine2_group_index, _mut_hadamard_unnormalized,
              _mut_hadamard_wrong_recursion, _mut_hadamard_skipped, _mut_bf16_shift,
              _mut_f16_as_bf16, _mut_rows_reversed, _mut_chunk_offset, _mut_argmax_last_tie,
              _mut_normwise_elementwise, _mut_magnitude_signed_x,
              _mut_magnitude_unrotated, _mut_accept_counts_all_matches, _mut_affine1_group_64,
-             _mut_affine1_bias_on_set_bits_only, _mut_signs_after_rotation]
+             _mut_affine1_bias_on_set_bits_only, _mut_signs_after_rotation,
+             _mut_experts_first_slot_only, _mut_experts_slot_as_row, _mut_experts_wraps_out_of_range,
+             _mut_experts_off_by_one]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__[5:])
