@@ -113,7 +113,7 @@ struct MfmaArgs {
 //   job (first 128 bytes): grouped expert verify, the workgroup's job (find_job)
 constexpr int JOB_BYTES = 128;
 struct LdsLayout {
-  int a_off, e_off, xp_off, xp_pitch, ytile_off, slot_off, row_off, flag_off, total;
+  int a_off, e_off, xp_off, xp_pitch, ytile_off, slot_off, row_off, flag_off, red_off, total;
   __host__ __device__ LdsLayout(int fmt, int M, int win_steps, int tiles_max) {
     const int groups = win_steps * fmt_gps(fmt);
     const int pitch = groups * fmt_gs(fmt) + 16;   // must equal MfmaArgs::a_pitch
@@ -125,7 +125,8 @@ struct LdsLayout {
     slot_off = ytile_off + tiles_max * MAXM * 16 * 4;
     row_off = slot_off + NW * 2 * MAXM * 16 * 4;
     flag_off = row_off + 2 * MAXM * 4;
-    total = flag_off + 16;
+    red_off = flag_off + 16;   // split tiles of the window, one word per wave boundary
+    total = red_off + NW * 4;
   }
 };
 
@@ -694,7 +695,9 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
-  const int r0 = (int)(((long long)A.N * rgi) / rg), r1 = (int)(((long long)A.N * (rgi + 1)) / rg);
+  // row group rgi: rows [r0, r1), the first N % rg groups one row longer
+  const int rq = A.N / rg, rrem = A.N - rq * rg;
+  const int r0 = rgi * rq + min(rgi, rrem), r1 = r0 + rq + (rgi < rrem ? 1 : 0);
   const int T = (r1 - r0 + 15) / 16;
   const int S = A.K / KSTEP;
   const int kb0 = (S * ksi) / A.ks, kb1 = (S * (ksi + 1)) / A.ks;   // this slice's K-steps
@@ -721,7 +724,6 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   const uint32_t xp_lane0 = L.xp_off + (uint32_t)arow * L.xp_pitch + (uint32_t)g * 16u;
 
   float* ytile = reinterpret_cast<float*>(smem + L.ytile_off);
-  for (int e = tid; e < T * MAXM * 16; e += NTHREADS) ytile[e] = 0.0f;
   {
     // the zero rows: never written by the staging, so cleared once per launch
     uint32_t* za = reinterpret_cast<uint32_t*>(smem + L.a_off + M * A.a_pitch);
@@ -733,6 +735,8 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   }
   if (!NORM && tid < MAXM) reinterpret_cast<float*>(smem + L.row_off)[MAXM + tid] = 1.0f;
 
+  for (int e = tid; e < T * MAXM * 16; e += NTHREADS) ytile[e] = 0.0f;
+
   const char* wbase = reinterpret_cast<const char*>(wq) + (size_t)r0 * wrow;
   const char* sbase = reinterpret_cast<const char*>(sc) + (size_t)r0 * srow;
   const char* bbase = reinterpret_cast<const char*>(bi) + (size_t)r0 * srow;
@@ -740,13 +744,12 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   for (int ws0 = kb0; ws0 < kb1; ws0 += A.win_steps) {
     const int ns = min(A.win_steps, kb1 - ws0);
     const int UW = T * ns;
-    const int ua = (int)(((long long)UW * wid) / NW), ub = (int)(((long long)UW * (wid + 1)) / NW);
+    const int ua = (int)(((uint32_t)UW * wid) / NW), ub = (int)(((uint32_t)UW * (wid + 1)) / NW);
     const int nu = ub - ua;
 
     // Load cursor (tile lt, step ls), kept uniform; the lane part of a load address is a
-    // per-tile constant, the rest is a scalar offset.  Loads past the wave's last unit
-    // repeat the last unit, so every ring slot is reloaded unconditionally and the loads
-    // of later units stay in flight while earlier ones compute.
+    // per-tile constant, the rest is a scalar offset.  Each of the wave's units is loaded
+    // once, PREF units ahead of the one computing.
     int lt = nu > 0 ? ua / ns : 0, ls = nu > 0 ? ua - lt * ns : 0, issued = 0;
     uint32_t lw_lane = 0, ls_lane = 0;
     auto set_load_tile = [&](int t) {
@@ -786,12 +789,36 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     XStage xs;
     stage_load<XT>(A, M, xmap, ws0 * KSTEP, ns * KSTEP, xs);
     lds_barrier();  // previous window's readers are done with the LDS
+    // The tiles split between waves in this window, for the reduction after it: wave
+    // boundary bw (lanes 0..NW-2 of wave 0) records, when it falls strictly inside a tile
+    // and is that tile's first such boundary, the tile, the waves whose unit range meets
+    // it (mask) and which of them started before it (their slot 1).  Bit 31 marks a
+    // record.  Written after the barrier that ends the previous window's reduction, read
+    // after the one that follows the staging.
+    if (wid == 0 && lane < NW - 1) {
+      const int bw = lane + 1;
+      const int B = (int)(((uint32_t)UW * bw) / NW);
+      const int t = B / ns, t0 = t * ns;
+      uint32_t rec = 0;
+      if (B > 0 && B < UW && B != t0 && !(bw > 1 && (int)(((uint32_t)UW * (bw - 1)) / NW) > t0)) {
+        uint32_t mask = 0, late = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+          const int a2 = (int)(((uint32_t)UW * w2) / NW), b2 = (int)(((uint32_t)UW * (w2 + 1)) / NW);
+          if (a2 < b2 && b2 > t0 && a2 < t0 + ns) {
+            mask |= 1u << w2;
+            if (a2 < t0) late |= 1u << w2;
+          }
+        }
+        rec = (1u << 31) | ((uint32_t)t << 16) | (late << 8) | mask;
+      }
+      reinterpret_cast<uint32_t*>(smem + L.red_off)[lane] = rec;
+    }
     stage_compute<FMT, XT>(A, M, smem, L, ws0 * KSTEP, ns * KSTEP, xs);
     Unit<FMT> ring[PREF];
-    if (nu > 0) {
 #pragma unroll
-      for (int d = 0; d < PREF; ++d) issue(ring[d]);
-    }
+    for (int d = 0; d < PREF; ++d)
+      if (d < nu) issue(ring[d]);
     lds_barrier();
 
     int ct = nu > 0 ? ua / ns : 0, cs = nu > 0 ? ua - ct * ns : 0;
@@ -807,7 +834,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
           compute_unit<FMT, MODE>(ring[d], smem, a_lane, e_lane, xp_lane, mk, mg, yacc, yb);
           if (++cs == ns || base + d + 1 == nu) {
             const bool sole = ua <= ct * ns && ub >= (ct + 1) * ns;
-            flush_tile<FMT, MODE>(smem, L, ct, sole, ct == ua / ns ? 0 : 1, wid, g, i, yacc, yb);
+            flush_tile<FMT, MODE>(smem, L, ct, sole, ua >= ct * ns ? 0 : 1, wid, g, i, yacc, yb);
 #pragma unroll
             for (int r = 0; r < 4; ++r) yacc[r] = 0.f;
             yb = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -815,31 +842,33 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
             ++ct;
           }
         }
-        issue(ring[d]);
+        // refill the slot only while units remain: a load past the last unit would still
+        // be in flight after the loop, and the first reuse of its registers would wait
+        // for it
+        if (base + d + PREF < nu) issue(ring[d]);
       }
     }
     lds_barrier();
 
     // fixed-order reduction of tiles split between waves: a tile is split when a wave
     // boundary falls strictly inside it; its contributors are the non-empty waves whose
-    // unit range meets it, summed in wave order.
+    // unit range meets it, summed in wave order (a contributor's slot 0 holds the tile
+    // its range starts in, slot 1 the tile it ends in).  Two waves take each boundary;
+    // every wave's candidate slot is read at once and non-contributors add +0.
     {
       const float* slots = reinterpret_cast<const float*>(smem + L.slot_off);
+      const uint32_t* red = reinterpret_cast<const uint32_t*>(smem + L.red_off);
       const int e = tid & 127;                 // element (row, col) of a tile
-      for (int bw = 1 + (tid >> 7); bw < NW; bw += NTHREADS / 128) {
-        const int B = (int)(((long long)UW * bw) / NW);
-        if (B <= 0 || B >= UW || B % ns == 0) continue;
-        const int t = B / ns;
-        // handle tile t once: by the first boundary inside it
-        const int Bprev = (int)(((long long)UW * (bw - 1)) / NW);
-        if (bw > 1 && Bprev > t * ns && Bprev % ns != 0 && Bprev / ns == t) continue;
+      for (int bw = 1 + __builtin_amdgcn_readfirstlane(tid >> 7); bw < NW; bw += NTHREADS / 128) {
+        const uint32_t rec = __builtin_amdgcn_readfirstlane(red[bw - 1]);
+        if (!(rec >> 31)) continue;
+        const int t = (int)((rec >> 16) & 0x7FFFu);
+        float v[NW];
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) v[w2] = slots[(w2 * 2 + ((rec >> (8 + w2)) & 1u)) * (MAXM * 16) + e];
         float sum = 0.0f;
-        for (int w2 = 0; w2 < NW; ++w2) {
-          const int a2 = (int)(((long long)UW * w2) / NW), b2 = (int)(((long long)UW * (w2 + 1)) / NW);
-          if (a2 >= b2 || b2 <= t * ns || a2 >= (t + 1) * ns) continue;
-          const int slot = (t == a2 / ns) ? 0 : 1;
-          sum += slots[(w2 * 2 + slot) * (MAXM * 16) + e];
-        }
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) sum += ((rec >> w2) & 1u) ? v[w2] : 0.0f;
         ytile[t * (MAXM * 16) + e] += sum;
       }
     }
@@ -931,6 +960,7 @@ static bool finish_plan(int fmt, int M, int K, int N, int rg, int ks, const Devi
   p->rg = rg;
   const int rows_max = (N + rg - 1) / rg + 1;
   p->tiles_max = (rows_max + 15) / 16 + 1;
+  if (p->tiles_max > 32767) return false;   // the split-tile records hold 15-bit tile indices
   const int s_wg = (S + ks - 1) / ks;
   p->win_steps = window_steps(fmt, M, s_wg, p->tiles_max, dev.max_lds, &p->lds);
   // Units in flight per wave: one when each wave streams only a few units (the first
