@@ -230,17 +230,24 @@ __device__ __forceinline__ void load_x32_f32(const void* x, int K, int m, int k0
 constexpr int MAXT = 3;   // activation chunks (32 K of one row) per thread and window
 struct XStage {
   u32x4 d[MAXT][4];       // raw fp16/bf16 bits of 32 consecutive activations
+  int m[MAXT], c[MAXT];   // the chunk's row and its index within the row's window
 };
 
 template <int XT>
 // xmap: the x row of each row (grouped expert verify), or null for x rows 0..M-1.
 __device__ __forceinline__ void stage_load(const MfmaArgs& A, int M, const int* xmap, int k0, int WK, XStage& xs) {
   const int nchunks = WK / 32, ntask = M * nchunks;
+  // row = t / nchunks = (t / 32) / (WK / 1024) for t < MAXT * NTHREADS, by a float
+  // reciprocal: (n + 1/2) / s lies at least 1/(2s) from an integer, far beyond the
+  // rounding of the product for n < 64 and s <= 64
+  const float inv_steps = 1.0f / (float)(WK / KSTEP);
 #pragma unroll
   for (int j = 0; j < MAXT; ++j) {
     const int t = threadIdx.x + j * NTHREADS;
+    const int m = (int)(((float)(t >> 5) + 0.5f) * inv_steps), c = t - m * nchunks;
+    xs.m[j] = m;
+    xs.c[j] = c;
     if (t < ntask) {
-      const int m = t / nchunks, c = t - m * nchunks;
       const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.x) + (size_t)(xmap ? xmap[m] : m) * A.K + k0 + 32 * c);
 #pragma unroll
       for (int q = 0; q < 4; ++q) xs.d[j][q] = p[q];
@@ -256,6 +263,14 @@ __device__ __forceinline__ void chunk_halves(const XStage& xs, int j, uint32_t h
       hv[8 * q + 2 * i] = xs.d[j][q][i] & 0xFFFFu;
       hv[8 * q + 2 * i + 1] = xs.d[j][q][i] >> 16;
     }
+}
+
+// A pair of raw 16-bit activations of chunk j as one dword: element a in the low half,
+// element b in the high half (a and b of the same parity), by one byte permute.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pair_raw(const XStage& xs, int j, int a, int b) {
+  const uint32_t lo = xs.d[j][(a >> 1) >> 2][(a >> 1) & 3], hi = xs.d[j][(b >> 1) >> 2][(b >> 1) & 3];
+  return __builtin_amdgcn_perm(hi, lo, (a & 1) ? 0x07060302u : 0x05040100u);
 }
 
 template <int XT>
@@ -283,12 +298,16 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
     for (int j = 0; j < MAXT; ++j) {
       const int t = tid + j * NTHREADS;
       if (t < ntask) {
-        uint32_t hv[32];
-        chunk_halves(xs, j, hv);
-        float mx = 0.0f;
+        // magnitudes of one 16-bit float type order like their bit patterns with the sign
+        // cleared: two per packed integer max
+        u16x2 mx2 = {0, 0};
 #pragma unroll
-        for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(half_bits_to_f32<XT>(hv[e])));
-        atomicMax(&rowmax[t / nchunks], __float_as_uint(mx));
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, xs.d[j][q][i] & 0x7FFF7FFFu));
+        const uint32_t mb = mx2[0] > mx2[1] ? mx2[0] : mx2[1];
+        atomicMax(&rowmax[xs.m[j]], __float_as_uint(half_bits_to_f32<XT>(mb)));
       }
     }
     lds_barrier();
@@ -312,25 +331,40 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
   for (int j = 0; j < MAXT; ++j) {
     const int t = tid + j * NTHREADS;
     if (t >= ntask) continue;   // whole blocks of 8 lanes skip together (32 | ntask, 64 | NTHREADS)
-    const int m = t / nchunks, c = t - m * nchunks;
-    uint32_t hv[32];  // fp16 bits, natural K order within the chunk
-    chunk_halves(xs, j, hv);
-    if constexpr (NORM) {
+    const int m = xs.m[j], c = xs.c[j];
+    uint32_t hv[32];  // rotated and rescaled fp16 bits, natural K order (rotated format only)
+    float scale = 1.0f;
+    if constexpr (NORM) scale = rowf[m];
+    if constexpr (HAD) {
+      chunk_halves(xs, j, hv);
       float v[32];
 #pragma unroll
       for (int e = 0; e < 32; ++e) v[e] = half_bits_to_f32<XT>(hv[e]);
-      float scale = rowf[m];
-      if constexpr (HAD) {
-        if (A.signs) {
-          const uint32_t sw = A.signs[(k0 >> 5) + c];   // the chunk's 32 sign bits
+      if (A.signs) {
+        const uint32_t sw = A.signs[(k0 >> 5) + c];   // the chunk's 32 sign bits
 #pragma unroll
-          for (int e = 0; e < 32; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((sw >> e) & 1u) << 31));
-        }
-        scale *= fwht_lanes(v, c & ((1 << A.had_stages) - 1), A.had_stages) * A.had_scale;
+        for (int e = 0; e < 32; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((sw >> e) & 1u) << 31));
       }
+      scale *= fwht_lanes(v, c & ((1 << A.had_stages) - 1), A.had_stages) * A.had_scale;
 #pragma unroll
       for (int e = 0; e < 32; ++e) hv[e] = f32_to_f16_bits(v[e] * scale);
     }
+    // Activations a (low half) and b (high half) of the chunk as an fp16 pair.  bf16 input:
+    // the power-of-two rescale maps it exactly into fp16 (8 significant bits fit in 11;
+    // only values over 2^27 times smaller than the row maximum reach the fp16
+    // subnormals), so converting a pair at once with truncation gives the same halves.
+    auto pair = [&](int a, int b) -> uint32_t {
+      if constexpr (HAD) {
+        return hv[a] | (hv[b] << 16);
+      } else if constexpr (NORM) {
+        const uint32_t da = xs.d[j][(a >> 1) >> 2][(a >> 1) & 3], db = xs.d[j][(b >> 1) >> 2][(b >> 1) & 3];
+        const float fa = __uint_as_float((a & 1) ? (da & 0xFFFF0000u) : (da << 16));
+        const float fb = __uint_as_float((b & 1) ? (db & 0xFFFF0000u) : (db << 16));
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa * scale, fb * scale));
+      } else {
+        return pair_raw(xs, j, a, b);
+      }
+    };
 
     // pair dwords, sums, LDS writes
     char* arow = smem + L.a_off + m * pitch;
@@ -342,7 +376,7 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
       float e = 0.0f, xsum = 0.0f;
 #pragma unroll
       for (int b0 = 0; b0 < 16; ++b0) {
-        pd[b0] = hv[b0] | (hv[b0 + 16] << 16);
+        pd[b0] = pair(b0, b0 + 16);
         const _Float16 cf = (_Float16)(sign1_beta(b0) + (FMT == SIGN1 ? 1.0f : 0.0f));
         const f16x2 ph = __builtin_bit_cast(f16x2, pd[b0]);
         e = __builtin_amdgcn_fdot2(ph, f16x2{cf, cf}, e, false);
@@ -382,7 +416,7 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
         uint32_t pd[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          pd[jj] = hv[16 * ww + jj] | (hv[16 * ww + jj + 8] << 16);
+          pd[jj] = pair(16 * ww + jj, 16 * ww + jj + 8);
           const _Float16 bj = (_Float16)affine2_beta(jj);
           const f16x2 ph = __builtin_bit_cast(f16x2, pd[jj]);
           r = __builtin_amdgcn_fdot2(ph, f16x2{bj, bj}, r, false);
