@@ -604,10 +604,11 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
 
 // Finishes a wave's contribution to tile t for the current window: undo the row scaling,
 // sum the lane-groups holding the same rows (register swaps between lane rows), then
-// either add into the tile accumulator (sole contributor) or park it in the wave's slot
-// for the fixed-order reduction.
+// either add into the tile accumulator (sole contributor; the first window stores, so the
+// accumulator needs no clearing) or park it in the wave's slot for the fixed-order
+// reduction.
 template <int FMT, int MODE>
-__device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t, bool sole, int slot,
+__device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t, bool sole, bool first, int slot,
                                            int wid, int g, int i, const float yacc[4], const f32x4& yb) {
   const float* invf = reinterpret_cast<const float*>(smem + L.row_off) + MAXM;
   const int m0 = MODE == VAR_MFMA_Q ? 0 : 4 * (g & 1);
@@ -629,7 +630,7 @@ __device__ __forceinline__ void flush_tile(char* smem, const LdsLayout& L, int t
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float* p = dst + (m0 + r) * 16 + i;
-      *p = sole ? *p + v[r] : v[r];
+      *p = sole && !first ? *p + v[r] : v[r];
     }
   }
 }
@@ -761,15 +762,14 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   {
     // the zero rows: never written by the staging, so cleared once per launch
     uint32_t* za = reinterpret_cast<uint32_t*>(smem + L.a_off + M * A.a_pitch);
-    for (int e = tid; e < A.a_pitch / 4; e += NTHREADS) za[e] = 0u;
+    for (int e = tid; e < A.a_pitch / 16; e += NTHREADS) reinterpret_cast<u32x4*>(za)[e] = u32x4{0u, 0u, 0u, 0u};
     if constexpr (F::AFFINE) {
       uint32_t* zx = reinterpret_cast<uint32_t*>(smem + L.xp_off + M * L.xp_pitch);
-      for (int e = tid; e < L.xp_pitch / 4; e += NTHREADS) zx[e] = 0u;
+      for (int e = tid; e < L.xp_pitch / 16; e += NTHREADS) reinterpret_cast<u32x4*>(zx)[e] = u32x4{0u, 0u, 0u, 0u};
     }
   }
   if (!NORM && tid < MAXM) reinterpret_cast<float*>(smem + L.row_off)[MAXM + tid] = 1.0f;
 
-  for (int e = tid; e < T * MAXM * 16; e += NTHREADS) ytile[e] = 0.0f;
 
   const char* wbase = reinterpret_cast<const char*>(wq) + (size_t)r0 * wrow;
   const char* sbase = reinterpret_cast<const char*>(sc) + (size_t)r0 * srow;
@@ -868,7 +868,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
           compute_unit<FMT, MODE>(ring[d], smem, a_lane, e_lane, xp_lane, mk, mg, yacc, yb);
           if (++cs == ns || base + d + 1 == nu) {
             const bool sole = ua <= ct * ns && ub >= (ct + 1) * ns;
-            flush_tile<FMT, MODE>(smem, L, ct, sole, ua >= ct * ns ? 0 : 1, wid, g, i, yacc, yb);
+            flush_tile<FMT, MODE>(smem, L, ct, sole, ws0 == kb0, ua >= ct * ns ? 0 : 1, wid, g, i, yacc, yb);
 #pragma unroll
             for (int r = 0; r < 4; ++r) yacc[r] = 0.f;
             yb = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -903,7 +903,8 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
         float sum = 0.0f;
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2) sum += ((rec >> w2) & 1u) ? v[w2] : 0.0f;
-        ytile[t * (MAXM * 16) + e] += sum;
+        float* yt = ytile + t * (MAXM * 16) + e;
+        *yt = ws0 == kb0 ? sum : *yt + sum;
       }
     }
   }
