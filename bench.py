@@ -3,11 +3,14 @@
 
 Default workload: 2-bit affine g64 weights, MLP up-projection shape K=5120, N=17408,
 fp16 activations, verify calls at every row count M = 1..8.  A "step" is one verify call
-at each M (8 calls).  The timed region runs `--steps` steps as eight blocks of calls of
-one row count each, with a HIP event pair around each block (events on the stream the
-kernels run on), and cycles through a pool of >= 1 GiB of distinct weight copies so the
-256 MB Infinity Cache cannot serve repeated calls.  Inputs are resident in HBM before
-timing starts.
+at each M (8 calls).  The timed region runs exactly `--steps` steps, split into `--trials`
+trials; each trial runs one block of calls per row count with a HIP event pair around it
+(events on the stream the kernels run on), and the calls cycle through a pool of >= 1 GiB of
+distinct weight copies so the 256 MB Infinity Cache cannot serve repeated calls.  Per-M
+figures are the median over the trials (the min is given too), and host_us_per_call is the
+host time of issuing a call through the Python binding.  Inputs are resident in HBM before
+timing starts.  stream_ceiling times the library's plain streaming-read kernel over the
+same bytes and pool size the same way: the bandwidth reading those bytes can reach here.
 
 For the output-head workload a call is the verify GEMM followed by the argmax of every row
 (the head's argmax step), so its per-M times include both kernels.
@@ -25,6 +28,8 @@ t(M=8)/t(M=1), a roofline object for the dominant kernel and the CPU oracle base
 Options:
   --workload NAME    another named workload (see synthetic.inputs.WORKLOADS)
   --m LIST           only these row counts, e.g. "8" (for profiling one kernel)
+  --trials T         split the timed steps into T trials (default 7); per-M figures are
+                     the median over the trials (and the min)
   --force-variant V  run every call on kernel variant V (vg_mfma_q, vg_mfma_h, vg_valu)
                      instead of the per-shape dispatch, for A/B timing
   --table            also print one JSON line per workload and M (not the default)
@@ -78,32 +83,61 @@ def x_bytes(case, M):
     return M * case.K * (4 if case.x_dtype == "f32" else 2)
 
 
+def host_cpu() -> dict:
+    """Host CPU model and logical core count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for l in f:
+                if l.startswith("model name"):
+                    model = l.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "os_cpu_count": os.cpu_count()}
+
+
+def _timed_reps(fn, budget_s: float, max_reps: int):
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        fn()
+        reps += 1
+        if time.perf_counter() - t0 > budget_s or reps >= max_reps:
+            break
+    return (time.perf_counter() - t0) / reps, reps
+
+
 def cpu_baseline(case) -> dict:
-    """The oracle (fp64 numpy, untuned) on the host, on a bounded sample of columns."""
+    """The oracle (fp64 numpy, untuned) on the host, on a bounded sample of columns: with
+    BLAS on every thread it uses, and on one thread."""
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     M = 8
     ncols = min(case.N, 8192)
     cols = np.arange(ncols)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oracle.verify_columns(case.fmt, case.x(M), case.x_dtype, case.words, case.scales,
-                              case.biases, cols)
-        reps += 1
-        if time.perf_counter() - t0 > 10.0 or reps >= 20:
-            break
-    dt = (time.perf_counter() - t0) / reps
     frac = ncols / case.N
+
+    def run():
+        oracle.verify_columns(case.fmt, case.x(M), case.x_dtype, case.words, case.scales, case.biases, cols)
+
+    dt, reps = _timed_reps(run, 10.0, 20)
     gbs = packed_bytes(case) * frac / dt / 1e9
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            dt1, reps1 = _timed_reps(run, 5.0, 5)
+        one = {"value": packed_bytes(case) * frac / dt1 / 1e9, "reps": reps1, "ms_per_rep": round(dt1 * 1e3, 1)}
     return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"M=8, first {ncols} of {case.N} output columns of {case.fmt} K={case.K}, "
                       f"{reps} reps, {dt * 1e3:.1f} ms/rep; us/call-equivalent "
-                      f"{dt / frac * 1e6:.0f}"}
+                      f"{dt / frac * 1e6:.0f}",
+            "one_thread": one, "host": host_cpu()}
 
 
 def cpu_baseline_experts(ec, routes) -> dict:
@@ -234,6 +268,40 @@ def bench_experts(args, vg, torch, dev) -> dict:
     return line
 
 
+def trial_sizes(steps: int, trials: int):
+    """Split `steps` timed steps into `trials` trials of near-equal size (all of them run)."""
+    trials = max(1, min(trials, steps))
+    return [steps // trials + (1 if t < steps % trials else 0) for t in range(trials)]
+
+
+def stream_ceiling(vg, torch, dev, nbytes: int, ncopy: int, warmup: int, sizes) -> dict:
+    """The library's streaming-read kernel over a pool of `ncopy` distinct buffers of one
+    call's packed bytes, timed like the calls (median over the trials): the bandwidth a
+    kernel doing nothing but reading those bytes reaches here."""
+    n16 = (nbytes + 15) // 16 * 16
+    pool = [torch.empty((n16 // 4,), dtype=torch.int32, device=dev).fill_(1) for _ in range(ncopy)]
+    sink = torch.empty((vg.lib().vg_stream_read_blocks(),), dtype=torch.int32, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    for j in range(warmup):
+        vg.stream_read(pool[j % ncopy], n16, sink, stream=sh)
+    torch.cuda.synchronize()
+    per = []
+    j = 0
+    for n in sizes:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            vg.stream_read(pool[j % ncopy], n16, sink, stream=sh)
+            j += 1
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / n)
+    us = float(np.median(per))
+    del pool
+    return {"us_per_call": round(us, 3), "gbs": round(n16 / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * n16 / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1), "bytes": n16}
+
+
 def load_traffic(kernel: str, digest: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -304,6 +372,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--trials", type=int, default=7)
     ap.add_argument("--workload", default="mlp_up_affine2_k5120_n17408")
     ap.add_argument("--table", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -366,37 +435,51 @@ def main() -> int:
         head = name.startswith("head_")
         idx = {M: torch.empty((M,), dtype=torch.int32, device=dev) for M in Ms}
 
+        sh = torch.cuda.current_stream().cuda_stream   # the raw handle: no lookup per call
+
         def call(M, j):
             w, s, b = pool[j % ncopy]
-            vg.verify_gemm(fmt, x_all[M], w, s, b, y=ys[M])
+            vg.verify_gemm(fmt, x_all[M], w, s, b, y=ys[M], stream=sh)
             if head:
-                vg.verify_argmax_rows(ys[M], idx=idx[M])
+                vg.verify_argmax_rows(ys[M], idx=idx[M], stream=sh)
 
         for M in Ms:
             for j in range(args.warmup):
                 call(M, j)
         torch.cuda.synchronize()
 
-        ev = {M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
+        # the K timed steps run as `trials` trials; each (trial, M) block of calls has its own
+        # event pair on the kernels' stream
+        sizes = trial_sizes(args.steps, args.trials)
+        ev = [{M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
+              for _ in sizes]
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
+        host_s = {M: 0.0 for M in Ms}
         j = 0
-        for M in Ms:
-            ev[M][0].record()
-            for _ in range(args.steps):
-                call(M, j)
-                j += 1
-            ev[M][1].record()
+        for t, n in enumerate(sizes):
+            for M in Ms:
+                ev[t][M][0].record()
+                h0 = time.perf_counter()
+                for _ in range(n):
+                    call(M, j)
+                    j += 1
+                host_s[M] += time.perf_counter() - h0
+                ev[t][M][1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
-        us = {M: ev[M][0].elapsed_time(ev[M][1]) * 1e3 / args.steps for M in Ms}
+        trial_us = {M: [ev[t][M][0].elapsed_time(ev[t][M][1]) * 1e3 / n for t, n in enumerate(sizes)] for M in Ms}
+        us = {M: float(np.median(trial_us[M])) for M in Ms}
         total_s = sum(us.values()) * args.steps * 1e-6
         value = pb * len(Ms) * args.steps / total_s / 1e9
         per_m = {str(M): {"us_per_call": round(us[M], 3),
+                          "us_per_call_min": round(min(trial_us[M]), 3),
+                          "host_us_per_call": round(host_s[M] / args.steps * 1e6, 2),
                           "gbs": round(pb / (us[M] * 1e-6) / 1e9, 1),
                           "pct_hbm_peak": round(100 * pb / (us[M] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
                           "variant": vg.variant_name(vg.plan_variant(fmt, x_dtype, M, N, K))}
                  for M in Ms}
+        ceiling = stream_ceiling(vg, torch, dev, pb, ncopy, args.warmup, sizes)
         Mtop = max(Ms)
         kern = per_m[str(Mtop)]["variant"]
         algo = pb + x_bytes(case, Mtop) + Mtop * N * 4
@@ -416,6 +499,8 @@ def main() -> int:
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic, "kernel": kern, "M": Mtop,
                          "algorithmic_bytes_per_launch": algo},
+            "stream_ceiling": ceiling,
+            "trials": len(sizes),
             "wall_s_timed": round(wall, 4),
         }
         if name == args.workload:

@@ -51,6 +51,8 @@ _SIGS = {
     "vg_variant_count": (_I, []),
     "vg_plan_ksplit": (_I, [_I, _I, _I, _I, _I]),
     "vg_force_ksplit": (_I, [_I]),
+    "vg_stream_read_blocks": (_I, []),
+    "vg_stream_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
     "vg_debug_unpack_sign1": (_I, [_P, _I, _I, _P, _P]),
     "vg_debug_unpack_affine2": (_I, [_P, _I, _I, _P, _P]),
 }
@@ -83,6 +85,10 @@ def _torch():
 
 
 def _stream(stream):
+    """A HIP stream handle: None (torch's current stream), a torch stream, or a raw handle
+    (int), which skips the current-stream lookup on hot call paths."""
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -216,6 +222,15 @@ def verify_accept_greedy(y, draft, idx=None, accepted=None, stream=None):
         accepted = torch.empty((1,), dtype=torch.int32, device=y.device)
     _check(lib().verify_accept_greedy(_ptr(y), M, N, _ptr(draft), _ptr(idx), _ptr(accepted), _stream(stream)))
     return idx, accepted
+
+
+def stream_read(buf, nbytes: int, sink=None, stream=None):
+    """Measurement aid: read nbytes of the device tensor buf once (vg_stream_read)."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty((lib().vg_stream_read_blocks(),), dtype=torch.int32, device=buf.device)
+    _check(lib().vg_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
+    return sink
 
 
 def debug_unpack(fmt: str, w, K, codes=None, stream=None):

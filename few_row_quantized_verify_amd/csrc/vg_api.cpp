@@ -401,6 +401,25 @@ int vg_plan_ksplit(int format, int x_dtype, int M, int N, int K) {
   return vg::plan_mfma(format, var, M, K, N, dev, g_forced_ks, &p) ? p.ks : -1;
 }
 
+int vg_stream_read_blocks(void) {
+  vg::DeviceInfo dev;
+  if (device_info(&dev) != VG_OK) return -1;
+  return vg::stream_read_blocks(dev);
+}
+
+vg_status vg_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (vg_status s = check_ptr(buf, "buf")) return s;
+  if (bytes == 0 || bytes % 16 != 0) return fail(VG_ERR_SHAPE, "bytes=%zu is not a positive multiple of 16", bytes);
+  if (!sink) return fail(VG_ERR_ARG, "sink is null");
+  if (reinterpret_cast<uintptr_t>(sink) & 3u) return fail(VG_ERR_ALIGN, "sink is not 4-byte aligned");
+  vg::DeviceInfo dev;
+  if (vg_status s = device_info(&dev)) return s;
+  const hipError_t e = vg::launch_stream_read(buf, bytes, sink, dev, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return VG_OK;
+}
+
 vg_status vg_debug_unpack_sign1(const uint32_t* wbits, int N, int K, uint8_t* codes, void* stream) {
   if (N < 1 || K < 32 || K % 32 != 0) return fail(VG_ERR_SHAPE, "bad shape N=%d K=%d", N, K);
   if (vg_status s = check_ptr(wbits, "wbits")) return s;

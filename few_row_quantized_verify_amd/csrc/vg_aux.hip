@@ -304,6 +304,42 @@ hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32
 }
 
 // ---------------------------------------------------------------------------------------
+// Streaming read of a buffer, for the measurement's achievable-bandwidth reference: every
+// byte is read once with 16-byte non-temporal loads, four in flight per thread, and folded
+// into one word per workgroup so the loads cannot be elided.
+constexpr int STREAM_THREADS = 256;
+constexpr int STREAM_UNROLL = 4;
+__global__ __launch_bounds__(STREAM_THREADS) void vg_stream_read_kernel(const u32x4* buf, size_t n16, uint32_t* sink) {
+  __shared__ uint32_t part[STREAM_THREADS / 64];
+  const size_t stride = (size_t)gridDim.x * STREAM_THREADS;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * STREAM_THREADS + threadIdx.x;
+  for (; i + (STREAM_UNROLL - 1) * stride < n16; i += STREAM_UNROLL * stride) {
+    u32x4 v[STREAM_UNROLL];
+#pragma unroll
+    for (int u = 0; u < STREAM_UNROLL; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < STREAM_UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(buf + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+int stream_read_blocks(const DeviceInfo& dev) { return dev.cu_count * 8; }
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, const DeviceInfo& dev, hipStream_t s) {
+  hipLaunchKernelGGL(vg_stream_read_kernel, dim3(stream_read_blocks(dev)), dim3(STREAM_THREADS), 0, s,
+                     static_cast<const u32x4*>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 // Decode codes through the GEMM's register extraction: a register half holds
 // BETA + DELTA * code, so code = (half - BETA) / DELTA exactly.
 __global__ __launch_bounds__(256) void vg_debug_unpack_kernel(int fmt, const uint32_t* w, int N, int K, uint8_t* codes) {

@@ -72,6 +72,9 @@ hipError_t launch_hadamard(const void* x, int xt, int M, int K, int block, const
 int argmax_chunks(int N);
 hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
                          float* pval, int32_t* pidx, uint32_t* counters, hipStream_t s);
+// Streaming read of `bytes` (a multiple of 16) from buf; one word per workgroup to sink.
+int stream_read_blocks(const DeviceInfo& dev);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_debug_unpack(int fmt, const uint32_t* w, int N, int K, uint8_t* codes,
                                hipStream_t s);
 

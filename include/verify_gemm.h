@@ -39,6 +39,7 @@
 #ifndef VERIFY_GEMM_H
 #define VERIFY_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -218,6 +219,18 @@ int vg_plan_ksplit(int format, int x_dtype, int M, int N, int K);
  * the dispatch.  Values above K/1024 are capped.  VG_ERR_ARG outside 0..64.
  */
 vg_status vg_force_ksplit(int ksplit);
+
+/*
+ * Measurement aid: a plain streaming read of `bytes` (a positive multiple of 16) from the
+ * 16-byte aligned device buffer `buf`, every byte read once with 16-byte non-temporal
+ * loads.  Not part of the method: timed at the byte count of a verify call, it shows the
+ * bandwidth a kernel doing nothing but reading those bytes reaches on this device, the
+ * ceiling beside which the verify GEMM's fraction of the HBM peak is read.  Writes one word
+ * per workgroup to sink (uint32 [vg_stream_read_blocks()], device, 4-byte aligned).
+ * Validation as elsewhere: VG_ERR_ARG, VG_ERR_ALIGN, VG_ERR_SHAPE.
+ */
+int vg_stream_read_blocks(void);
+vg_status vg_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /*
  * Debug: decode the packed codes on the GPU into one byte per weight, codes[N, K] uint8

@@ -180,3 +180,13 @@ def test_experts_validation():
     assert call(fmt=B.FMT_AFFINE1, b=None) == B.VG_ERR_ARG
     assert call(y=A + 8) == B.VG_ERR_ALIGN
     assert call(x=None) == B.VG_ERR_ARG
+
+
+def test_stream_read_validation():
+    L = B.lib()
+    assert L.vg_stream_read(None, 1024, ALIGNED, None) == B.VG_ERR_ARG
+    assert L.vg_stream_read(ALIGNED + 4, 1024, ALIGNED, None) == B.VG_ERR_ALIGN
+    assert L.vg_stream_read(ALIGNED, 0, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.vg_stream_read(ALIGNED, 1000, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.vg_stream_read(ALIGNED, 1024, None, None) == B.VG_ERR_ARG
+    assert L.vg_stream_read(ALIGNED, 1024, ALIGNED + 2, None) == B.VG_ERR_ALIGN

@@ -440,3 +440,16 @@ def test_had2_blocks_and_signs(vg, block, K, N, x_dtype):
             torch.cuda.synchronize()
             check(case, M, y.cpu().numpy().astype(np.float64), had={"block": block, "signs": sg},
                   label=f"had{block}{'s' if sg is not None else ''}")
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 1 << 20, (1 << 24) + 48])
+def test_stream_read_reads_every_word(vg, nbytes):
+    """The measurement's streaming read touches every word once: the XOR of its per-
+    workgroup results equals the XOR of all words of the buffer."""
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = vg.stream_read(buf, nbytes)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
