@@ -46,6 +46,19 @@ __host__ __device__ constexpr float sign1_beta(int b0) {
 }
 constexpr float SIGN1_DELTA = 2.0f;
 
+// ---- 1-bit codes against bf16 activations: bf16 operand halves ------------------------
+// With bf16 activations the MFMA takes bf16 on both sides, so the codes decode to bf16
+// (7 stored mantissa bits).  Register b0 (0..15) holds the bits b0 and b0+16 of the word,
+// taken at position p = b0 & 7 of w (b0 < 8) or of w >> 8 (b0 >= 8).  Positions 0..6 are
+// mantissa bits (magic exponent 135-p, BETA = 2^(8-p)); position 7 is the exponent's
+// lowest bit (magic 2.0 -> 4.0).  DELTA = 2 again, and every BETA + 2 is a bf16 value.
+__host__ __device__ constexpr uint32_t bf16_magic_sign1(int p) {
+  return p == 7 ? 0x4000u : (uint32_t)(135 - p) << 7;
+}
+__host__ __device__ constexpr float sign1_beta_bf16(int b0) {
+  return (b0 & 7) == 7 ? 2.0f : (float)(1 << (8 - (b0 & 7)));
+}
+
 // ---- 2-bit affine format: 8 registers per 32-bit word ---------------------------------
 // Register j (0..7) holds codes j and j+8 (bits 2j.. and 2j+16..), taken at position p of
 // a shifted copy:  j 0,1 -> (w << 6) at p = 2j+6;  j 2..4 -> w at p = 2j;

@@ -36,6 +36,8 @@ namespace vg {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -74,6 +76,11 @@ __host__ __device__ constexpr int fmt_word_k(int fmt) { return fmt_one_bit(fmt) 
 __host__ __device__ constexpr int fmt_gps(int fmt) { return fmt_one_bit(fmt) ? 8 : 16; }   // groups per K-step
 __host__ __device__ constexpr int fmt_gl(int fmt) { return fmt_one_bit(fmt) ? 2 : 4; }     // Fmt<>::GL
 constexpr int KSTEP = 1024;   // K per unit, both formats
+// bf16 activations meet 1-bit codes in bf16 MFMAs (the codes decode to bf16 exactly);
+// against 2-bit codes, and for the rotated format, each activation row is rescaled by a
+// power of two into fp16 first.
+__host__ __device__ constexpr bool bf16_codes(int fmt, int xt) { return fmt_one_bit(fmt) && xt == XBF16; }
+__host__ __device__ constexpr bool x_rescaled(int fmt, int xt) { return fmt == HAD2 || (xt == XBF16 && !fmt_one_bit(fmt)); }
 
 struct MfmaArgs {
   const void* x;
@@ -85,8 +92,8 @@ struct MfmaArgs {
   int win_steps;   // K-steps (of KSTEP) per staging window
   int tiles_max;   // ytile capacity
   int a_pitch;     // LDS bytes per activation row in a window
-  uint32_t mask[6];   // code-extraction masks per bit position (see vg_device.h)
-  uint32_t magic[6];  // fp16 magic pairs per bit position
+  uint32_t mask[8];   // code-extraction masks per bit position (see vg_device.h)
+  uint32_t magic[8];  // magic pairs per bit position (fp16; bf16 for 1-bit codes with bf16 x)
   int rg, ks;         // row groups x K slices; workgroup b takes row group b / ks, slice b % ks
   int had_stages;     // rotated format: log2(block / 32) cross-lane butterfly stages
   float had_scale;    // 1 / sqrt(block)
@@ -219,11 +226,12 @@ __device__ __forceinline__ void load_x32_f32(const void* x, int K, int m, int k0
 // fp16, k_j = j-th K index of the window, i.e. exactly the pairing of unpacked code
 // registers (bits p and p+16).  An MFMA operand of 4 consecutive registers therefore maps
 // to 16 contiguous bytes.
-// Sums per (group, row), fp32, computed from the same fp16 operand values:
+// Sums per (group, row), fp32, computed from the same operand values:
 //   1-bit:  E = sum_k a_k * (BETA_k + 1)          (stored negated)
 //   2-bit:  R = sum_k a_k * BETA_k (stored negated),  X = sum_k a_k
 // The activations a are x * f (f a per-row power of two chosen so the fp16 values cannot
-// overflow; f = 1 for fp16 input without rotation), rotated first for the Hadamard format.
+// overflow; f = 1 for fp16 input without rotation and for bf16 input against 1-bit codes,
+// which stays bf16), rotated first for the Hadamard format.
 // The staging is split in two so the activation loads can be issued before a wave's
 // weight prefetch: loads enter the memory pipeline in order, and staged behind the weight
 // burst they would delay every workgroup's first MFMA by that whole burst.
@@ -283,7 +291,8 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
                               const XStage& xs) {
   using F = Fmt<FMT>;
   constexpr bool HAD = FMT == HAD2;
-  constexpr bool NORM = HAD || XT == XBF16;
+  constexpr bool NORM = x_rescaled(FMT, XT);
+  constexpr bool BF = bf16_codes(FMT, XT);
   const int tid = threadIdx.x;
   const int nchunks = WK / 32;
   const int ntask = M * nchunks;
@@ -349,10 +358,11 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
 #pragma unroll
       for (int e = 0; e < 32; ++e) hv[e] = f32_to_f16_bits(v[e] * scale);
     }
-    // Activations a (low half) and b (high half) of the chunk as an fp16 pair.  bf16 input:
-    // the power-of-two rescale maps it exactly into fp16 (8 significant bits fit in 11;
-    // only values over 2^27 times smaller than the row maximum reach the fp16
-    // subnormals), so converting a pair at once with truncation gives the same halves.
+    // Activations a (low half) and b (high half) of the chunk as an operand pair.  bf16
+    // input against 2-bit codes: the power-of-two rescale maps it exactly into fp16 (8
+    // significant bits fit in 11; only values over 2^27 times smaller than the row maximum
+    // reach the fp16 subnormals), so converting a pair at once with truncation gives the
+    // same halves.  Against 1-bit codes bf16 stays bf16 (the codes decode to bf16).
     auto pair = [&](int a, int b) -> uint32_t {
       if constexpr (HAD) {
         return hv[a] | (hv[b] << 16);
@@ -377,11 +387,20 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
 #pragma unroll
       for (int b0 = 0; b0 < 16; ++b0) {
         pd[b0] = pair(b0, b0 + 16);
-        const _Float16 cf = (_Float16)(sign1_beta(b0) + (FMT == SIGN1 ? 1.0f : 0.0f));
-        const f16x2 ph = __builtin_bit_cast(f16x2, pd[b0]);
-        e = __builtin_amdgcn_fdot2(ph, f16x2{cf, cf}, e, false);
-        if constexpr (F::AFFINE) xsum = __builtin_amdgcn_fdot2(ph, f16x2{(_Float16)1.0f, (_Float16)1.0f}, xsum, false);
+        if constexpr (BF) {
+          // BETA + 1 is no bf16 value beyond 128: sum a BETA and sum a apart
+          const bf16x2 ph = __builtin_bit_cast(bf16x2, pd[b0]);
+          const __bf16 cb = (__bf16)sign1_beta_bf16(b0), one = (__bf16)1.0f;
+          e = __builtin_amdgcn_fdot2_f32_bf16(ph, bf16x2{cb, cb}, e, false);
+          xsum = __builtin_amdgcn_fdot2_f32_bf16(ph, bf16x2{one, one}, xsum, false);
+        } else {
+          const _Float16 cf = (_Float16)(sign1_beta(b0) + (FMT == SIGN1 ? 1.0f : 0.0f));
+          const f16x2 ph = __builtin_bit_cast(f16x2, pd[b0]);
+          e = __builtin_amdgcn_fdot2(ph, f16x2{cf, cf}, e, false);
+          if constexpr (F::AFFINE) xsum = __builtin_amdgcn_fdot2(ph, f16x2{(_Float16)1.0f, (_Float16)1.0f}, xsum, false);
+        }
       }
+      if constexpr (BF && FMT == SIGN1) e += xsum;
       u32x4* dst = reinterpret_cast<u32x4*>(arow + (c >> 2) * F::GS + (c & 3) * F::WB);
 #pragma unroll
       for (int q = 0; q < 4; ++q) dst[q] = u32x4{pd[4 * q], pd[4 * q + 1], pd[4 * q + 2], pd[4 * q + 3]};
@@ -394,7 +413,19 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
       if ((c & 3) == 0) {
         const int grp = c >> 2;
         reinterpret_cast<float*>(smem + L.e_off)[grp * MAXM + m] = -e;
-        if constexpr (F::AFFINE) {
+        if constexpr (F::AFFINE && BF) {
+          // group sum / 128 as bf16 hi and lo parts (unscaled bf16 rows can exceed fp16's
+          // range): the quad of GL = 2 groups holds (hi, lo) twice, K slots
+          // [hi0 hi1 lo0 lo1 hi0 hi1 lo0 lo1] against biases [bh bh bl bl] (compute_unit)
+          const float xm = xsum * (1.0f / F::G);
+          const uint32_t hb = __float_as_uint(xm) >> 16;
+          const float lo = xm - __uint_as_float(hb << 16);   // exact
+          const uint16_t lb = __builtin_bit_cast(uint16_t, (__bf16)lo);
+          uint16_t* xp = reinterpret_cast<uint16_t*>(smem + L.xp_off + m * L.xp_pitch + (grp / F::GL) * 16);
+          const int h = grp % F::GL;
+          xp[h] = xp[4 + h] = (uint16_t)hb;
+          xp[2 + h] = xp[6 + h] = lb;
+        } else if constexpr (F::AFFINE) {
           // group sum / 128 as fp16 hi and lo parts; a quad holds GL = 2 groups, its unused
           // halves are cleared by the quad's first group
           const float xm = xsum * (1.0f / F::G);
@@ -460,9 +491,13 @@ __device__ __forceinline__ float half_of(uint32_t pair, int hi) {
 
 // Code extraction with the masks and magics held in registers (one v_and_or_b32 per
 // operand register; as literals the compiler would split it into an AND and an OR).
-template <int FMT>
+template <int FMT, bool BF>
 __device__ __forceinline__ void unpack_word_rt(uint32_t w, uint32_t* out, const uint32_t* mk, const uint32_t* mg) {
-  if constexpr (Fmt<FMT>::ONE_BIT) {
+  if constexpr (BF) {
+    const uint32_t src[2] = {w, w >> 8};
+#pragma unroll
+    for (int b0 = 0; b0 < 16; ++b0) out[b0] = (src[b0 >> 3] & mk[b0 & 7]) | mg[b0 & 7];
+  } else if constexpr (Fmt<FMT>::ONE_BIT) {
     const uint32_t src[3] = {w, w << 5, w >> 6};
 #pragma unroll
     for (int b0 = 0; b0 < 16; ++b0) {
@@ -497,7 +532,7 @@ __device__ __forceinline__ void read_a(const char* smem, uint32_t addr, f16x8* d
   for (int q = 0; q < Fmt<FMT>::NQ; ++q) dst[q] = *reinterpret_cast<const f16x8*>(smem + addr + 16 * q);
 }
 
-template <int FMT, int MODE>
+template <int FMT, int MODE, bool BF>
 __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* smem, uint32_t a_lane, uint32_t e_lane,
                                              uint32_t xp_lane, const uint32_t* mk, const uint32_t* mg,
                                              float yacc[4], f32x4& yb) {
@@ -574,14 +609,21 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
       }
     }
     uint32_t pa[F::PAIRS], pb[F::PAIRS];
-    unpack_word_rt<FMT>(wa[pi][w], pa, mk, mg);
-    unpack_word_rt<FMT>(wb[pi][w], pb, mk, mg);
+    unpack_word_rt<FMT, BF>(wa[pi][w], pa, mk, mg);
+    unpack_word_rt<FMT, BF>(wb[pi][w], pb, mk, mg);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const f16x8 ba = __builtin_bit_cast(f16x8, u32x4{pa[4 * q], pa[4 * q + 1], pa[4 * q + 2], pa[4 * q + 3]});
-      const f16x8 bb = __builtin_bit_cast(f16x8, u32x4{pb[4 * q], pb[4 * q + 1], pb[4 * q + 2], pb[4 * q + 3]});
-      acc_a = __builtin_amdgcn_mfma_f32_16x16x32_f16(abuf[st & 1][q], ba, acc_a, 0, 0, 0);
-      acc_b = __builtin_amdgcn_mfma_f32_16x16x32_f16(abuf[st & 1][NQ + q], bb, acc_b, 0, 0, 0);
+      const u32x4 ba = u32x4{pa[4 * q], pa[4 * q + 1], pa[4 * q + 2], pa[4 * q + 3]};
+      const u32x4 bb = u32x4{pb[4 * q], pb[4 * q + 1], pb[4 * q + 2], pb[4 * q + 3]};
+      if constexpr (BF) {
+        acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, abuf[st & 1][q]),
+                                                         __builtin_bit_cast(bf16x8, ba), acc_a, 0, 0, 0);
+        acc_b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, abuf[st & 1][NQ + q]),
+                                                         __builtin_bit_cast(bf16x8, bb), acc_b, 0, 0, 0);
+      } else {
+        acc_a = __builtin_amdgcn_mfma_f32_16x16x32_f16(abuf[st & 1][q], __builtin_bit_cast(f16x8, ba), acc_a, 0, 0, 0);
+        acc_b = __builtin_amdgcn_mfma_f32_16x16x32_f16(abuf[st & 1][NQ + q], __builtin_bit_cast(f16x8, bb), acc_b, 0, 0, 0);
+      }
     }
     if (w == WPP - 1) {
 #pragma unroll
@@ -592,10 +634,23 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
     // K slots: the lane-group's GL group sums as hi parts (halves 0..3), then lo parts
     // (halves 4..7); with GL = 2 the unused halves are zero on both sides
     const f16x8 xa = *reinterpret_cast<const f16x8*>(smem + xp_lane);
-    u32x4 bw;
-    if constexpr (GL == 4) bw = u32x4{U.b[0], U.b[1], U.b[0], U.b[1]};
-    else bw = u32x4{U.b[0], 0u, U.b[0], 0u};
-    yb = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, __builtin_bit_cast(f16x8, bw), yb, 0, 0, 0);
+    if constexpr (BF) {
+      // bf16 (X hi, X lo) against the two fp16 biases split exactly into bf16 hi + lo
+      // (11 significant bits = 8 + 3): every cross product of the parts is one K slot
+      static_assert(GL == 2, "bf16 bias quads hold two groups");
+      const float f0 = half_of(U.b[0], 0), f1 = half_of(U.b[0], 1);
+      const float l0 = f0 - __uint_as_float(__float_as_uint(f0) & 0xFFFF0000u);
+      const float l1 = f1 - __uint_as_float(__float_as_uint(f1) & 0xFFFF0000u);
+      const uint32_t dh = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+      const uint32_t dl = __builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u);
+      yb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                   __builtin_bit_cast(bf16x8, u32x4{dh, dh, dl, dl}), yb, 0, 0, 0);
+    } else {
+      u32x4 bw;
+      if constexpr (GL == 4) bw = u32x4{U.b[0], U.b[1], U.b[0], U.b[1]};
+      else bw = u32x4{U.b[0], 0u, U.b[0], 0u};
+      yb = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, __builtin_bit_cast(f16x8, bw), yb, 0, 0, 0);
+    }
   } else {
     (void)xp_lane;
     (void)yb;
@@ -707,7 +762,9 @@ template <int FMT, int MODE, int XT, int PREF>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, GPS = 4 * GL;
-  constexpr bool NORM = FMT == HAD2 || XT == XBF16;
+  constexpr bool NORM = x_rescaled(FMT, XT);
+  constexpr bool BF = bf16_codes(FMT, XT);
+  constexpr int NMK = BF ? 8 : 6;   // bit positions in use
   // The workgroup's job: row group and K slice of the call, or for a grouped expert verify
   // a row group of one job, whose rows are gathered from x and scattered to y.
   int M = A.M, rgi, ksi = 0, rg = A.rg;
@@ -740,9 +797,9 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   const uint32_t srow = (uint32_t)(A.K / F::G) * 2u;        // bytes of scales per row
   // masks stay in SGPRs, magics are moved into VGPRs once: v_and_or_b32 may read only one
   // scalar operand, and with both scalar the compiler would emit a separate AND and OR.
-  uint32_t mk[6], mg[6];
+  uint32_t mk[NMK], mg[NMK];
 #pragma unroll
-  for (int k = 0; k < 6; ++k) {
+  for (int k = 0; k < NMK; ++k) {
     mk[k] = A.mask[k];
     asm volatile("v_mov_b32 %0, %1" : "=v"(mg[k]) : "s"(A.magic[k]));
   }
@@ -869,7 +926,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
           const uint32_t a_lane = a_lane0 + (uint32_t)cs * (GPS * F::GS);
           const uint32_t e_lane = e_lane0 + (uint32_t)cs * (GPS * MAXM * 4);
           const uint32_t xp_lane = xp_lane0 + (uint32_t)cs * 64u;   // 4 quads of groups per unit
-          compute_unit<FMT, MODE>(ring[d], smem, a_lane, e_lane, xp_lane, mk, mg, yacc, yb);
+          compute_unit<FMT, MODE, BF>(ring[d], smem, a_lane, e_lane, xp_lane, mk, mg, yacc, yb);
           if (++cs == ns || base + d + 1 == nu) {
             const bool sole = ua <= ct * ns && ub >= (ct + 1) * ns;
             flush_tile<FMT, MODE>(smem, L, ct, sole, ws0 == kb0, ua >= ct * ns ? 0 : 1, wid, g, i, yacc, yb);
@@ -1103,8 +1160,13 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.had_stages = c.had_block == 64 ? 1 : (c.had_block == 256 ? 3 : 2);
   A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
   A.signs = c.signs;
-  for (int k = 0; k < 6; ++k) {
-    if (fmt_one_bit(FMT)) {
+  for (int k = 0; k < 8; ++k) {
+    if (bf16_codes(FMT, XT)) {
+      A.mask[k] = (1u << k) | (1u << (k + 16));   // positions 0..7
+      A.magic[k] = bf16_magic_sign1(k) | (bf16_magic_sign1(k) << 16);
+    } else if (k >= 6) {
+      A.mask[k] = A.magic[k] = 0u;
+    } else if (fmt_one_bit(FMT)) {
       const int q = 5 + k;   // positions 5..10
       A.mask[k] = (1u << q) | (1u << (q + 16));
       A.magic[k] = half_magic_sign1(q) | (half_magic_sign1(q) << 16);

@@ -25,6 +25,10 @@
  *     different workspaces.
  *   - Activations x are row-major [M, K] of dtype VG_F32, VG_F16 or VG_BF16 (raw IEEE bits);
  *     outputs y are row-major fp32 [M, N]; rows >= M are never read or written.
+ *     VG_BF16 activations against the 1-bit formats enter the matrix cores unscaled,
+ *     and their fp32 sums carry per-group offsets of up to 2^15 times an activation: such
+ *     activations must stay below 2^110 in magnitude (larger ones give non-finite
+ *     outputs).  Every other combination is bounded by fp32's range alone.
  *   - Packed weights, row-major over the N output rows, little-endian words, LSB first:
  *       1-bit sign:  wbits[N, K/32] uint32; weight k of a row is bit k%32 of word k/32;
  *                    bit 0 -> -scale, bit 1 -> +scale; one fp16 scale per 128 weights,

@@ -184,15 +184,20 @@ def test_output_rows_beyond_m_untouched(vg):
     assert torch.all(y[3:] == 7.25)
 
 
-def test_large_magnitude_bf16_rows(vg):
-    """bf16 rows far outside fp16 range are handled by per-row scaling."""
-    case = draw_case("sign1", 1024, 64, "bf16", seed=10)
+@pytest.mark.parametrize("fmt", ["sign1", "affine1", "affine2"])
+def test_large_magnitude_bf16_rows(vg, fmt):
+    """bf16 rows far outside fp16 range: 2-bit codes rescale each row into fp16, 1-bit
+    codes meet bf16 unscaled in bf16 MFMAs, documented up to |x| < 2^110 (row 2 sits just
+    below: N(0,1) draws times 2^106)."""
+    case = draw_case(fmt, 1024, 64, "bf16", seed=10)
     from synthetic import bf16_bits
     x64 = oracle.decode_bf16(case.x_all)
     x64[0] *= 2.0 ** 40
     x64[1] *= 2.0 ** -40
+    x64[2] *= 2.0 ** 106
+    x64[3] *= 2.0 ** -100
     case.x_all = bf16_bits(x64)
-    for M in (2, 8):
+    for M in (2, 4, 8):
         check(case, M, run(vg, case, M), label="bf16-range")
 
 
