@@ -157,7 +157,7 @@ hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev) {
 // GEMM prologue.
 template <int CTRL>
 __device__ __forceinline__ float dpp_quad_aux(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 __global__ __launch_bounds__(256) void vg_hadamard_kernel(const void* x, int xt, int M, int K, int block,

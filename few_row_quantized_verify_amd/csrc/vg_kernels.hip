@@ -145,10 +145,11 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float v) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);  // round to nearest even
 }
 // CTRL 0xB1: quad_perm [1,0,3,2] (partner lane ^1); 0x4E: quad_perm [2,3,0,1] (lane ^2).
+// Every lane of a quad permutation has a source, so no old value is kept (bound_ctrl):
+// the compiler can then fold the move into the arithmetic that consumes it as a DPP operand.
 template <int CTRL>
 __device__ __forceinline__ float dpp_quad(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // Lane l ^ 4 within groups of 32 lanes (ds_swizzle, bit-mask mode: and 0x1f, xor 4).
