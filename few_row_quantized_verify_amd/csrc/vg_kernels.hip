@@ -1005,8 +1005,19 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     const int m = e / nr, rr = e - m * nr;
     const float* src = A.part + (size_t)m * A.N + r0 + rr;
     float sum = 0.0f;
-    for (int k = 0; k < A.ks; ++k)
-      sum += __hip_atomic_load(src + (size_t)k * M * A.N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // up to 8 slices' loads in flight at once (each is a trip past the L2), added in slice
+    // order
+    for (int k0 = 0; k0 < A.ks; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[k] = k0 + k < A.ks ? __hip_atomic_load(src + (size_t)(k0 + k) * M * A.N, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k0 + k < A.ks) sum += v[k];
+    }
     A.y[(size_t)m * A.N + r0 + rr] = sum;
   }
   if (tid == 0) __hip_atomic_store(A.counters + rgi, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
