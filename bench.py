@@ -28,6 +28,9 @@ t(M=8)/t(M=1), a roofline object for the dominant kernel and the CPU oracle base
 Options:
   --workload NAME    another named workload (see synthetic.inputs.WORKLOADS)
   --m LIST           only these row counts, e.g. "8" (for profiling one kernel)
+  --warmup W         untimed warm-up steps before the timed ones (default 200: a few tens of
+                     ms of calls, which the GPU needs to reach steady clocks; measured on
+                     MI355X, the first ~10 ms of back-to-back calls run up to 10% slower)
   --trials T         split the timed steps into T trials (default 7); per-M figures are
                      the median over the trials (and the min)
   --force-variant V  run every call on kernel variant V (vg_mfma_q, vg_mfma_h, vg_valu)
@@ -371,7 +374,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--trials", type=int, default=7)
     ap.add_argument("--workload", default="mlp_up_affine2_k5120_n17408")
     ap.add_argument("--table", action="store_true")
