@@ -82,35 +82,6 @@ constexpr int KSTEP = 1024;   // K per unit, both formats
 __host__ __device__ constexpr bool bf16_codes(int fmt, int xt) { return fmt_one_bit(fmt) && xt == XBF16; }
 __host__ __device__ constexpr bool x_rescaled(int fmt, int xt) { return fmt == HAD2 || (xt == XBF16 && !fmt_one_bit(fmt)); }
 
-struct MfmaArgs {
-  const void* x;
-  const uint32_t* w;
-  const uint16_t* scales;
-  const uint16_t* biases;
-  float* y;
-  int M, K, N;
-  int win_steps;   // K-steps (of KSTEP) per staging window
-  int tiles_max;   // ytile capacity
-  int a_pitch;     // LDS bytes per activation row in a window
-  uint32_t mask[8];   // code-extraction masks per bit position (see vg_device.h)
-  uint32_t magic[8];  // magic pairs per bit position (fp16; bf16 for 1-bit codes with bf16 x)
-  int rg, ks;         // row groups x K slices; workgroup b takes row group b / ks, slice b % ks
-  int had_stages;     // rotated format: log2(block / 32) cross-lane butterfly stages
-  float had_scale;    // 1 / sqrt(block)
-  const uint32_t* signs;  // rotated format: optional sign bits [K/32] (bit set: negate x[:, k])
-  float* part;        // ks > 1: partial outputs [ks][M][N]
-  uint32_t* counters; // ks > 1: arrivals per row group (zero between calls)
-  // Grouped expert verify (route non-null, ks = 1): route [M, topk] names the expert of
-  // each (row, slot); values outside 0..E-1 mark unused slots.  Each workgroup groups the
-  // routing by expert into jobs of at most cap rows and takes one row group of one job
-  // (find_job); rg is then the fewest row groups per job the plan sized the LDS for.
-  // Expert e's codes start e * w_estride bytes into w, its scales and biases e * s_estride
-  // bytes into scales and biases; y is [M * topk, N].
-  const int32_t* route;
-  int topk, E, cap;
-  long long w_estride, s_estride;
-};
-
 // LDS carve-up (byte offsets), computed identically on host and device.
 //   a:  activation operand rows 0..M-1 of the window, then row M, all zeros (read by the
 //       lanes whose operand row carries no drafted row)
@@ -121,6 +92,7 @@ struct MfmaArgs {
 constexpr int JOB_BYTES = 128;
 struct LdsLayout {
   int a_off, e_off, xp_off, xp_pitch, ytile_off, slot_off, row_off, flag_off, red_off, total;
+  LdsLayout() = default;
   __host__ __device__ LdsLayout(int fmt, int M, int win_steps, int tiles_max) {
     const int groups = win_steps * fmt_gps(fmt);
     const int pitch = groups * fmt_gs(fmt) + 16;   // must equal MfmaArgs::a_pitch
@@ -135,6 +107,40 @@ struct LdsLayout {
     red_off = flag_off + 16;   // split tiles of the window, one word per wave boundary
     total = red_off + NW * 4;
   }
+};
+
+struct MfmaArgs {
+  const void* x;
+  const uint32_t* w;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  float* y;
+  int M, K, N;
+  int win_steps;   // K-steps (of KSTEP) per staging window
+  int tiles_max;   // ytile capacity
+  int a_pitch;     // LDS bytes per activation row in a window
+  uint32_t mask[8];   // code-extraction masks per bit position (see vg_device.h)
+  uint32_t magic[8];  // magic pairs per bit position (fp16; bf16 for 1-bit codes with bf16 x)
+  int rg, ks;         // row groups x K slices; workgroup b takes row group b / ks, slice b % ks
+  // Per-call constants the host works out once, so the workgroups' shared scalar unit does
+  // not (eight waves each running the same integer divisions cost about a microsecond):
+  int rq, rrem;        // N = rq * rg + rrem
+  uint32_t ks_magic;   // ks >= 2: ceil(2^32 / ks), n / ks = mulhi(n, ks_magic) for n * ks < 2^32
+  LdsLayout lay;       // the LDS carve-up at M (a grouped verify's jobs work out their own)
+  int had_stages;     // rotated format: log2(block / 32) cross-lane butterfly stages
+  float had_scale;    // 1 / sqrt(block)
+  const uint32_t* signs;  // rotated format: optional sign bits [K/32] (bit set: negate x[:, k])
+  float* part;        // ks > 1: partial outputs [ks][M][N]
+  uint32_t* counters; // ks > 1: arrivals per row group (zero between calls)
+  // Grouped expert verify (route non-null, ks = 1): route [M, topk] names the expert of
+  // each (row, slot); values outside 0..E-1 mark unused slots.  Each workgroup groups the
+  // routing by expert into jobs of at most cap rows and takes one row group of one job
+  // (find_job); rg is then the fewest row groups per job the plan sized the LDS for.
+  // Expert e's codes start e * w_estride bytes into w, its scales and biases e * s_estride
+  // bytes into scales and biases; y is [M * topk, N].
+  const int32_t* route;
+  int topk, E, cap;
+  long long w_estride, s_estride;
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -781,19 +787,21 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     sc = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(sc) + e * A.s_estride);
     if (bi) bi = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(bi) + e * A.s_estride);
   } else {
-    rgi = blockIdx.x / A.ks;
+    rgi = A.ks == 1 ? (int)blockIdx.x : (int)__umulhi(blockIdx.x, A.ks_magic);
     ksi = blockIdx.x - rgi * A.ks;
   }
-  const LdsLayout L(FMT, M, A.win_steps, A.tiles_max);
+  const LdsLayout L = A.route ? LdsLayout(FMT, M, A.win_steps, A.tiles_max) : A.lay;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
   // row group rgi: rows [r0, r1), the first N % rg groups one row longer
-  const int rq = A.N / rg, rrem = A.N - rq * rg;
+  const int rq = A.route ? A.N / rg : A.rq, rrem = A.route ? A.N - rq * rg : A.rrem;
   const int r0 = rgi * rq + min(rgi, rrem), r1 = r0 + rq + (rgi < rrem ? 1 : 0);
   const int T = (r1 - r0 + 15) / 16;
   const int S = A.K / KSTEP;
-  const int kb0 = (S * ksi) / A.ks, kb1 = (S * (ksi + 1)) / A.ks;   // this slice's K-steps
+  // this slice's K-steps, S * ksi / ks and S * (ksi + 1) / ks
+  const int kb0 = A.ks == 1 ? 0 : (int)__umulhi((uint32_t)(S * ksi), A.ks_magic);
+  const int kb1 = A.ks == 1 ? S : (int)__umulhi((uint32_t)(S * (ksi + 1)), A.ks_magic);
   const uint32_t wrow = (uint32_t)(A.K / F::WORD_K) * 4u;   // bytes of codes per row
   const uint32_t srow = (uint32_t)(A.K / F::G) * 2u;        // bytes of scales per row
   // masks stay in SGPRs, magics are moved into VGPRs once: v_and_or_b32 may read only one
@@ -1069,6 +1077,8 @@ static bool finish_plan(int fmt, int M, int K, int N, int rg, int ks, const Devi
   const int rows_max = (N + rg - 1) / rg + 1;
   p->tiles_max = (rows_max + 15) / 16 + 1;
   if (p->tiles_max > 32767) return false;   // the split-tile records hold 15-bit tile indices
+  // the kernels divide by ks with a multiply-high, exact for n * ks < 2^32 (n <= S * ks)
+  if ((uint64_t)(K / KSTEP) * (uint64_t)ks * (uint64_t)ks >= (1ull << 31)) return false;
   const int s_wg = (S + ks - 1) / ks;
   p->win_steps = window_steps(fmt, M, s_wg, p->tiles_max, dev.max_lds, &p->lds);
   // Units in flight per wave: one when each wave streams only a few units (the first
@@ -1161,6 +1171,10 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.a_pitch = p.win_steps * fmt_gps(FMT) * fmt_gs(FMT) + 16;
   A.rg = p.rg;
   A.ks = p.ks;
+  A.rq = c.N / p.rg;
+  A.rrem = c.N - A.rq * p.rg;
+  A.ks_magic = p.ks > 1 ? (uint32_t)(((1ull << 32) + (uint64_t)p.ks - 1) / (uint64_t)p.ks) : 0u;
+  A.lay = LdsLayout(FMT, c.M, p.win_steps, p.tiles_max);
   A.part = part;
   A.counters = counters;
   A.route = c.route;
