@@ -126,6 +126,7 @@ struct MfmaArgs {
   // not (eight waves each running the same integer divisions cost about a microsecond):
   int rq, rrem;        // N = rq * rg + rrem
   uint32_t ks_magic;   // ks >= 2: ceil(2^32 / ks), n / ks = mulhi(n, ks_magic) for n * ks < 2^32
+  uint32_t ws_magic;   // win_steps >= 2: the same for win_steps
   LdsLayout lay;       // the LDS carve-up at M (a grouped verify's jobs work out their own)
   int had_stages;     // rotated format: log2(block / 32) cross-lane butterfly stages
   float had_scale;    // 1 / sqrt(block)
@@ -850,7 +851,9 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     // Load cursor (tile lt, step ls), kept uniform; the lane part of a load address is a
     // per-tile constant, the rest is a scalar offset.  Each of the wave's units is loaded
     // once, PREF units ahead of the one computing.
-    int lt = nu > 0 ? ua / ns : 0, ls = nu > 0 ? ua - lt * ns : 0, issued = 0;
+    // ua / ns: a multiply-high for full windows (ua * ns < 2^27 here)
+    const int ua_t = ns == 1 ? ua : (ns == A.win_steps ? (int)__umulhi((uint32_t)ua, A.ws_magic) : ua / ns);
+    int lt = nu > 0 ? ua_t : 0, ls = nu > 0 ? ua - lt * ns : 0, issued = 0;
     uint32_t lw_lane = 0, ls_lane = 0;
     auto set_load_tile = [&](int t) {
       const int rr = min(16 * t + i, r1 - 1 - r0) - 16 * t;   // clamp rows past the range
@@ -894,7 +897,9 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     // and is that tile's first such boundary, the tile, the waves whose unit range meets
     // it (mask) and which of them started before it (their slot 1).  Bit 31 marks a
     // record.  Written after the barrier that ends the previous window's reduction, read
-    // after the one that follows the staging.
+    // after the one that follows the staging.  (Not the last wave: it carries the extra
+    // unit when the units do not divide evenly, and delaying its first load costs the
+    // whole call up to a microsecond, measured on MI355X.)
     if (wid == 0 && lane < NW - 1) {
       const int bw = lane + 1;
       const int B = (int)(((uint32_t)UW * bw) / NW);
@@ -925,7 +930,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     // priority on their SIMD shortens the window's slowest wave (measured on MI355X).
     if (nu > (int)((uint32_t)UW / NW)) __builtin_amdgcn_s_setprio(3);
     else __builtin_amdgcn_s_setprio(1);
-    int ct = nu > 0 ? ua / ns : 0, cs = nu > 0 ? ua - ct * ns : 0;
+    int ct = nu > 0 ? ua_t : 0, cs = nu > 0 ? ua - ct * ns : 0;
     float yacc[4] = {0.f, 0.f, 0.f, 0.f};
     f32x4 yb = {0.f, 0.f, 0.f, 0.f};
     for (int base = 0; base < nu; base += PREF) {
@@ -1174,6 +1179,7 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.rq = c.N / p.rg;
   A.rrem = c.N - A.rq * p.rg;
   A.ks_magic = p.ks > 1 ? (uint32_t)(((1ull << 32) + (uint64_t)p.ks - 1) / (uint64_t)p.ks) : 0u;
+  A.ws_magic = p.win_steps > 1 ? (uint32_t)(((1ull << 32) + (uint64_t)p.win_steps - 1) / (uint64_t)p.win_steps) : 0u;
   A.lay = LdsLayout(FMT, c.M, p.win_steps, p.tiles_max);
   A.part = part;
   A.counters = counters;
