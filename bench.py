@@ -12,8 +12,9 @@ host time of issuing a call through the Python binding.  Inputs are resident in 
 timing starts.  stream_ceiling times the library's plain streaming-read kernel over the
 same bytes and pool size the same way: the bandwidth reading those bytes can reach here.
 
-For the output-head workload a call is the verify GEMM followed by the argmax of every row
-(the head's argmax step), so its per-M times include both kernels.
+For the output-head workload a call is the verify GEMM with the argmax of every row (the
+head's argmax step) in one call, `verify_gemm_argmax`, whose argmax runs fused into the GEMM's
+epilogue on this shape; its per-M times include it.
 
 For a routed-expert workload (synthetic.inputs.EXPERT_WORKLOADS) a call is one grouped
 expert verify of M rows, each routed to topk of the E experts; the calls cycle through 64
@@ -442,9 +443,10 @@ def main() -> int:
 
         def call(M, j):
             w, s, b = pool[j % ncopy]
-            vg.verify_gemm(fmt, x_all[M], w, s, b, y=ys[M], stream=sh)
             if head:
-                vg.verify_argmax_rows(ys[M], idx=idx[M], stream=sh)
+                vg.verify_gemm_argmax(fmt, x_all[M], w, s, b, y=ys[M], idx=idx[M], stream=sh)
+            else:
+                vg.verify_gemm(fmt, x_all[M], w, s, b, y=ys[M], stream=sh)
 
         for M in Ms:
             for j in range(args.warmup):

@@ -43,6 +43,7 @@ _SIGS = {
     "hadamard_rotate": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "verify_argmax_rows": (_I, [_P, _I, _I, _P, _P]),
     "verify_accept_greedy": (_I, [_P, _I, _I, _P, _P, _P, _P]),
+    "verify_gemm_argmax": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "verify_gemm_experts": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P]),
     "vg_last_error": (ctypes.c_char_p, []),
     "vg_plan_variant": (_I, [_I, _I, _I, _I, _I]),
@@ -170,6 +171,28 @@ def verify_gemm(fmt: str, x, w, scales, biases=None, y=None, stream=None):
     if fmt == "affine1":
         return verify_gemm_affine1(x, w, scales, biases, y, stream)
     raise ValueError(fmt)
+
+
+def verify_gemm_argmax(fmt: str, x, w, scales, biases=None, y=None, idx=None, draft=None, accepted=None,
+                       stream=None):
+    """The verify GEMM and the argmax of every output row in one call (the argmax fused into
+    the GEMM where the plan allows).  Returns (y, idx), or (y, idx, accepted) when draft
+    (int32 [M] on the device) is given."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if idx is None:
+        idx = torch.empty((M,), dtype=torch.int32, device=x.device)
+    if draft is not None and accepted is None:
+        accepted = torch.empty((1,), dtype=torch.int32, device=x.device)
+    null = ctypes.c_void_p(0)
+    _check(lib().verify_gemm_argmax(FORMATS[fmt], _ptr(x), _xdtype(x), M, K, _ptr(w), _ptr(scales),
+                                    null if biases is None else _ptr(biases), N, _ptr(y), _ptr(idx),
+                                    null if draft is None else _ptr(draft),
+                                    null if accepted is None else _ptr(accepted), _stream(stream)))
+    return (y, idx) if draft is None else (y, idx, accepted)
 
 
 def verify_gemm_experts(fmt: str, x, route, w, scales, biases=None, y=None, stream=None):

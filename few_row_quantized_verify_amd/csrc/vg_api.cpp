@@ -116,7 +116,8 @@ struct Workspace {
 std::mutex g_ws_mu;
 Workspace g_ws[64];
 int g_ws_count = 0;
-constexpr size_t kCounterBytes = 4096;   // >= 4 bytes per row group (<= 1024 groups)
+constexpr size_t kCounterBytes = 8192;   // split-K counters (<= 768 row groups), the argmax
+                                         // kernel's counters, the fused argmax's keys
 
 vg_status workspace(int dev, hipStream_t stream, size_t part_bytes, float** part, uint32_t** counters) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
@@ -152,9 +153,24 @@ vg_status workspace(int dev, hipStream_t stream, size_t part_bytes, float** part
   return VG_OK;
 }
 
+vg_status run_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
+                     void* stream);
+
+// Fused argmax keys and arrival counter, in the workspace's counter area above the argmax
+// kernel's counters: one 128-byte line per row's key from byte 4096 (every workgroup
+// updates every row's key; keys sharing a line would serialize those updates), then the
+// counter's line.
+constexpr int kFusedKeyBase = 1024;                                  // u32 index
+constexpr int kFusedKeyStride = 16;                                  // u64 elements (128 B)
+constexpr int kFusedCountIndex = kFusedKeyBase + 32 * VG_MAX_ROWS;   // u32 index
+
+// The verify GEMM; with idx non-null also the argmax of every row (and the accepted prefix
+// when draft is non-null): fused into the GEMM's epilogue when the plan runs the MFMA
+// kernels with one K slice, else the argmax kernel after it (same results either way).
 vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint32_t* w,
                    const uint16_t* scales, const uint16_t* biases, int N, float* y, void* stream,
-                   int had_block = 128, const uint32_t* signs = nullptr) {
+                   int had_block = 128, const uint32_t* signs = nullptr, int32_t* idx = nullptr,
+                   const int32_t* draft = nullptr, int32_t* accepted = nullptr) {
   std::call_once(g_env_once, read_env);
   vg::DeviceInfo dev;
   if (vg_status s = device_info(&dev)) return s;
@@ -168,6 +184,7 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, static_cast<hipStream_t>(stream),
                  had_block, signs};
   hipError_t e;
+  bool fused = false;
   if (var == vg::VAR_VALU) {
     e = vg::launch_valu(c, dev);
   } else {
@@ -179,10 +196,21 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
     if (p.ks > 1) {
       if (p.rg > 768) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
       if (vg_status s = workspace(dev.id, c.stream, vg::mfma_workspace_bytes(M, N, p), &part, &counters)) return s;
+    } else if (idx) {
+      if (vg_status s = workspace(dev.id, c.stream, 0, &part, &counters)) return s;
+      part = nullptr;
+      c.idx = idx;
+      c.draft = draft;
+      c.accepted = accepted;
+      c.amax_key = reinterpret_cast<unsigned long long*>(counters + kFusedKeyBase);
+      c.amax_count = counters + kFusedCountIndex;
+      counters = nullptr;
+      fused = true;
     }
     e = vg::launch_mfma(c, var, p, part, counters, dev);
   }
   if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  if (idx && !fused) return run_argmax(y, M, N, idx, draft, accepted, stream);
   g_err[0] = '\0';
   return VG_OK;
 }
@@ -335,6 +363,26 @@ vg_status hadamard_rotate_signed(const void* x, int x_dtype, int M, int K, int b
 vg_status hadamard_rotate(const void* x, int x_dtype, int M, int K, int block, float* x_out,
                           void* stream) {
   return hadamard_rotate_signed(x, x_dtype, M, K, block, nullptr, x_out, stream);
+}
+
+vg_status verify_gemm_argmax(int format, const void* x, int x_dtype, int M, int K, const uint32_t* w,
+                             const uint16_t* scales, const uint16_t* biases, int N, float* y, int32_t* idx,
+                             const int32_t* draft, int32_t* accepted, void* stream) {
+  if (format != vg::SIGN1 && format != vg::AFFINE2 && format != vg::HAD2 && format != vg::AFFINE1)
+    return fail(VG_ERR_ARG, "unknown format %d", format);
+  if (vg_status s = check_common(x, x_dtype, M, K, N)) return s;
+  const int G = vg::fmt_one_bit(format) || format == vg::HAD2 ? 128 : 64;
+  if (K % G != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of %d", K, G);
+  if (vg_status s = check_ptr(w, "w")) return s;
+  if (vg_status s = check_ptr(scales, "scales")) return s;
+  if (format != vg::SIGN1)
+    if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_ptr(y, "y")) return s;
+  if (!idx) return fail(VG_ERR_ARG, "idx is null");
+  if (reinterpret_cast<uintptr_t>(idx) & 3u) return fail(VG_ERR_ALIGN, "idx is not 4-byte aligned");
+  if ((draft == nullptr) != (accepted == nullptr)) return fail(VG_ERR_ARG, "draft and accepted go together");
+  return run_gemm(format, x, x_dtype, M, K, w, scales, format == vg::SIGN1 ? nullptr : biases, N, y, stream, 128,
+                  nullptr, idx, draft, accepted);
 }
 
 vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* stream) {

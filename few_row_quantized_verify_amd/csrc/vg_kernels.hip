@@ -142,6 +142,15 @@ struct MfmaArgs {
   const int32_t* route;
   int topk, E, cap;
   long long w_estride, s_estride;
+  // Fused argmax (plain calls with ks = 1; idx null otherwise): idx [M] gets each row's
+  // argmax over the N columns, and with draft non-null accepted[0] the number of leading
+  // rows whose argmax equals draft[m].  amax_key (row m's key at amax_key[16 m], one
+  // 128-byte line per row) and amax_count are zero between calls.
+  int32_t* idx;
+  const int32_t* draft;
+  int32_t* accepted;
+  unsigned long long* amax_key;
+  uint32_t* amax_count;
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -766,6 +775,61 @@ __device__ bool find_job(const MfmaArgs& A, char* smem, int& M, int& expert, int
   return true;
 }
 
+// Fused argmax of the output head (the head's verify is checked by its argmax): wave m
+// takes row m of the workgroup's columns and folds each (value, column) into one 64-bit key
+// that orders like (value, -column): larger value first, then the lower column, and NaN
+// never enters.  The keys meet in one per-row maximum across workgroups; the last
+// workgroup to arrive turns them into indices (0 for a row with no key), counts the
+// accepted prefix when a draft is given, and leaves keys and counter zero for the next
+// call.  The keys and the counter are agent-scope atomics, as in the split-K reduction.
+constexpr int AMAX_STRIDE = 16;   // u64 elements between rows' keys: a 128-byte line each
+__device__ __forceinline__ unsigned long long arg_key(float v, int n) {
+  const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);   // -0 ties with +0
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // orders like v
+  return ((unsigned long long)o << 32) | (uint32_t)~(uint32_t)n;
+}
+
+__device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, const float* ytile, int M, int r0,
+                             int nr, int wid, int lane) {
+  if (wid < M) {
+    unsigned long long best = 0ull;
+    for (int rr = lane; rr < nr; rr += 64) {
+      const float v = ytile[(rr >> 4) * (MAXM * 16) + wid * 16 + (rr & 15)];
+      if (v == v) {
+        const unsigned long long k = arg_key(v, r0 + rr);
+        best = k > best ? k : best;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const unsigned long long o = __shfl_xor(best, off);
+      best = o > best ? o : best;
+    }
+    if (lane == 0 && best != 0ull)
+      __hip_atomic_fetch_max(A.amax_key + wid * AMAX_STRIDE, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's key has landed
+  lds_barrier();
+  uint32_t* flag = reinterpret_cast<uint32_t*>(smem + L.flag_off);
+  if (threadIdx.x == 0)
+    flag[0] = __hip_atomic_fetch_add(A.amax_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              gridDim.x - 1u ? 1u : 0u;
+  lds_barrier();
+  if (flag[0] == 0u || threadIdx.x != 0) return;
+  int agreed = 0;
+  bool agree = A.draft != nullptr;
+  for (int m = 0; m < M; ++m) {
+    const unsigned long long k = __hip_atomic_load(A.amax_key + m * AMAX_STRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int id = k == 0ull ? 0 : (int)~(uint32_t)k;
+    A.idx[m] = id;
+    __hip_atomic_store(A.amax_key + m * AMAX_STRIDE, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (agree && id == A.draft[m]) ++agreed;
+    else agree = false;
+  }
+  if (A.accepted) A.accepted[0] = agreed;
+  __hip_atomic_store(A.amax_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int FMT, int MODE, int XT, int PREF>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
@@ -992,6 +1056,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       const int m = e / nr, rr = e - m * nr;
       A.y[(size_t)(xmap ? xmap[MAXM + m] : m) * A.N + r0 + rr] = ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)];
     }
+    if (A.idx) fused_argmax(A, smem, L, ytile, M, r0, nr, wid, lane);
     return;
   }
   // K split across workgroups: park this slice's partial, and let the last slice of the row
@@ -1189,6 +1254,11 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.cap = c.cap;
   A.w_estride = c.w_estride;
   A.s_estride = c.s_estride;
+  A.idx = c.idx;
+  A.draft = c.draft;
+  A.accepted = c.accepted;
+  A.amax_key = c.amax_key;
+  A.amax_count = c.amax_count;
   A.had_stages = c.had_block == 64 ? 1 : (c.had_block == 256 ? 3 : 2);
   A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
   A.signs = c.signs;

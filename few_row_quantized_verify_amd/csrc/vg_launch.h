@@ -31,6 +31,14 @@ struct GemmCall {
   const int32_t* route;
   int topk, E, cap;
   long long w_estride, s_estride;
+  // fused argmax of every row (MFMA variants with one K slice): idx [M], and with draft
+  // non-null the accepted prefix length; the per-row keys and the arrival counter sit in
+  // the library's per-stream workspace and are zero between calls
+  int32_t* idx = nullptr;
+  const int32_t* draft = nullptr;
+  int32_t* accepted = nullptr;
+  unsigned long long* amax_key = nullptr;
+  uint32_t* amax_count = nullptr;
 };
 
 struct DeviceInfo {

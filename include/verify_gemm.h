@@ -154,6 +154,30 @@ vg_status hadamard_rotate_signed(const void* x, int x_dtype, int M, int K, int b
 vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* stream);
 
 /*
+ * The verify GEMM of one format followed by the argmax of every output row, as one call:
+ * y as verify_gemm_<format> computes it, idx[m] = argmax_n y[m, n] as verify_argmax_rows
+ * computes it, and with draft non-null accepted[0] as verify_accept_greedy computes it (the
+ * output head's verify is checked by its argmax: "dflash-mlx-bonsai2" README, "Verify it
+ * yourself").  When the dispatch runs the MFMA kernels with K in one slice (the output-head
+ * shapes), the argmax is fused into the GEMM's epilogue: each workgroup folds its columns'
+ * best (value, column) per row into a per-row 64-bit maximum and the last workgroup to
+ * finish writes idx, so the logits are not read back and no second kernel runs.  Otherwise
+ * the argmax kernel runs after the GEMM on the same stream.  Results are identical either
+ * way (the argmax rule is order-independent).
+ *   format  VG_FMT_SIGN1, VG_FMT_AFFINE2, VG_FMT_HAD2 (block 128, unsigned) or
+ *           VG_FMT_AFFINE1; w, scales, biases as in that format's call (biases unused and
+ *           may be NULL for VG_FMT_SIGN1).
+ *   y       fp32 [M, N], written as by the plain call.
+ *   idx     int32 [M] on the device (4-byte aligned).
+ *   draft, accepted  both NULL, or int32 [M] and int32 [1] on the device.
+ * Requirements and errors as the format's call, plus idx non-null.  Uses the per-stream
+ * workspace described above (allocated on the first call on a stream that needs it).
+ */
+vg_status verify_gemm_argmax(int format, const void* x, int x_dtype, int M, int K, const uint32_t* w,
+                             const uint16_t* scales, const uint16_t* biases, int N, float* y, int32_t* idx,
+                             const int32_t* draft, int32_t* accepted, void* stream);
+
+/*
  * Greedy acceptance of a drafted block: idx[m] = argmax_n y[m, n] as verify_argmax_rows,
  * and accepted[0] = the number of leading rows m with idx[m] == draft[m] (0..M), i.e. the
  * length of the drafted prefix the target model agrees with; when it is below M,

@@ -24,7 +24,8 @@ def test_header_declares_the_boundary():
                "verify_argmax_rows", "vg_last_error", "vg_plan_variant", "vg_variant_name",
                "vg_force_variant", "vg_variant_count", "vg_debug_unpack_sign1", "vg_debug_unpack_affine2",
                "vg_plan_ksplit", "vg_force_ksplit", "verify_accept_greedy", "verify_gemm_affine1",
-               "verify_gemm_had2_signed", "hadamard_rotate_signed", "verify_gemm_experts"):
+               "verify_gemm_had2_signed", "hadamard_rotate_signed", "verify_gemm_experts",
+               "verify_gemm_argmax"):
         assert fn in names, fn
 
 
@@ -142,6 +143,29 @@ def test_accept_greedy_validation():
     assert L.verify_accept_greedy(ALIGNED, 2, 100, ALIGNED, ALIGNED, None, None) == B.VG_ERR_ARG
     assert L.verify_accept_greedy(ALIGNED, 9, 100, ALIGNED, ALIGNED, ALIGNED, None) == B.VG_ERR_SHAPE
     assert L.verify_accept_greedy(ALIGNED + 2, 2, 100, ALIGNED, ALIGNED, ALIGNED, None) == B.VG_ERR_ALIGN
+
+
+def test_gemm_argmax_validation():
+    """Every argument check of the fused GEMM + argmax call runs on the host, before any
+    device work."""
+    L = B.lib()
+    A, F16 = ALIGNED, B.VG_F16
+
+    def call(fmt=1, x=A, xt=F16, M=2, K=1024, w=A, s=A, b=A, N=64, y=A, idx=A, d=None, acc=None):
+        return L.verify_gemm_argmax(fmt, x, xt, M, K, w, s, b, N, y, idx, d, acc, None)
+
+    assert call(fmt=7) == B.VG_ERR_ARG
+    assert call(idx=None) == B.VG_ERR_ARG
+    assert call(idx=A + 2) == B.VG_ERR_ALIGN
+    assert call(d=A) == B.VG_ERR_ARG
+    assert call(acc=A) == B.VG_ERR_ARG
+    assert call(M=9) == B.VG_ERR_SHAPE
+    assert call(M=0) == B.VG_ERR_SHAPE
+    assert call(fmt=0, K=1088) == B.VG_ERR_SHAPE      # 1-bit groups of 128
+    assert call(fmt=2, K=1088) == B.VG_ERR_SHAPE      # rotated blocks of 128
+    assert call(b=None) == B.VG_ERR_ARG               # 2-bit affine needs biases
+    assert call(xt=5) == B.VG_ERR_DTYPE
+    assert call(y=None) == B.VG_ERR_ARG
 
 
 def test_hadamard_block_must_divide_k_and_signs_aligned():
