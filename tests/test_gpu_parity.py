@@ -116,8 +116,11 @@ def test_small_all_rows(vg, fmt, K, N, x_dtype):
 
 @pytest.mark.parametrize("fmt,K", [("sign1", 1024), ("affine2", 1024), ("had2", 1024), ("affine1", 1024)])
 @pytest.mark.parametrize("N", [1, 17, 33, 257])
-def test_ragged_n(vg, fmt, K, N):
-    case = draw_case(fmt, K, N, "f16", seed=2)
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+def test_ragged_n(vg, fmt, K, N, x_dtype):
+    """bf16 takes a path of its own: bf16 MFMAs for the 1-bit formats, per-row rescaling
+    into fp16 for the 2-bit ones."""
+    case = draw_case(fmt, K, N, x_dtype, seed=2)
     for M in (1, 4, 5, 8):
         check(case, M, run(vg, case, M), label="ragged")
 
