@@ -157,11 +157,10 @@ vg_status run_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* 
                      void* stream);
 
 // Fused argmax keys and arrival counter, in the workspace's counter area above the argmax
-// kernel's counters: one 128-byte line per row's key from byte 4096 (every workgroup
-// updates every row's key; keys sharing a line would serialize those updates), then the
-// counter's line.
-constexpr int kFusedKeyBase = 1024;                                  // u32 index
-constexpr int kFusedKeyStride = 16;                                  // u64 elements (128 B)
+// kernel's counters (u32 768 .. 1056: nine counters, one 128-byte line each): one 128-byte
+// line per row's key (every workgroup updates every row's key; keys sharing a line would
+// serialize those updates), then the counter's line.
+constexpr int kFusedKeyBase = 1088;                                  // u32 index (8-byte aligned)
 constexpr int kFusedCountIndex = kFusedKeyBase + 32 * VG_MAX_ROWS;   // u32 index
 
 // The verify GEMM; with idx non-null also the argmax of every row (and the accepted prefix
@@ -261,7 +260,8 @@ vg_status run_experts(int fmt, const void* x, int x_dtype, int M, int K, int E, 
   return VG_OK;
 }
 
-// Counters of the argmax kernel sit above those of the K-split reductions in the workspace.
+// Counters of the argmax kernel sit above those of the K-split reductions in the workspace
+// (nine of them, 128 bytes apart: u32 768 .. 1056).
 constexpr int kArgmaxCounterBase = 768;
 
 vg_status run_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,

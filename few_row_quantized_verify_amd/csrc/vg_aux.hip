@@ -10,7 +10,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int VALU_THREADS = 256;
 constexpr int VALU_WK = 2048;   // K per LDS window (fp32 activations, 8 rows: 64 KB)
 constexpr int MAXM = 8;
-constexpr int VG_MAX_ROWS_DEV = 8;   // counters[0..7]: rows; counters[8]: finished rows
+constexpr int VG_MAX_ROWS_DEV = 8;   // counter m (row m, m < 8) and counter 8 (finished rows)
+// Each counter has its own 128-byte line: all of a row's chunks update it, and counters
+// sharing a line would serialize every row's updates behind each other.
+constexpr int ARG_CTR_STRIDE = 32;   // u32 elements
 
 __device__ __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 __device__ __forceinline__ float x_at(const void* x, int xt, size_t idx) {
@@ -266,7 +269,8 @@ __global__ __launch_bounds__(ARG_THREADS) void vg_argmax_kernel(const float* y, 
     __hip_atomic_store(pval + m * C + c, sv[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(pidx + m * C + c, si[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial has landed
-    last = __hip_atomic_fetch_add(counters + m, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(C - 1);
+    last = __hip_atomic_fetch_add(counters + m * ARG_CTR_STRIDE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)(C - 1);
   }
   __syncthreads();
   if (!last) return;
@@ -282,16 +286,17 @@ __global__ __launch_bounds__(ARG_THREADS) void vg_argmax_kernel(const float* y, 
   if (threadIdx.x != 0) return;
   const int32_t am = si[0] < 0 ? 0 : si[0];
   __hip_atomic_store(idx + m, am, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(counters + m, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(counters + m * ARG_CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (draft == nullptr) return;
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  if (__hip_atomic_fetch_add(counters + VG_MAX_ROWS_DEV, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)(M - 1))
+  if (__hip_atomic_fetch_add(counters + VG_MAX_ROWS_DEV * ARG_CTR_STRIDE, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) != (uint32_t)(M - 1))
     return;
   // last row to finish: the drafted prefix the target agrees with
   int L = 0;
   while (L < M && __hip_atomic_load(idx + L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == draft[L]) ++L;
   accepted[0] = L;
-  __hip_atomic_store(counters + VG_MAX_ROWS_DEV, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(counters + VG_MAX_ROWS_DEV * ARG_CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 int argmax_chunks(int N) { return (N + ARG_CHUNK - 1) / ARG_CHUNK; }
