@@ -116,8 +116,16 @@ struct Workspace {
 std::mutex g_ws_mu;
 Workspace g_ws[64];
 int g_ws_count = 0;
-constexpr size_t kCounterBytes = 8192;   // split-K counters (<= 768 row groups), the argmax
-                                         // kernel's counters, the fused argmax's keys
+// Counter area (zeroed at allocation, left zero by every call), u32 indices, each counter and
+// key on its own 128-byte line:
+//   [0, 24576)       split-K arrival counters, row group r at r * 32 (r < 768)
+//   [24576, 24864)   the argmax kernel's nine counters (rows 0..7, finished rows)
+//   [24864, 25120)   the fused argmax's per-row 64-bit keys, then its arrival counter
+constexpr int kArgmaxCounterBase = vg::MAX_SPLIT_ROW_GROUPS * vg::SPLIT_CTR_STRIDE;
+constexpr int kFusedKeyBase = kArgmaxCounterBase + 32 * (VG_MAX_ROWS + 1);   // 8-byte aligned
+constexpr int kFusedCountIndex = kFusedKeyBase + 32 * VG_MAX_ROWS;
+constexpr size_t kCounterBytes = 102400;
+static_assert((kFusedCountIndex + 32) * 4 <= (int)kCounterBytes, "counter area too small");
 
 vg_status workspace(int dev, hipStream_t stream, size_t part_bytes, float** part, uint32_t** counters) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
@@ -156,12 +164,6 @@ vg_status workspace(int dev, hipStream_t stream, size_t part_bytes, float** part
 vg_status run_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
                      void* stream);
 
-// Fused argmax keys and arrival counter, in the workspace's counter area above the argmax
-// kernel's counters (u32 768 .. 1056: nine counters, one 128-byte line each): one 128-byte
-// line per row's key (every workgroup updates every row's key; keys sharing a line would
-// serialize those updates), then the counter's line.
-constexpr int kFusedKeyBase = 1088;                                  // u32 index (8-byte aligned)
-constexpr int kFusedCountIndex = kFusedKeyBase + 32 * VG_MAX_ROWS;   // u32 index
 
 // The verify GEMM; with idx non-null also the argmax of every row (and the accepted prefix
 // when draft is non-null): fused into the GEMM's epilogue when the plan runs the MFMA
@@ -193,7 +195,7 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
     float* part = nullptr;
     uint32_t* counters = nullptr;
     if (p.ks > 1) {
-      if (p.rg > 768) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
+      if (p.rg > vg::MAX_SPLIT_ROW_GROUPS) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
       if (vg_status s = workspace(dev.id, c.stream, vg::mfma_workspace_bytes(M, N, p), &part, &counters)) return s;
     } else if (idx) {
       if (vg_status s = workspace(dev.id, c.stream, 0, &part, &counters)) return s;
@@ -260,9 +262,6 @@ vg_status run_experts(int fmt, const void* x, int x_dtype, int M, int K, int E, 
   return VG_OK;
 }
 
-// Counters of the argmax kernel sit above those of the K-split reductions in the workspace
-// (nine of them, 128 bytes apart: u32 768 .. 1056).
-constexpr int kArgmaxCounterBase = 768;
 
 vg_status run_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
                      void* stream) {

@@ -132,7 +132,8 @@ struct MfmaArgs {
   float had_scale;    // 1 / sqrt(block)
   const uint32_t* signs;  // rotated format: optional sign bits [K/32] (bit set: negate x[:, k])
   float* part;        // ks > 1: partial outputs [ks][M][N]
-  uint32_t* counters; // ks > 1: arrivals per row group (zero between calls)
+  uint32_t* counters; // ks > 1: arrivals per row group (zero between calls), row group r's at
+                      // counters[r * SPLIT_CTR_STRIDE]
   // Grouped expert verify (route non-null, ks = 1): route [M, topk] names the expert of
   // each (row, slot); values outside 0..E-1 mark unused slots.  Each workgroup groups the
   // routing by expert into jobs of at most cap rows and takes one row group of one job
@@ -1074,7 +1075,8 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   lds_barrier();
   uint32_t* flag = reinterpret_cast<uint32_t*>(smem + L.flag_off);
   if (tid == 0) {
-    const uint32_t before = __hip_atomic_fetch_add(A.counters + rgi, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t before = __hip_atomic_fetch_add(A.counters + rgi * SPLIT_CTR_STRIDE, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
     flag[0] = before == (uint32_t)(A.ks - 1) ? 1u : 0u;
   }
   lds_barrier();
@@ -1098,7 +1100,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     }
     A.y[(size_t)m * A.N + r0 + rr] = sum;
   }
-  if (tid == 0) __hip_atomic_store(A.counters + rgi, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(A.counters + rgi * SPLIT_CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The kernel names carry the variant name, so a trace shows which variant ran.

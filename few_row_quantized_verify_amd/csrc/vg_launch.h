@@ -14,6 +14,11 @@ enum Variant : int {
   VAR_COUNT = 3
 };
 
+// Split-K arrival counters in the workspace: one per row group (at most 768), each on its
+// own 128-byte line (a line's atomics serialize, and the row groups finish together).
+constexpr int SPLIT_CTR_STRIDE = 32;   // u32 elements
+constexpr int MAX_SPLIT_ROW_GROUPS = 768;
+
 struct GemmCall {
   int fmt;            // Format
   int xt;             // 0 f32, 1 f16, 2 bf16
