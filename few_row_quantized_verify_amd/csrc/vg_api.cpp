@@ -120,11 +120,12 @@ int g_ws_count = 0;
 // key on its own 128-byte line:
 //   [0, 24576)       split-K arrival counters, row group r at r * 32 (r < 768)
 //   [24576, 24864)   the argmax kernel's nine counters (rows 0..7, finished rows)
-//   [24864, 25120)   the fused argmax's per-row 64-bit keys, then its arrival counter
+//   [24864, 28960)   the fused argmax's 64-bit keys, 16 slots per row
+//   [28960, 28992)   the fused argmax's arrival counter
 constexpr int kArgmaxCounterBase = vg::MAX_SPLIT_ROW_GROUPS * vg::SPLIT_CTR_STRIDE;
 constexpr int kFusedKeyBase = kArgmaxCounterBase + 32 * (VG_MAX_ROWS + 1);   // 8-byte aligned
-constexpr int kFusedCountIndex = kFusedKeyBase + 32 * VG_MAX_ROWS;
-constexpr size_t kCounterBytes = 102400;
+constexpr int kFusedCountIndex = kFusedKeyBase + 32 * 16 * VG_MAX_ROWS;
+constexpr size_t kCounterBytes = 116736;
 static_assert((kFusedCountIndex + 32) * 4 <= (int)kCounterBytes, "counter area too small");
 
 vg_status workspace(int dev, hipStream_t stream, size_t part_bytes, float** part, uint32_t** counters) {

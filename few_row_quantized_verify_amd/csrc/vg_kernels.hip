@@ -145,8 +145,8 @@ struct MfmaArgs {
   long long w_estride, s_estride;
   // Fused argmax (plain calls with ks = 1; idx null otherwise): idx [M] gets each row's
   // argmax over the N columns, and with draft non-null accepted[0] the number of leading
-  // rows whose argmax equals draft[m].  amax_key (row m's key at amax_key[16 m], one
-  // 128-byte line per row) and amax_count are zero between calls.
+  // rows whose argmax equals draft[m].  amax_key (row m's slot s at amax_key[16 (16 m + s)],
+  // a 128-byte line each) and amax_count are zero between calls.
   int32_t* idx;
   const int32_t* draft;
   int32_t* accepted;
@@ -783,7 +783,8 @@ __device__ bool find_job(const MfmaArgs& A, char* smem, int& M, int& expert, int
 // workgroup to arrive turns them into indices (0 for a row with no key), counts the
 // accepted prefix when a draft is given, and leaves keys and counter zero for the next
 // call.  The keys and the counter are agent-scope atomics, as in the split-K reduction.
-constexpr int AMAX_STRIDE = 16;   // u64 elements between rows' keys: a 128-byte line each
+constexpr int AMAX_STRIDE = 16;   // u64 elements between keys: a 128-byte line each
+constexpr int AMAX_SLOTS = 16;    // key slots per row
 __device__ __forceinline__ unsigned long long arg_key(float v, int n) {
   const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);   // -0 ties with +0
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // orders like v
@@ -792,6 +793,10 @@ __device__ __forceinline__ unsigned long long arg_key(float v, int n) {
 
 __device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, const float* ytile, int M, int r0,
                              int nr, int wid, int lane) {
+  // Workgroup b updates slot b % AMAX_SLOTS of each row's key, so no key line takes more
+  // than 1 / AMAX_SLOTS of the workgroups' maxima (a line's atomics serialize); the last
+  // workgroup to arrive reads every slot.
+  const uint32_t slot = blockIdx.x % AMAX_SLOTS;
   if (wid < M) {
     unsigned long long best = 0ull;
     for (int rr = lane; rr < nr; rr += 64) {
@@ -807,7 +812,8 @@ __device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, 
       best = o > best ? o : best;
     }
     if (lane == 0 && best != 0ull)
-      __hip_atomic_fetch_max(A.amax_key + wid * AMAX_STRIDE, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_max(A.amax_key + (wid * AMAX_SLOTS + slot) * AMAX_STRIDE, best, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's key has landed
   lds_barrier();
@@ -816,19 +822,35 @@ __device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, 
     flag[0] = __hip_atomic_fetch_add(A.amax_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               gridDim.x - 1u ? 1u : 0u;
   lds_barrier();
-  if (flag[0] == 0u || threadIdx.x != 0) return;
+  if (flag[0] == 0u) return;
+  // the last workgroup: row m's winner over the slots (lane s of wave m reads slot s), then
+  // the keys and the counter cleared for the next call
+  if (wid < M) {
+    unsigned long long k = 0ull;
+    if (lane < AMAX_SLOTS) {
+      unsigned long long* kp = A.amax_key + (wid * AMAX_SLOTS + lane) * AMAX_STRIDE;
+      k = __hip_atomic_load(kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(kp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int off = AMAX_SLOTS / 2; off >= 1; off >>= 1) {
+      const unsigned long long o = __shfl_xor(k, off);
+      k = o > k ? o : k;
+    }
+    if (lane == 0) reinterpret_cast<int*>(smem + L.slot_off)[wid] = k == 0ull ? 0 : (int)~(uint32_t)k;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(A.amax_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lds_barrier();
+  if (threadIdx.x != 0) return;
+  const int* ids = reinterpret_cast<const int*>(smem + L.slot_off);   // the split-tile slots are free now
   int agreed = 0;
   bool agree = A.draft != nullptr;
   for (int m = 0; m < M; ++m) {
-    const unsigned long long k = __hip_atomic_load(A.amax_key + m * AMAX_STRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int id = k == 0ull ? 0 : (int)~(uint32_t)k;
-    A.idx[m] = id;
-    __hip_atomic_store(A.amax_key + m * AMAX_STRIDE, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (agree && id == A.draft[m]) ++agreed;
+    A.idx[m] = ids[m];
+    if (agree && ids[m] == A.draft[m]) ++agreed;
     else agree = false;
   }
   if (A.accepted) A.accepted[0] = agreed;
-  __hip_atomic_store(A.amax_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int FMT, int MODE, int XT, int PREF>
