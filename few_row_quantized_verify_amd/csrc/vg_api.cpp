@@ -278,8 +278,8 @@ vg_status run_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* 
   const size_t parts = (size_t)vg::argmax_chunks(N) * M;
   float* part = nullptr;
   uint32_t* counters = nullptr;
-  if (vg_status s = workspace(dev.id, st, parts * 8, &part, &counters)) return s;
-  const hipError_t e = vg::launch_argmax(y, M, N, idx, draft, accepted, part, reinterpret_cast<int32_t*>(part + parts),
+  if (vg_status s = workspace(dev.id, st, parts * vg::ARG_KEY_BYTES, &part, &counters)) return s;
+  const hipError_t e = vg::launch_argmax(y, M, N, idx, draft, accepted, reinterpret_cast<unsigned long long*>(part),
                                          counters + kArgmaxCounterBase, st);
   if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';

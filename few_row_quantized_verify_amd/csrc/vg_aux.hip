@@ -215,40 +215,44 @@ hipError_t launch_hadamard(const void* x, int xt, int M, int K, int block, const
 // ---------------------------------------------------------------------------------------
 // Per-row argmax of fp32 logits over the whole chip, then (optionally) greedy acceptance of
 // a drafted block.  Block (c, m) scans columns [c*ARG_CHUNK, ...) of row m and parks its
-// (value, index); the last chunk of a row to arrive combines the row's chunks in chunk
-// order, and the last row to finish counts the leading rows whose argmax equals the
-// drafted token ("dflash-mlx-bonsai2" README, "Verify it yourself": greedy acceptance and
-// argmax parity).  Lowest index on ties; NaN is never selected (a row of only NaN gives 0).
-// The parked values and the counters are agent-scope atomic accesses (they bypass the
-// per-XCD L2 caches), so no device-wide fence is needed.
+// best (value, column) as one 64-bit key that orders like (value, -column): the value's bits
+// made order-preserving in the high half (-0 taken as +0), the complemented column in the
+// low half, NaN never entering.  The last chunk of a row to arrive takes the maximum over
+// the row's keys, and the last row to finish counts the leading rows whose argmax equals
+// the drafted token ("dflash-mlx-bonsai2" README, "Verify it yourself": greedy acceptance
+// and argmax parity).  Lowest column on ties; a row of only NaN gives 0.  The parked keys
+// and the counters are agent-scope atomic accesses (they bypass the per-XCD L2 caches), so
+// no device-wide fence is needed; each key has its own 128-byte line.
 constexpr int ARG_THREADS = 256;
 constexpr int ARG_PER_THREAD = 8;                          // loads in flight per thread
 constexpr int ARG_CHUNK = ARG_THREADS * ARG_PER_THREAD;    // columns per block
+constexpr int ARG_KEY_STRIDE = 16;                         // u64 elements between parked keys
 
-__device__ __forceinline__ bool arg_better(float v2, int i2, float v1, int i1) {
-  return i2 >= 0 && (i1 < 0 || v2 > v1 || (v2 == v1 && i2 < i1));
+__device__ __forceinline__ unsigned long long arg_key_aux(float v, int n) {
+  const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // orders like v
+  return ((unsigned long long)o << 32) | (uint32_t)~(uint32_t)n;
 }
 
-// Block-wide (value, index) selection; the rule (larger value, then lower index, NaN and
-// empty never win) is order-independent, so the result does not depend on the tree shape.
-__device__ __forceinline__ void arg_block_reduce(float* sv, int* si, float v, int i) {
-  sv[threadIdx.x] = v;
-  si[threadIdx.x] = i;
-  __syncthreads();
-  for (int off = ARG_THREADS / 2; off > 0; off >>= 1) {
-    if (threadIdx.x < off && arg_better(sv[threadIdx.x + off], si[threadIdx.x + off], sv[threadIdx.x], si[threadIdx.x])) {
-      sv[threadIdx.x] = sv[threadIdx.x + off];
-      si[threadIdx.x] = si[threadIdx.x + off];
-    }
-    __syncthreads();
+// Block-wide maximum of the threads' keys: across each wave by shuffles, then the four
+// waves' maxima through LDS.
+__device__ __forceinline__ unsigned long long arg_block_max(unsigned long long* sk, unsigned long long k) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(k, off);
+    k = o > k ? o : k;
   }
+  if ((threadIdx.x & 63) == 0) sk[threadIdx.x >> 6] = k;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < ARG_THREADS / 64; ++w) k = sk[w] > k ? sk[w] : k;
+  return k;
 }
 
 __global__ __launch_bounds__(ARG_THREADS) void vg_argmax_kernel(const float* y, int M, int N, int32_t* idx,
                                                               const int32_t* draft, int32_t* accepted,
-                                                              float* pval, int32_t* pidx, uint32_t* counters) {
-  __shared__ float sv[ARG_THREADS];
-  __shared__ int si[ARG_THREADS];
+                                                              unsigned long long* pkey, uint32_t* counters) {
+  __shared__ unsigned long long sk[ARG_THREADS / 64];
   __shared__ uint32_t last;
   const int c = blockIdx.x, m = blockIdx.y, C = gridDim.x;
   const float* row = y + (size_t)m * N;
@@ -259,32 +263,34 @@ __global__ __launch_bounds__(ARG_THREADS) void vg_argmax_kernel(const float* y, 
     const int n = n0 + e * ARG_THREADS;
     v[e] = n < N ? row[n] : __builtin_nanf("");
   }
-  float best = -INFINITY;
-  int bi = -1;
+  unsigned long long best = 0ull;
 #pragma unroll
-  for (int e = 0; e < ARG_PER_THREAD; ++e)
-    if (v[e] > best || (bi < 0 && v[e] == v[e])) { best = v[e]; bi = n0 + e * ARG_THREADS; }
-  arg_block_reduce(sv, si, best, bi);
+  for (int e = 0; e < ARG_PER_THREAD; ++e) {
+    if (v[e] == v[e]) {
+      const unsigned long long k = arg_key_aux(v[e], n0 + e * ARG_THREADS);
+      best = k > best ? k : best;
+    }
+  }
+  best = arg_block_max(sk, best);
   if (threadIdx.x == 0) {
-    __hip_atomic_store(pval + m * C + c, sv[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(pidx + m * C + c, si[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial has landed
+    __hip_atomic_store(pkey + (size_t)(m * C + c) * ARG_KEY_STRIDE, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the key has landed
     last = __hip_atomic_fetch_add(counters + m * ARG_CTR_STRIDE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
            (uint32_t)(C - 1);
   }
   __syncthreads();
   if (!last) return;
-  // last chunk of row m to finish: select among the row's C partials
-  best = -INFINITY;
-  bi = -1;
+  // last chunk of row m to finish: the maximum over the row's C keys
+  best = 0ull;
   for (int k = threadIdx.x; k < C; k += ARG_THREADS) {
-    const float pv = __hip_atomic_load(pval + m * C + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int pi = __hip_atomic_load(pidx + m * C + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (arg_better(pv, pi, best, bi)) { best = pv; bi = pi; }
+    const unsigned long long pk =
+        __hip_atomic_load(pkey + (size_t)(m * C + k) * ARG_KEY_STRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    best = pk > best ? pk : best;
   }
-  arg_block_reduce(sv, si, best, bi);
+  __syncthreads();   // sk is reused
+  best = arg_block_max(sk, best);
   if (threadIdx.x != 0) return;
-  const int32_t am = si[0] < 0 ? 0 : si[0];
+  const int32_t am = best == 0ull ? 0 : (int32_t)~(uint32_t)best;
   __hip_atomic_store(idx + m, am, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(counters + m * ARG_CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (draft == nullptr) return;
@@ -302,9 +308,9 @@ __global__ __launch_bounds__(ARG_THREADS) void vg_argmax_kernel(const float* y, 
 int argmax_chunks(int N) { return (N + ARG_CHUNK - 1) / ARG_CHUNK; }
 
 hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
-                         float* pval, int32_t* pidx, uint32_t* counters, hipStream_t s) {
+                         unsigned long long* pkey, uint32_t* counters, hipStream_t s) {
   hipLaunchKernelGGL(vg_argmax_kernel, dim3(argmax_chunks(N), M), dim3(ARG_THREADS), 0, s, y, M, N, idx, draft,
-                     accepted, pval, pidx, counters);
+                     accepted, pkey, counters);
   return hipGetLastError();
 }
 

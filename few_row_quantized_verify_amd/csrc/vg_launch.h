@@ -80,11 +80,12 @@ hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev);
 hipError_t launch_hadamard(const void* x, int xt, int M, int K, int block, const uint32_t* signs, float* out,
                            hipStream_t s);
 // Argmax of each row over the whole chip; with draft/accepted non-null also the greedy
-// acceptance count.  pval/pidx: argmax_chunks(N) * M partials; counters: 9 zeroed words
-// (left zeroed).
+// acceptance count.  pkey: argmax_chunks(N) * M parked keys, ARG_KEY_BYTES apart; counters:
+// 9 zeroed words 128 bytes apart (left zeroed).
 int argmax_chunks(int N);
 hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
-                         float* pval, int32_t* pidx, uint32_t* counters, hipStream_t s);
+                         unsigned long long* pkey, uint32_t* counters, hipStream_t s);
+constexpr int ARG_KEY_BYTES = 128;   // workspace bytes per parked key (one line each)
 // Streaming read of `bytes` (a multiple of 16) from buf; one word per workgroup to sink.
 int stream_read_blocks(const DeviceInfo& dev);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, const DeviceInfo& dev, hipStream_t s);
