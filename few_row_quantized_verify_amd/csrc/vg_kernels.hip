@@ -27,6 +27,11 @@
 //     pairs share a group after one permlane16 swap of two words.  Every accumulator
 //     register therefore holds one quantization group's dot products, and the per-group
 //     scale (and bias) is applied once per group in fp32.
+//   * K split across workgroups (tall K, or the rotated format from M = 4): each slice
+//     parks its partial outputs and the last slice of a row group to arrive adds them in
+//     slice order.
+//   * The output-head epilogue (verify_gemm_argmax, one K slice): every row's argmax over
+//     the workgroups' columns as one 64-bit maximum per row (fused_argmax).
 #include <atomic>
 
 #include "vg_device.h"
