@@ -8,7 +8,14 @@ namespace vg {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int VALU_THREADS = 256;
-constexpr int VALU_WK = 2048;   // K per LDS window (fp32 activations, 8 rows: 64 KB)
+constexpr int VALU_WK = 2048;   // K per LDS window
+// In LDS every word's K values (32 or 16) are followed by 4 unused floats, so the parts of a
+// row, which read their words' values at the same offset at the same time, fall on different
+// bank quads instead of all on one (a word is 128 or 64 bytes wide).
+constexpr int VALU_PAD = 4;
+constexpr int VALU_PITCH = VALU_WK + VALU_WK / 16 * VALU_PAD;   // floats per staged row
+template <int WK>
+__device__ __forceinline__ int xs_col(int k) { return k + (k / WK) * VALU_PAD; }
 constexpr int MAXM = 8;
 constexpr int VG_MAX_ROWS_DEV = 8;   // counter m (row m, m < 8) and counter 8 (finished rows)
 // Each counter has its own 128-byte line: all of a row's chunks update it, and counters
@@ -38,19 +45,21 @@ __device__ __forceinline__ float had_norm(int block) {
   return block == 64 ? 0.125f : (block == 256 ? 0.0625f : 0.08838834764831845f);   // 1/sqrt(block)
 }
 
-// In-place unnormalized Walsh-Hadamard transform of the `block`-blocks of an LDS buffer
-// [MAXM][len] (len a multiple of block), butterfly stage by stage.
-__device__ void lds_fwht(float* xs, int M, int len, int block) {
-  const int pairs = M * len / 2, half = block / 2;
+// In-place unnormalized Walsh-Hadamard transform of the `block`-blocks of the first `len`
+// elements of each staged row (len a multiple of block), butterfly stage by stage.
+template <int WK>
+__device__ void lds_fwht(float* xs, int rows, int len, int block) {
+  const int pairs = rows * len / 2, half = block / 2;
   for (int h = 1; h < block; h <<= 1) {
     for (int p = threadIdx.x; p < pairs; p += blockDim.x) {
       const int m = p / (len / 2), q = p - m * (len / 2);
       const int blk = q / half, r = q - blk * half;          // block/2 butterflies per block
       const int lo = (r / h) * (2 * h) + (r % h);
-      float* b = xs + m * len + blk * block;
-      const float a0 = b[lo], a1 = b[lo + h];
-      b[lo] = a0 + a1;
-      b[lo + h] = a0 - a1;
+      float* b = xs + m * VALU_PITCH;
+      const int i0 = xs_col<WK>(blk * block + lo), i1 = xs_col<WK>(blk * block + lo + h);
+      const float a0 = b[i0], a1 = b[i1];
+      b[i0] = a0 + a1;
+      b[i1] = a0 - a1;
     }
     __syncthreads();
   }
@@ -61,97 +70,165 @@ __device__ void lds_fwht(float* xs, int M, int len, int block) {
 // p takes words p, p + VALU_PARTS, ...), so neighbouring threads read neighbouring words of
 // a row and threads of equal part read the same activations (an LDS broadcast).  The parts
 // are added in part order through LDS, so results do not depend on timing.
-constexpr int VALU_PARTS = 8;
+//
+// The kernel is latency-bound at the sizes it serves (few workgroups, one wave per SIMD), so
+// every thread issues all of its loads of a window at once: its weight words, scales and
+// biases, then its share of the activation window.  MM is the row count rounded up to
+// 1, 2, 4 or 8; staged rows M..MM-1 are zeros, so the row loops carry no run-time bounds.
+constexpr int VALU_PARTS = 16;
 constexpr int VALU_ROWS = VALU_THREADS / VALU_PARTS;
 
-template <int FMT>
+template <int XT>
+__device__ __forceinline__ float load_x(const void* x, size_t idx) {
+  if constexpr (XT == 0) return static_cast<const float*>(x)[idx];
+  const uint32_t h = static_cast<const uint16_t*>(x)[idx];
+  if constexpr (XT == 2) return __uint_as_float(h << 16);
+  return h2f(h);
+}
+
+// A thread's share of an activation window: elements k = tid + i * VALU_THREADS of every row,
+// all loads issued back to back (rows M..MM-1 and k >= len read as zeros, without a load).
+constexpr int VALU_NI = VALU_WK / VALU_THREADS;
+template <int XT, int MM>
+__device__ __forceinline__ void load_window(const void* x, int M, int K, int k0, int len,
+                                            float (&v)[MM][VALU_NI]) {
+#pragma unroll
+  for (int m = 0; m < MM; ++m)
+#pragma unroll
+    for (int i = 0; i < VALU_NI; ++i) {
+      const int k = threadIdx.x + i * VALU_THREADS;
+      v[m][i] = (m < M && k < len) ? load_x<XT>(x, (size_t)m * K + k0 + k) : 0.0f;
+    }
+}
+
+template <int WK, int MM>
+__device__ __forceinline__ void store_window(const float (&v)[MM][VALU_NI], int len, float* xs) {
+#pragma unroll
+  for (int m = 0; m < MM; ++m)
+#pragma unroll
+    for (int i = 0; i < VALU_NI; ++i) {
+      const int k = threadIdx.x + i * VALU_THREADS;
+      if (k < len) xs[m * VALU_PITCH + xs_col<WK>(k)] = v[m][i];
+    }
+}
+
+template <int FMT, int XT, int MM>
 __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
-  __shared__ float xs[MAXM * VALU_WK];
-  __shared__ float red[VALU_ROWS][VALU_PARTS][MAXM];
+  __shared__ float xs[MAXM * VALU_PITCH];
+  __shared__ float red[VALU_ROWS][VALU_PARTS][MM + 1];   // +1: rows of parts on different banks
   constexpr int G = fmt_one_bit(FMT) ? 128 : 64;
-  constexpr int WK = fmt_one_bit(FMT) ? 32 : 16;   // K per word
+  constexpr int WK = fmt_one_bit(FMT) ? 32 : 16;        // K per word
+  constexpr int NWJ = VALU_WK / WK / VALU_PARTS;         // words per thread per full window
+  constexpr bool BIAS = FMT != SIGN1;
   const int part = threadIdx.x % VALU_PARTS, lr = threadIdx.x / VALU_PARTS;
   const int n = blockIdx.x * VALU_ROWS + lr;
-  const bool live = n < A.N;
-  const size_t wrow = (size_t)n * (A.K / WK), grow = (size_t)n * (A.K / G);
-  float acc[MAXM];
+  const int nl = min(n, A.N - 1);                        // rows past N compute row N-1, unstored
+  const size_t wrow = (size_t)nl * (A.K / WK), grow = (size_t)nl * (A.K / G);
+  float acc[MM];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
+  for (int m = 0; m < MM; ++m) acc[m] = 0.0f;
   for (int k0 = 0; k0 < A.K; k0 += VALU_WK) {
-    const int len = min(VALU_WK, A.K - k0);
-    __syncthreads();
-    for (int e = threadIdx.x; e < A.M * len; e += VALU_THREADS) {
-      const int m = e / len, k = e - m * len;
-      xs[m * len + k] = x_at(A.x, A.xt, (size_t)m * A.K + k0 + k);
+    const int len = min(VALU_WK, A.K - k0), nw = len / WK;
+    uint32_t word[NWJ], scb[NWJ], bib[NWJ];             // raw: converted where used
+#pragma unroll
+    for (int j = 0; j < NWJ; ++j) {                      // clamped: every load in bounds
+      const int wi = min(part + j * VALU_PARTS, nw - 1);
+      const int k = k0 + WK * wi;
+      word[j] = A.w[wrow + k / WK];
+      scb[j] = A.scales[grow + k / G];
+      bib[j] = BIAS ? A.biases[grow + k / G] : 0u;
     }
+    float xv[MM][VALU_NI];
+    load_window<XT, MM>(A.x, A.M, A.K, k0, len, xv);
+    __syncthreads();                                     // the previous window is consumed
+    store_window<WK, MM>(xv, len, xs);
     __syncthreads();
     if constexpr (FMT == HAD2) {
       if (A.signs) {
-        for (int e = threadIdx.x; e < A.M * len; e += VALU_THREADS) {
-          const int k = k0 + e % len;
-          if ((A.signs[k >> 5] >> (k & 31)) & 1u) xs[e] = -xs[e];
+        for (int e = threadIdx.x; e < MM * len; e += VALU_THREADS) {
+          const int m = e / len, kk = e - m * len, k = k0 + kk;
+          float* p = xs + m * VALU_PITCH + xs_col<WK>(kk);
+          if ((A.signs[k >> 5] >> (k & 31)) & 1u) *p = -*p;
         }
         __syncthreads();
       }
-      lds_fwht(xs, A.M, len, A.had_block);
+      lds_fwht<WK>(xs, MM, len, A.had_block);
       const float nrm = had_norm(A.had_block);
-      for (int e = threadIdx.x; e < A.M * len; e += VALU_THREADS) xs[e] *= nrm;
+      for (int e = threadIdx.x; e < MM * len; e += VALU_THREADS) {
+        const int m = e / len, kk = e - m * len;
+        xs[m * VALU_PITCH + xs_col<WK>(kk)] *= nrm;
+      }
       __syncthreads();
     }
-    if (live) {
-      for (int wi = part; wi < len / WK; wi += VALU_PARTS) {
-        const int k = k0 + WK * wi;
-        const uint32_t word = A.w[wrow + k / WK];
-        const size_t gi = grow + k / G;
-        const float sc = h2f(A.scales[gi]);
-        const float* xw = xs + WK * wi;
+#pragma unroll
+    for (int j = 0; j < NWJ; ++j) {
+      const int wi = part + j * VALU_PARTS;
+      if (wi < nw) {
+        const float* xw = xs + (WK + VALU_PAD) * wi;
+        const float scj = h2f(scb[j]), bij = BIAS ? h2f(bib[j]) : 0.0f;
         if constexpr (fmt_one_bit(FMT)) {
-          const float b = FMT == AFFINE1 ? h2f(A.biases[gi]) : 0.0f;
+          const float won = FMT == AFFINE1 ? scj + bij : scj;    // one fp32 rounding at most
+          const float woff = FMT == AFFINE1 ? bij : -scj;
 #pragma unroll 4
           for (int bit = 0; bit < 32; ++bit) {
-            const bool on = ((word >> bit) & 1u) != 0u;
-            const float wv = FMT == AFFINE1 ? (on ? sc + b : b) : (on ? sc : -sc);   // exact in fp32
+            const float wv = ((word[j] >> bit) & 1u) ? won : woff;
 #pragma unroll
-            for (int m = 0; m < MAXM; ++m)
-              if (m < A.M) acc[m] = __builtin_fmaf(xw[m * len + bit], wv, acc[m]);
+            for (int m = 0; m < MM; ++m) acc[m] = __builtin_fmaf(xw[m * VALU_PITCH + bit], wv, acc[m]);
           }
         } else {
-          const float b = h2f(A.biases[gi]);
 #pragma unroll 4
           for (int c = 0; c < 16; ++c) {
-            const float wv = (float)((word >> (2 * c)) & 3u) * sc + b;   // exact in fp32
+            const float wv = (float)((word[j] >> (2 * c)) & 3u) * scj + bij;   // one fp32 rounding at most
 #pragma unroll
-            for (int m = 0; m < MAXM; ++m)
-              if (m < A.M) acc[m] = __builtin_fmaf(xw[m * len + c], wv, acc[m]);
+            for (int m = 0; m < MM; ++m) acc[m] = __builtin_fmaf(xw[m * VALU_PITCH + c], wv, acc[m]);
           }
         }
       }
     }
   }
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) red[lr][part][m] = acc[m];
+  for (int m = 0; m < MM; ++m) red[lr][part][m] = acc[m];
   __syncthreads();
-  if (part == 0 && live) {
-    for (int m = 0; m < A.M; ++m) {
-      float sum = 0.0f;
-      for (int q = 0; q < VALU_PARTS; ++q) sum += red[lr][q][m];
-      A.y[(size_t)m * A.N + n] = sum;
-    }
+  // Thread (lr, m) adds row m's parts in part order.
+  if (part < A.M && n < A.N) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < VALU_PARTS; ++q) sum += red[lr][q][part];
+    A.y[(size_t)part * A.N + n] = sum;
   }
+}
+
+template <int FMT, int XT>
+static void launch_valu_m(const ValuArgs& A, dim3 grid, hipStream_t s) {
+  if (A.M <= 1) hipLaunchKernelGGL((vg_valu<FMT, XT, 1>), grid, dim3(VALU_THREADS), 0, s, A);
+  else if (A.M <= 2) hipLaunchKernelGGL((vg_valu<FMT, XT, 2>), grid, dim3(VALU_THREADS), 0, s, A);
+  else if (A.M <= 4) hipLaunchKernelGGL((vg_valu<FMT, XT, 4>), grid, dim3(VALU_THREADS), 0, s, A);
+  else hipLaunchKernelGGL((vg_valu<FMT, XT, 8>), grid, dim3(VALU_THREADS), 0, s, A);
+}
+
+template <int FMT>
+static hipError_t launch_valu_x(const ValuArgs& A, dim3 grid, hipStream_t s) {
+  switch (A.xt) {
+    case 0: launch_valu_m<FMT, 0>(A, grid, s); break;
+    case 1: launch_valu_m<FMT, 1>(A, grid, s); break;
+    case 2: launch_valu_m<FMT, 2>(A, grid, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev) {
   (void)dev;
+  if (c.M < 1 || c.M > MAXM || c.N < 1) return hipErrorInvalidValue;
   ValuArgs A{c.x, c.xt, c.w, c.scales, c.biases, c.y, c.M, c.K, c.N, c.had_block, c.signs};
   const dim3 grid((c.N + VALU_ROWS - 1) / VALU_ROWS);
   switch (c.fmt) {
-    case SIGN1: hipLaunchKernelGGL(vg_valu<SIGN1>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
-    case AFFINE2: hipLaunchKernelGGL(vg_valu<AFFINE2>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
-    case HAD2: hipLaunchKernelGGL(vg_valu<HAD2>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
-    case AFFINE1: hipLaunchKernelGGL(vg_valu<AFFINE1>, grid, dim3(VALU_THREADS), 0, c.stream, A); break;
+    case SIGN1: return launch_valu_x<SIGN1>(A, grid, c.stream);
+    case AFFINE2: return launch_valu_x<AFFINE2>(A, grid, c.stream);
+    case HAD2: return launch_valu_x<HAD2>(A, grid, c.stream);
+    case AFFINE1: return launch_valu_x<AFFINE1>(A, grid, c.stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------

@@ -150,6 +150,18 @@ def test_forced_variant_refuses_unsupported_rows(vg):
         vg.force_variant(-1)
 
 
+@pytest.mark.parametrize("fmt,K", [("affine2", 4160), ("had2", 4224), ("sign1", 4224), ("affine1", 2176)])
+@pytest.mark.parametrize("x_dtype", ["f32", "f16"])
+def test_valu_windows_every_row_count(vg, fmt, K, x_dtype):
+    """The VALU kernel stages the activations in windows of 2048: two full windows and a
+    last one narrower than the workgroup (64 or 128 wide), at every row count (the kernel
+    rounds M up to 1, 2, 4 or 8 with zero rows), N not a multiple of its 16 rows."""
+    case = draw_case(fmt, K, 37, x_dtype, seed=70)
+    for M in range(1, 9):
+        assert vg.plan_variant(fmt, x_dtype, M, 37, K) == VALU
+        check(case, M, run(vg, case, M), label=f"valu-windows[{x_dtype}]")
+
+
 @pytest.mark.parametrize("fmt,K", [("affine2", 320), ("had2", 384), ("sign1", 640), ("affine2", 768),
                                    ("sign1", 1152)])
 def test_k_not_multiple_of_step_falls_back(vg, fmt, K):
