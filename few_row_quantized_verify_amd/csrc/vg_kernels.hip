@@ -555,10 +555,13 @@ __device__ __forceinline__ void read_a(const char* smem, uint32_t addr, f16x8* d
   for (int q = 0; q < Fmt<FMT>::NQ; ++q) dst[q] = *reinterpret_cast<const f16x8*>(smem + addr + 16 * q);
 }
 
-template <int FMT, int MODE, bool BF>
+// AMASK: only the lanes whose operand row is a drafted row (a_on) read their A operands; the
+// others keep the zeros abuf was cleared to.  abuf lives across units for that reason.
+template <int FMT, int MODE, bool BF, bool AMASK>
 __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* smem, uint32_t a_lane, uint32_t e_lane,
                                              uint32_t xp_lane, const uint32_t* mk, const uint32_t* mg,
-                                             float yacc[4], f32x4& yb) {
+                                             float yacc[4], f32x4& yb, bool a_on,
+                                             f16x8 (&abuf)[2][2 * Fmt<FMT>::NQ]) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, NQ = F::NQ;
   constexpr int NPAIR = MODE == VAR_MFMA_Q ? GL / 2 : GL;
@@ -609,9 +612,10 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
     }
   }
 
-  f16x8 abuf[2][2 * NQ];
-  read_a<FMT>(smem, a_lane + ga[0] * F::GS, abuf[0]);
-  read_a<FMT>(smem, a_lane + gb[0] * F::GS, abuf[0] + NQ);
+  if (!AMASK || a_on) {
+    read_a<FMT>(smem, a_lane + ga[0] * F::GS, abuf[0]);
+    read_a<FMT>(smem, a_lane + gb[0] * F::GS, abuf[0] + NQ);
+  }
   f32x4 ea = *reinterpret_cast<const f32x4*>(smem + e_lane + ga[0] * (MAXM * 4));
   f32x4 eb = *reinterpret_cast<const f32x4*>(smem + e_lane + gb[0] * (MAXM * 4));
   f32x4 acc_a = ea, acc_b = eb;
@@ -620,8 +624,10 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
     const int pi = st / WPP, w = st % WPP;
     if (st + 1 < NSTEP) {
       const int pn = (st + 1) / WPP, wn = (st + 1) % WPP;
-      read_a<FMT>(smem, a_lane + ga[pn] * F::GS + wn * F::WB, abuf[(st + 1) & 1]);
-      read_a<FMT>(smem, a_lane + gb[pn] * F::GS + wn * F::WB, abuf[(st + 1) & 1] + NQ);
+      if (!AMASK || a_on) {
+        read_a<FMT>(smem, a_lane + ga[pn] * F::GS + wn * F::WB, abuf[(st + 1) & 1]);
+        read_a<FMT>(smem, a_lane + gb[pn] * F::GS + wn * F::WB, abuf[(st + 1) & 1] + NQ);
+      }
     }
     if (w == 0) {
       acc_a = ea;
@@ -858,7 +864,7 @@ __device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, 
   if (A.accepted) A.accepted[0] = agreed;
 }
 
-template <int FMT, int MODE, int XT, int PREF>
+template <int FMT, int MODE, int XT, int PREF, bool AMASK>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, GPS = 4 * GL;
@@ -917,6 +923,11 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   const uint32_t e_lane0 = L.e_off + ((MODE == VAR_MFMA_Q ? GL * g : 2 * (g >> 1) * GL) * MAXM + m0) * 4;
   const uint32_t xp_lane0 = L.xp_off + (uint32_t)arow * L.xp_pitch + (uint32_t)g * 16u;
 
+  f16x8 abuf[2][2 * F::NQ];   // A operands, double-buffered across steps (see compute_unit)
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int q = 0; q < 2 * F::NQ; ++q) abuf[u][q] = f16x8{};
   float* ytile = reinterpret_cast<float*>(smem + L.ytile_off);
   {
     // the zero rows: never written by the staging, so cleared once per launch
@@ -1032,7 +1043,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
           const uint32_t a_lane = a_lane0 + (uint32_t)cs * (GPS * F::GS);
           const uint32_t e_lane = e_lane0 + (uint32_t)cs * (GPS * MAXM * 4);
           const uint32_t xp_lane = xp_lane0 + (uint32_t)cs * 64u;   // 4 quads of groups per unit
-          compute_unit<FMT, MODE, BF>(ring[d], smem, a_lane, e_lane, xp_lane, mk, mg, yacc, yb);
+          compute_unit<FMT, MODE, BF, AMASK>(ring[d], smem, a_lane, e_lane, xp_lane, mk, mg, yacc, yb, av, abuf);
           if (++cs == ns || base + d + 1 == nu) {
             const bool sole = ua <= ct * ns && ub >= (ct + 1) * ns;
             flush_tile<FMT, MODE>(smem, L, ct, sole, ws0 == kb0, ua >= ct * ns ? 0 : 1, wid, g, i, yacc, yb);
@@ -1134,12 +1145,12 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
 template <int FMT, int XT, int PREF>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_q(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_Q, XT, PREF>(A, smem);
+  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false>(A, smem);
 }
-template <int FMT, int XT, int PREF>
+template <int FMT, int XT, int PREF, bool AMASK>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_H, XT, PREF>(A, smem);
+  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK>(A, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1250,9 +1261,22 @@ static hipError_t allow_lds(void (*kern)(MfmaArgs), std::atomic<uint64_t>& done,
 
 template <int FMT, int MODE, int XT, int PREF>
 static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t stream, const DeviceInfo& dev) {
-  void (*kern)(MfmaArgs) = MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT, PREF> : vg_mfma_h<FMT, XT, PREF>;
+  // 1-bit codes at 8 rows: the A-operand reads of the lanes without a drafted row are
+  // masked off (AMASK).  With the zero row those reads carry 4 * 8 + 4 distinct addresses,
+  // one more LDS pass per read than the 32 of the drafted rows; the masking costs three
+  // scalar instructions per read group, which pays at 8 rows only (measured on MI355X).
+  constexpr bool MASKABLE = MODE == VAR_MFMA_H && fmt_one_bit(FMT);
+  void (*kern)(MfmaArgs) = MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT, PREF> : vg_mfma_h<FMT, XT, PREF, false>;
   static std::atomic<uint64_t> attr_done{0};
-  const hipError_t e = allow_lds(kern, attr_done, dev);
+  static std::atomic<uint64_t> attr_done_mask{0};
+  std::atomic<uint64_t>* done = &attr_done;
+  if constexpr (MASKABLE) {
+    if (A.M == 8) {
+      kern = vg_mfma_h<FMT, XT, PREF, true>;
+      done = &attr_done_mask;
+    }
+  }
+  const hipError_t e = allow_lds(kern, *done, dev);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(NTHREADS), p.lds, stream, A);
   return hipGetLastError();
