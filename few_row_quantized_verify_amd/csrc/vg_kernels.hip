@@ -26,7 +26,9 @@
 //     decodes its own quantization group.  Mode H: 2 blocks of 8 rows (M <= 8), lane-group
 //     pairs share a group after one permlane16 swap of two words.  Every accumulator
 //     register therefore holds one quantization group's dot products, and the per-group
-//     scale (and bias) is applied once per group in fp32.
+//     scale (and bias) is applied once per group in fp32.  The lanes whose A row carries
+//     no drafted row feed zeros: a zero row in LDS, or for 1-bit codes at 8 rows operand
+//     registers cleared once per launch, their reads masked off.
 //   * K split across workgroups (tall K, or the rotated format from M = 4): each slice
 //     parks its partial outputs and the last slice of a row group to arrive adds them in
 //     slice order.
