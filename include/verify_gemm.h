@@ -22,7 +22,10 @@
  *     allocated on the first such call on that stream (hipMalloc), grown when a larger
  *     call needs it (after synchronizing that stream) and kept until the process ends.
  *     Calls on one stream are ordered by the stream; calls on different streams use
- *     different workspaces.
+ *     different workspaces.  The kernels leave the workspace's counters and keys zero,
+ *     so once a stream's workspace exists (one earlier call of the same kind and no
+ *     larger size on that stream), its calls allocate nothing, enqueue kernel launches
+ *     only and can be captured in a HIP graph and replayed.
  *   - Activations x are row-major [M, K] of dtype VG_F32, VG_F16 or VG_BF16 (raw IEEE bits);
  *     outputs y are row-major fp32 [M, N]; rows >= M are never read or written.
  *     VG_BF16 activations against the 1-bit formats enter the matrix cores unscaled,
