@@ -349,6 +349,8 @@ def test_dispatch_splits_tall_k(vg):
     assert vg.plan_ksplit("sign1", "bf16", 8, 5120, 17408) > 1
     assert vg.plan_ksplit("affine2", "f16", 1, 17408, 5120) == 1
     assert vg.plan_ksplit("affine2", "f16", 8, 151936, 5120) == 1
+    for M in range(1, 9):   # the rotated attention shape: the transform split five ways
+        assert vg.plan_ksplit("had2", "f16", M, 6144, 5120) == 5
 
 
 # ----------------------------------------------------------------------------- greedy acceptance
