@@ -1193,11 +1193,10 @@ static bool finish_plan(int fmt, int M, int K, int N, int rg, int ks, const Devi
   if ((uint64_t)(K / KSTEP) * (uint64_t)ks * (uint64_t)ks >= (1ull << 31)) return false;
   const int s_wg = (S + ks - 1) / ks;
   p->win_steps = window_steps(fmt, M, s_wg, p->tiles_max, dev.max_lds, &p->lds);
-  // Units in flight per wave: one when each wave streams only a few units (the first
-  // loads then reach the compute sooner), two for long streams; the 1-bit format's units
-  // are half as large and always keep two.
-  const int units_per_wave = ((rows_max + 15) / 16) * s_wg / NW;
-  p->pref = fmt_one_bit(fmt) ? 2 : (units_per_wave < 8 ? 1 : 2);
+  // Units in flight per wave: two for the 1-bit formats (their units are half as large),
+  // one for the 2-bit formats, long streams included (a second unit in flight measured
+  // slower on every 2-bit shape, the 243 MB output head too).
+  p->pref = fmt_one_bit(fmt) ? 2 : 1;
   return p->win_steps > 0;
 }
 
@@ -1333,8 +1332,8 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
       A.magic[k] = half_magic_affine2(q) | (half_magic_affine2(q) << 16);
     }
   }
-  if (fmt_one_bit(FMT) || p.pref == 2) return launch_kern<FMT, MODE, XT, 2>(A, p, c.stream, dev);
-  return launch_kern<FMT, MODE, XT, 1>(A, p, c.stream, dev);
+  if constexpr (fmt_one_bit(FMT)) return launch_kern<FMT, MODE, XT, 2>(A, p, c.stream, dev);
+  else return launch_kern<FMT, MODE, XT, 1>(A, p, c.stream, dev);
 }
 
 hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float* part, uint32_t* counters,
