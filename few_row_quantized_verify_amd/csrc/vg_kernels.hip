@@ -1207,8 +1207,8 @@ bool plan_mfma(int fmt, int variant, int M, int K, int N, const DeviceInfo& dev,
   const int cus = dev.cu_count;
   // K slices: the count minimising a per-workgroup cost in bytes, which adds the weight
   // units it streams (16-row tiles, so a short last tile costs a whole one), the activation
-  // bytes it stages at half weight (they come from L2) or double weight for the rotated
-  // format (the transform runs in every workgroup), and for a split the partial outputs
+  // bytes it stages at full weight, double for the rotated format (the transform runs in
+  // every workgroup), and for a split the partial outputs
   // written and read back plus a fixed cost for the reduction at the end.  Measured on
   // MI355X against forced slice counts.
   int ks = 1;
@@ -1223,7 +1223,7 @@ bool plan_mfma(int fmt, int variant, int M, int K, int N, const DeviceInfo& dev,
       if (g > tiles) g = tiles;
       if (g < 1) g = 1;
       const int rows = (N + g - 1) / g, steps = (S + k - 1) / k;
-      const double stage_weight = fmt == HAD2 ? 2.0 : 0.5;
+      const double stage_weight = fmt == HAD2 ? 2.0 : 1.0;
       double cost = (double)((rows + 15) / 16) * steps * unit_bytes + stage_weight * steps * M * KSTEP * 2.0;
       if (k > 1) cost += 8.0 * k * M * rows + 20480.0;
       if (k == 1 || cost < best) { best = cost; ks = k; }

@@ -346,7 +346,8 @@ def test_k_split_counters_reset_across_calls_and_streams(vg, ksplit):
 
 
 def test_dispatch_splits_tall_k(vg):
-    assert vg.plan_ksplit("sign1", "bf16", 8, 5120, 17408) > 1
+    for M in range(1, 9):   # the 17408-deep down projection: six slices
+        assert vg.plan_ksplit("sign1", "bf16", M, 5120, 17408) == 6
     assert vg.plan_ksplit("affine2", "f16", 1, 17408, 5120) == 1
     assert vg.plan_ksplit("affine2", "f16", 8, 151936, 5120) == 1
     for M in range(1, 9):   # the rotated attention shape: the transform split five ways
