@@ -1,20 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the few-row quantized verify GEMM on one MI355X.
 
-Default workload: 2-bit affine g64 weights, MLP up-projection shape K=5120, N=17408,
+Headline workload: 2-bit affine g64 weights, MLP up-projection shape K=5120, N=17408,
 fp16 activations, verify calls at every row count M = 1..8.  A "step" is one verify call
 at each M (8 calls).  The timed region runs exactly `--steps` steps, split into `--trials`
 trials; each trial runs one block of calls per row count with a HIP event pair around it
 (events on the stream the kernels run on), and the calls cycle through a pool of >= 1 GiB of
-distinct weight copies so the 256 MB Infinity Cache cannot serve repeated calls.  Per-M
-figures are the median over the trials (the min is given too), and host_us_per_call is the
-host time of issuing a call through the Python binding.  Inputs are resident in HBM before
-timing starts.  stream_ceiling times the library's plain streaming-read kernel over the
-same bytes and pool size the same way: the bandwidth reading those bytes can reach here.
+distinct weight copies so the 256 MB Infinity Cache cannot serve repeated calls.  Inputs
+are resident in HBM before timing starts.
 
-For the output-head workload a call is the verify GEMM with the argmax of every row (the
-head's argmax step) in one call, `verify_gemm_argmax`, whose argmax runs fused into the GEMM's
-epilogue on this shape; its per-M times include it.
+Before each block a gate (the library's streaming read over a 1 GiB buffer) holds the GPU
+while the host enqueues the block, so the block's event pair times the calls running back
+to back on the device rather than the host's submission rate; host_us_per_call reports
+the latter.  Before anything is timed the GPU runs 50 ms of streaming reads (clock
+settle: the first ~10 ms of back-to-back work run up to 10% slower, measured on MI355X),
+then the `--warmup` untimed steps.  Per-M figures are the median over the trials (the min
+is given too).
+
+stream_ceiling times the library's plain streaming-read kernel over the same bytes and
+pool size the same way, swept over loads in flight per thread and workgroups per CU; the
+best configuration is what reading those bytes in one launch reaches here.
+
+per_workload: the same measurement of the other named workloads (1-bit MLP up and down,
+rotated attention, output head, 1-bit affine), summarised: per-M us/call, t8/t1, stream
+ceiling, roofline fraction.  For the output head a call is the verify GEMM with the argmax
+of every row in one call (`verify_gemm_argmax`, the argmax fused into the GEMM's epilogue
+on this shape), at M = 1 and the ragged M = 5..8.
 
 For a routed-expert workload (synthetic.inputs.EXPERT_WORKLOADS) a call is one grouped
 expert verify of M rows, each routed to topk of the E experts; the calls cycle through 64
@@ -27,16 +38,17 @@ moved per second over all timed calls (GB/s, 1e9), plus per-M microseconds per c
 t(M=8)/t(M=1), a roofline object for the dominant kernel and the CPU oracle baseline.
 
 Options:
-  --workload NAME    another named workload (see synthetic.inputs.WORKLOADS)
-  --m LIST           only these row counts, e.g. "8" (for profiling one kernel)
-  --warmup W         untimed warm-up steps before the timed ones (default 200: a few tens of
-                     ms of calls, which the GPU needs to reach steady clocks; measured on
-                     MI355X, the first ~10 ms of back-to-back calls run up to 10% slower)
+  --workload NAME    another named workload as the headline (see synthetic.inputs.WORKLOADS)
+  --m LIST           only these row counts, e.g. "8" (for profiling one kernel; no
+                     per-workload entries)
+  --warmup W         untimed warm-up steps before the timed ones (default 200)
   --trials T         split the timed steps into T trials (default 7); per-M figures are
                      the median over the trials (and the min)
-  --force-variant V  run every call on kernel variant V (vg_mfma_q, vg_mfma_h, vg_valu)
-                     instead of the per-shape dispatch, for A/B timing
-  --table            also print one JSON line per workload and M (not the default)
+  --force-variant V  run every call on kernel variant V (see vg_variant_name) instead of the
+                     per-shape dispatch, for A/B timing
+  --table            one JSON line per workload (instead of per_workload entries)
+  --no-per-workload  the headline workload only
+  --stream-sweep     print the streaming-read sweep at every workload's byte count, then exit
   --no-cpu           skip the CPU oracle baseline leg
   --copy-calibration run only a device-to-device copy of known size (for HBM counters)
   --ingest-counters FETCH WRITE CFETCH CWRITE
@@ -101,20 +113,10 @@ def host_cpu() -> dict:
     return {"model": model, "os_cpu_count": os.cpu_count()}
 
 
-def _timed_reps(fn, budget_s: float, max_reps: int):
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        fn()
-        reps += 1
-        if time.perf_counter() - t0 > budget_s or reps >= max_reps:
-            break
-    return (time.perf_counter() - t0) / reps, reps
-
-
 def cpu_baseline(case) -> dict:
-    """The oracle (fp64 numpy, untuned) on the host, on a bounded sample of columns: with
-    BLAS on every thread it uses, and on one thread."""
+    """The oracle (fp64 numpy, untuned) on the host: the whole call (every output column)
+    at M = 8, median of 3 runs with BLAS on every thread it uses, and one run on one
+    thread."""
     import oracle
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
@@ -123,25 +125,23 @@ def cpu_baseline(case) -> dict:
         threadpool_limits = None
         threads = os.cpu_count() or 1
     M = 8
-    ncols = min(case.N, 8192)
-    cols = np.arange(ncols)
-    frac = ncols / case.N
 
     def run():
-        oracle.verify_columns(case.fmt, case.x(M), case.x_dtype, case.words, case.scales, case.biases, cols)
+        t0 = time.perf_counter()
+        oracle.verify(case.fmt, case.x(M), case.x_dtype, case.words, case.scales, case.biases)
+        return time.perf_counter() - t0
 
-    dt, reps = _timed_reps(run, 10.0, 20)
-    gbs = packed_bytes(case) * frac / dt / 1e9
+    runs = [run() for _ in range(3)]
+    dt = float(np.median(runs))
     one = None
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
-            dt1, reps1 = _timed_reps(run, 5.0, 5)
-        one = {"value": packed_bytes(case) * frac / dt1 / 1e9, "reps": reps1, "ms_per_rep": round(dt1 * 1e3, 1)}
-    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"M=8, first {ncols} of {case.N} output columns of {case.fmt} K={case.K}, "
-                      f"{reps} reps, {dt * 1e3:.1f} ms/rep; us/call-equivalent "
-                      f"{dt / frac * 1e6:.0f}",
-            "one_thread": one, "host": host_cpu()}
+            dt1 = run()
+        one = {"value": packed_bytes(case) / dt1 / 1e9, "s_per_call": round(dt1, 3)}
+    return {"value": packed_bytes(case) / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole call, M=8, {case.fmt} K={case.K} N={case.N}: median of 3 runs "
+                      f"({', '.join(f'{r * 1e3:.0f}' for r in runs)} ms)",
+            "us_per_call": round(dt * 1e6), "one_thread": one, "host": host_cpu()}
 
 
 def cpu_baseline_experts(ec, routes) -> dict:
@@ -278,32 +278,95 @@ def trial_sizes(steps: int, trials: int):
     return [steps // trials + (1 if t < steps % trials else 0) for t in range(trials)]
 
 
-def stream_ceiling(vg, torch, dev, nbytes: int, ncopy: int, warmup: int, sizes) -> dict:
-    """The library's streaming-read kernel over a pool of `ncopy` distinct buffers of one
-    call's packed bytes, timed like the calls (median over the trials): the bandwidth a
-    kernel doing nothing but reading those bytes reaches here."""
-    n16 = (nbytes + 15) // 16 * 16
-    pool = [torch.empty((n16 // 4,), dtype=torch.int32, device=dev).fill_(1) for _ in range(ncopy)]
-    sink = torch.empty((vg.lib().vg_stream_read_blocks(),), dtype=torch.int32, device=dev)
-    sh = torch.cuda.current_stream().cuda_stream
-    for j in range(warmup):
-        vg.stream_read(pool[j % ncopy], n16, sink, stream=sh)
-    torch.cuda.synchronize()
-    per = []
-    j = 0
-    for n in sizes:
+class Gate:
+    """Holds the GPU busy while the host enqueues a block of calls, so the block then runs
+    back to back and its event pair times the device, not the host's submission rate (a
+    call through the binding costs the host ~5 us, about what the smaller calls cost the
+    GPU).  The gate is the library's streaming read over a 1 GiB buffer, enqueued before
+    the block's start event; passes over it are added as the block grows."""
+
+    HOST_US_PER_CALL = 8.0   # generous: measured 4-6 us on the boxes
+
+    def __init__(self, vg, torch, dev, sh):
+        self.vg, self.sh = vg, sh
+        self.buf = torch.empty((POOL_BYTES // 4,), dtype=torch.int32, device=dev).fill_(1)
+        self.sink = torch.zeros((vg.lib().vg_stream_read_blocks(),), dtype=torch.int32, device=dev)
+        self.us_per_pass = 180.0   # ~1 GiB at ~6 TB/s; refined by calibrate()
+
+    def calibrate(self, torch):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        self.hold(1)
         e0.record()
-        for _ in range(n):
-            vg.stream_read(pool[j % ncopy], n16, sink, stream=sh)
-            j += 1
+        for _ in range(4):
+            self.hold(1)
         e1.record()
         torch.cuda.synchronize()
-        per.append(e0.elapsed_time(e1) * 1e3 / n)
-    us = float(np.median(per))
+        self.us_per_pass = e0.elapsed_time(e1) * 1e3 / 4
+
+    def hold(self, passes):
+        for _ in range(passes):
+            self.vg.stream_read(self.buf, POOL_BYTES, self.sink, stream=self.sh, loads_in_flight=4, wgs_per_cu=8)
+
+    def before(self, ncalls):
+        self.hold(max(1, int(np.ceil(ncalls * self.HOST_US_PER_CALL / self.us_per_pass))))
+
+
+def timed_blocks(torch, call, Ms, sizes, gate, j0=0):
+    """Per (trial, M): a gate, then an event pair around that trial's block of calls on the
+    kernels' stream.  Returns (per-M list of trial us/call, per-M host s, next call index)."""
+    ev = [{M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
+          for _ in sizes]
+    host_s = {M: 0.0 for M in Ms}
+    j = j0
+    for t, n in enumerate(sizes):
+        for M in Ms:
+            gate.before(n)
+            ev[t][M][0].record()
+            h0 = time.perf_counter()
+            for _ in range(n):
+                call(M, j)
+                j += 1
+            host_s[M] += time.perf_counter() - h0
+            ev[t][M][1].record()
+    torch.cuda.synchronize()
+    trial_us = {M: [ev[t][M][0].elapsed_time(ev[t][M][1]) * 1e3 / n for t, n in enumerate(sizes)] for M in Ms}
+    return trial_us, host_s, j
+
+
+STREAM_SWEEP = [(lif, wgs) for lif in (1, 2, 4, 8, 16) for wgs in (1, 2, 4, 8, 16)]
+
+
+def stream_ceiling(vg, torch, dev, nbytes: int, ncopy: int, warmup: int, sizes, gate, sweep=STREAM_SWEEP,
+                   full=False) -> dict:
+    """The library's streaming-read kernel over a pool of `ncopy` distinct buffers of one
+    call's packed bytes, timed like the calls (gate, then an event pair per block; median
+    over the trials), in every configuration of `sweep` (16-byte loads in flight per
+    thread, workgroups of 256 threads per CU): the best is what reading those bytes in one
+    launch reaches here."""
+    n16 = (nbytes + 15) // 16 * 16
+    pool = [torch.empty((n16 // 4,), dtype=torch.int32, device=dev).fill_(1) for _ in range(ncopy)]
+    sink = torch.zeros((vg.lib().vg_stream_read_blocks(),), dtype=torch.int32, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    table = []
+    for lif, wgs in sweep:
+        def call(_, j):
+            vg.stream_read(pool[j % ncopy], n16, sink, stream=sh, loads_in_flight=lif, wgs_per_cu=wgs)
+        for j in range(max(3, warmup)):
+            call(0, j)
+        trial_us, _, _ = timed_blocks(torch, call, (0,), sizes, gate)
+        us = float(np.median(trial_us[0]))
+        table.append({"loads_in_flight": lif, "wgs_per_cu": wgs, "us_per_call": round(us, 3),
+                      "pct_hbm_peak": round(100 * n16 / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)})
     del pool
-    return {"us_per_call": round(us, 3), "gbs": round(n16 / (us * 1e-6) / 1e9, 1),
-            "pct_hbm_peak": round(100 * n16 / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1), "bytes": n16}
+    best = min(table, key=lambda r: r["us_per_call"])
+    us = best["us_per_call"]
+    out = {"us_per_call": us, "gbs": round(n16 / (us * 1e-6) / 1e9, 1),
+           "pct_hbm_peak": round(100 * n16 / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1), "bytes": n16,
+           "loads_in_flight": best["loads_in_flight"], "wgs_per_cu": best["wgs_per_cu"],
+           "configs_swept": len(table)}
+    if full:
+        out["sweep"] = table
+    return out
 
 
 def load_traffic(kernel: str, digest: str):
@@ -371,6 +434,135 @@ def ingest_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload, M) -
     return 0
 
 
+def raw_caller(vg, fmt, x, w, s, b, y, sh, idx=None):
+    """The C ABI entry point of one verify call with its arguments marshalled once (the
+    binding's checked wrapper has already run the same call once): the timed loop then
+    costs the host the ctypes call only."""
+    import ctypes
+    from few_row_quantized_verify_amd import binding as B
+    L = B.lib()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    M, K = x.shape
+    N = w.shape[0]
+    xt = B._xdtype(x)
+    st = ctypes.c_void_p(sh)
+    if idx is not None:
+        args = (B.FORMATS[fmt], P(x), xt, M, K, P(w), P(s), P(b) if b is not None else None, N, P(y), P(idx),
+                None, None, st)
+        fn = L.verify_gemm_argmax
+    elif fmt == "sign1":
+        args, fn = (P(x), xt, M, K, P(w), P(s), N, P(y), st), L.verify_gemm_sign1
+    elif fmt == "had2":
+        args, fn = (P(x), xt, M, K, P(w), P(s), P(b), N, 128, P(y), st), L.verify_gemm_had2
+    else:
+        fn = L.verify_gemm_affine2 if fmt == "affine2" else L.verify_gemm_affine1
+        args = (P(x), xt, M, K, P(w), P(s), P(b), N, P(y), st)
+
+    def call():
+        st_ = fn(*args)
+        if st_ != 0:
+            raise B.VerifyGemmError(st_, L.vg_last_error().decode())
+    return call
+
+
+def bench_workload(args, vg, torch, dev, name, Ms, gate, sh, full_sweep=False) -> dict:
+    """One workload at each row count in Ms: warm-up, then the timed steps as trials of
+    gated blocks of calls cycling through a >= 1 GiB pool of weight copies."""
+    from synthetic.torch_io import case_tensors, f16_tensor, words_tensor
+    fmt, K, N, x_dtype, _ = WORKLOADS[name]
+    case = workload_case(name, seed=0)
+    pb = packed_bytes(case)
+    ncopy = max(2, -(-POOL_BYTES // pb))
+    x_all = {M: case_tensors(case, M, dev)[0] for M in Ms}
+    w0 = words_tensor(case.words, dev)
+    s0 = f16_tensor(case.scales, dev)
+    b0 = f16_tensor(case.biases, dev) if case.biases is not None else None
+    pool = [(w0.clone(), s0.clone(), None if b0 is None else b0.clone()) for _ in range(ncopy)]
+    del w0, s0, b0
+    ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
+    head = name.startswith("head_")
+    idx = {M: torch.empty((M,), dtype=torch.int32, device=dev) for M in Ms}
+    # one checked call per (M, copy) through the binding, then the raw C ABI calls
+    calls = {}
+    for M in Ms:
+        for c, (w, s, b) in enumerate(pool):
+            if head:
+                vg.verify_gemm_argmax(fmt, x_all[M], w, s, b, y=ys[M], idx=idx[M], stream=sh)
+            else:
+                vg.verify_gemm(fmt, x_all[M], w, s, b, y=ys[M], stream=sh)
+            calls[M, c] = raw_caller(vg, fmt, x_all[M], w, s, b, ys[M], sh, idx[M] if head else None)
+
+    def call(M, j):
+        calls[M, j % ncopy]()
+
+    for M in Ms:
+        for j in range(args.warmup):
+            call(M, j)
+    torch.cuda.synchronize()
+    sizes = trial_sizes(args.steps, args.trials)
+    t_wall = time.perf_counter()
+    trial_us, host_s, _ = timed_blocks(torch, call, Ms, sizes, gate)
+    wall = time.perf_counter() - t_wall
+    us = {M: float(np.median(trial_us[M])) for M in Ms}
+    total_s = sum(us.values()) * args.steps * 1e-6
+    value = pb * len(Ms) * args.steps / total_s / 1e9
+    per_m = {str(M): {"us_per_call": round(us[M], 3),
+                      "us_per_call_min": round(min(trial_us[M]), 3),
+                      "host_us_per_call": round(host_s[M] / args.steps * 1e6, 2),
+                      "gbs": round(pb / (us[M] * 1e-6) / 1e9, 1),
+                      "pct_hbm_peak": round(100 * pb / (us[M] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                      "variant": vg.variant_name(vg.plan_variant(fmt, x_dtype, M, N, K)),
+                      "k_slices": vg.plan_ksplit(fmt, x_dtype, M, N, K)}
+             for M in Ms}
+    del pool, calls
+    torch.cuda.empty_cache()
+    ceiling = stream_ceiling(vg, torch, dev, pb, ncopy, min(args.warmup, 20), sizes, gate, full=full_sweep)
+    Mtop = max(Ms)
+    kern = per_m[str(Mtop)]["variant"]
+    algo = pb + x_bytes(case, Mtop) + Mtop * N * 4
+    achieved = algo / (us[Mtop] * 1e-6) / 1e9
+    traffic = load_traffic(f"{kern}/{name}/M{Mtop}", kernel_source_digest())
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sum(us.values()) * 1e-3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if x_dtype != "f32" else "f32", "data": "synthetic",
+        "config": {"workload": name, "format": fmt, "K": K, "N": N, "x_dtype": x_dtype,
+                   "M": list(Ms), "packed_bytes_per_call": pb, "weight_pool_copies": ncopy},
+        "per_m": per_m,
+        "t8_over_t1": round(us[Mtop] / us[min(Ms)], 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": kern, "M": Mtop,
+                     "algorithmic_bytes_per_launch": algo},
+        "stream_ceiling": ceiling,
+        "trials": len(sizes),
+        "wall_s_timed": round(wall, 4),
+    }
+    return line
+
+
+def summary(line) -> dict:
+    """The compact per-workload entry of the headline line."""
+    pm = line["per_m"]
+    return {"config": {k: line["config"][k] for k in ("format", "K", "N", "x_dtype", "packed_bytes_per_call")},
+            "us_per_call": {m: v["us_per_call"] for m, v in pm.items()},
+            "pct_hbm_peak": {m: v["pct_hbm_peak"] for m, v in pm.items()},
+            "variant": {m: v["variant"] for m, v in pm.items()},
+            "gbs_all_m": line["value"], "t8_over_t1": line["t8_over_t1"],
+            "stream_ceiling_us": line["stream_ceiling"]["us_per_call"],
+            "stream_ceiling_pct": line["stream_ceiling"]["pct_hbm_peak"],
+            "roofline_frac": line["roofline"]["frac"]}
+
+
+# The workloads measured beside the headline on every default run (the headline is the
+# 2-bit MLP up-projection; see the module docstring).
+PER_WORKLOAD = ["mlp_up_sign1_k5120_n17408", "mlp_down_sign1_k17408_n5120", "attn_had2_k5120_n6144",
+                "head_affine2_k5120_n151936", "mlp_up_affine1_k5120_n17408"]
+CLOCK_SETTLE_S = 0.05
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +572,8 @@ def main() -> int:
     ap.add_argument("--workload", default="mlp_up_affine2_k5120_n17408")
     ap.add_argument("--table", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-per-workload", action="store_true")
+    ap.add_argument("--stream-sweep", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--m", default=None)
     ap.add_argument("--force-variant", default=None)
@@ -395,7 +589,6 @@ def main() -> int:
 
     import torch
     import few_row_quantized_verify_amd as vg
-    from synthetic.torch_io import case_tensors, f16_tensor, words_tensor
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -420,102 +613,51 @@ def main() -> int:
     if args.workload in EXPERT_WORKLOADS:
         print(json.dumps(bench_experts(args, vg, torch, dev)))
         return 0
+
+    sh = torch.cuda.current_stream().cuda_stream   # the raw handle: no lookup per call
+    gate = Gate(vg, torch, dev, sh)
+    # clock settle: the GPU runs back-to-back work for a while before anything is timed
+    # (measured on MI355X: the first ~10 ms of calls run up to 10% slower)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < CLOCK_SETTLE_S:
+        gate.hold(4)
+        torch.cuda.synchronize()
+    gate.calibrate(torch)
+
+    if args.stream_sweep:
+        # the streaming-read ceiling swept at the byte counts of the workloads
+        sizes = trial_sizes(args.steps, args.trials)
+        for name in WORKLOADS:
+            if name.startswith("tiny_"):
+                continue
+            pb = packed_bytes(workload_case(name, seed=0, N=1)) // 1 * WORKLOADS[name][2]
+            ncopy = max(2, -(-POOL_BYTES // pb))
+            c = stream_ceiling(vg, torch, dev, pb, ncopy, min(args.warmup, 20), sizes, gate, full=True)
+            print(json.dumps({"stream_sweep": name, "bytes": pb, **c}), flush=True)
+        return 0
+
     names = list(WORKLOADS) if args.table else [args.workload]
+    Ms_arg = tuple(int(v) for v in args.m.split(",")) if args.m else None
     lines = []
     headline = None
     for name in names:
-        fmt, K, N, x_dtype, Ms = WORKLOADS[name]
-        if args.m:
-            Ms = tuple(int(v) for v in args.m.split(","))
-        case = workload_case(name, seed=0)
-        pb = packed_bytes(case)
-        ncopy = max(2, -(-POOL_BYTES // pb))
-        x_all = {M: case_tensors(case, M, dev)[0] for M in Ms}
-        w0 = words_tensor(case.words, dev)
-        s0 = f16_tensor(case.scales, dev)
-        b0 = f16_tensor(case.biases, dev) if case.biases is not None else None
-        pool = [(w0.clone(), s0.clone(), None if b0 is None else b0.clone()) for _ in range(ncopy)]
-        ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
-        head = name.startswith("head_")
-        idx = {M: torch.empty((M,), dtype=torch.int32, device=dev) for M in Ms}
-
-        sh = torch.cuda.current_stream().cuda_stream   # the raw handle: no lookup per call
-
-        def call(M, j):
-            w, s, b = pool[j % ncopy]
-            if head:
-                vg.verify_gemm_argmax(fmt, x_all[M], w, s, b, y=ys[M], idx=idx[M], stream=sh)
-            else:
-                vg.verify_gemm(fmt, x_all[M], w, s, b, y=ys[M], stream=sh)
-
-        for M in Ms:
-            for j in range(args.warmup):
-                call(M, j)
-        torch.cuda.synchronize()
-
-        # the K timed steps run as `trials` trials; each (trial, M) block of calls has its own
-        # event pair on the kernels' stream
-        sizes = trial_sizes(args.steps, args.trials)
-        ev = [{M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
-              for _ in sizes]
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter()
-        host_s = {M: 0.0 for M in Ms}
-        j = 0
-        for t, n in enumerate(sizes):
-            for M in Ms:
-                ev[t][M][0].record()
-                h0 = time.perf_counter()
-                for _ in range(n):
-                    call(M, j)
-                    j += 1
-                host_s[M] += time.perf_counter() - h0
-                ev[t][M][1].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t_wall
-        trial_us = {M: [ev[t][M][0].elapsed_time(ev[t][M][1]) * 1e3 / n for t, n in enumerate(sizes)] for M in Ms}
-        us = {M: float(np.median(trial_us[M])) for M in Ms}
-        total_s = sum(us.values()) * args.steps * 1e-6
-        value = pb * len(Ms) * args.steps / total_s / 1e9
-        per_m = {str(M): {"us_per_call": round(us[M], 3),
-                          "us_per_call_min": round(min(trial_us[M]), 3),
-                          "host_us_per_call": round(host_s[M] / args.steps * 1e6, 2),
-                          "gbs": round(pb / (us[M] * 1e-6) / 1e9, 1),
-                          "pct_hbm_peak": round(100 * pb / (us[M] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                          "variant": vg.variant_name(vg.plan_variant(fmt, x_dtype, M, N, K))}
-                 for M in Ms}
-        ceiling = stream_ceiling(vg, torch, dev, pb, ncopy, args.warmup, sizes)
-        Mtop = max(Ms)
-        kern = per_m[str(Mtop)]["variant"]
-        algo = pb + x_bytes(case, Mtop) + Mtop * N * 4
-        achieved = algo / (us[Mtop] * 1e-6) / 1e9
-        traffic = load_traffic(f"{kern}/{name}/M{Mtop}", kernel_source_digest())
-        line = {
-            "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(sum(us.values()) * 1e-3, 4),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "f16" if x_dtype != "f32" else "f32", "data": "synthetic",
-            "config": {"workload": name, "format": fmt, "K": K, "N": N, "x_dtype": x_dtype,
-                       "M": list(Ms), "packed_bytes_per_call": pb, "weight_pool_copies": ncopy},
-            "per_m": per_m,
-            "t8_over_t1": round(us[Mtop] / us[min(Ms)], 3),
-            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": traffic, "kernel": kern, "M": Mtop,
-                         "algorithmic_bytes_per_launch": algo},
-            "stream_ceiling": ceiling,
-            "trials": len(sizes),
-            "wall_s_timed": round(wall, 4),
-        }
+        Ms = Ms_arg or WORKLOADS[name][4]
+        line = bench_workload(args, vg, torch, dev, name, Ms, gate, sh)
         if name == args.workload:
             headline = line
         lines.append(line)
-        del pool
-        torch.cuda.empty_cache()
-
     if headline is None:
         headline = lines[0]
+    if not args.no_per_workload and not args.table and Ms_arg is None:
+        per = {}
+        for name in PER_WORKLOAD:
+            if name == args.workload:
+                continue
+            per[name] = summary(bench_workload(args, vg, torch, dev, name, WORKLOADS[name][4], gate, sh))
+        headline["per_workload"] = per
+    headline["clock_settle_s"] = CLOCK_SETTLE_S
+    headline["gate"] = {"kind": "streaming read of 1 GiB before each block of calls", "us_per_pass":
+                        round(gate.us_per_pass, 1)}
     if not args.no_cpu:
         headline["cpu_baseline"] = cpu_baseline(workload_case(headline["config"]["workload"], seed=0))
     if args.table:

@@ -46,6 +46,7 @@ _SIGS = {
     "verify_gemm_argmax": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "verify_gemm_experts": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P]),
     "vg_last_error": (ctypes.c_char_p, []),
+    "vg_release_stream_workspace": (_I, [_P]),
     "vg_plan_variant": (_I, [_I, _I, _I, _I, _I]),
     "vg_variant_name": (ctypes.c_char_p, [_I]),
     "vg_force_variant": (_I, [_I]),
@@ -54,6 +55,8 @@ _SIGS = {
     "vg_force_ksplit": (_I, [_I]),
     "vg_stream_read_blocks": (_I, []),
     "vg_stream_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
+    "vg_stream_read_config": (_I, [_P, ctypes.c_size_t, _P, _I, _I, _P]),
+    "vg_debug_unpack": (_I, [_I, _I, _P, _I, _I, _P, _P]),
     "vg_debug_unpack_sign1": (_I, [_P, _I, _I, _P, _P]),
     "vg_debug_unpack_affine2": (_I, [_P, _I, _I, _P, _P]),
 }
@@ -107,18 +110,96 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _out(y, M, N, device):
+# Elements per packed uint32 word and per quantization group of each format.
+_WORD_K = {FMT_SIGN1: 32, FMT_AFFINE1: 32, FMT_AFFINE2: 16, FMT_HAD2: 16}
+_GROUP = {FMT_SIGN1: 128, FMT_AFFINE1: 128, FMT_AFFINE2: 64, FMT_HAD2: 64}
+_HAS_BIAS = {FMT_SIGN1: False, FMT_AFFINE1: True, FMT_AFFINE2: True, FMT_HAD2: True}
+
+
+def _bad(status, msg):
+    raise VerifyGemmError(status, msg)
+
+
+def _tensor(t, name, shape, dtypes, dev=None):
+    """The C ABI sees raw pointers only, so the binding checks what they point to: exact
+    shape, dtype, row-major contiguity, and (last, so CPU-side checks come first) that the
+    tensor lives on the same GPU as the activations."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        _bad(VG_ERR_ARG, f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        _bad(VG_ERR_SHAPE, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        _bad(VG_ERR_DTYPE, f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if not t.is_contiguous():
+        _bad(VG_ERR_SHAPE, f"{name} must be contiguous (row-major)")
+    if dev is not None and t.device != dev:
+        _bad(VG_ERR_ARG, f"{name} is on {t.device}, expected {dev}")
+    return t
+
+
+def _device(x):
+    """The activations' device: a GPU, and the current one (the library launches there)."""
+    torch = _torch()
+    if not x.is_cuda:
+        _bad(VG_ERR_ARG, f"x is on {x.device}, expected a GPU tensor")
+    if x.device.index != torch.cuda.current_device():
+        _bad(VG_ERR_ARG, f"x is on {x.device}, but the current device is cuda:{torch.cuda.current_device()}")
+    return x.device
+
+
+def _x(x):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        _bad(VG_ERR_SHAPE, "x must be a 2-D tensor [M, K]")
+    _tensor(x, "x", x.shape, (torch.float32, torch.float16, torch.bfloat16))
+    return x.shape
+
+
+def _weights(fmt, w, scales, biases, N, K, lead=()):
+    torch = _torch()
+    wk, g = _WORD_K[fmt], _GROUP[fmt]
+    if K % g:
+        _bad(VG_ERR_SHAPE, f"K={K} is not a multiple of the group size {g}")
+    _tensor(w, "w", (*lead, N, K // wk), (torch.int32,))
+    _tensor(scales, "scales", (*lead, N, K // g), (torch.float16,))
+    if _HAS_BIAS[fmt]:
+        if biases is None:
+            _bad(VG_ERR_ARG, "biases are required for this format")
+        _tensor(biases, "biases", (*lead, N, K // g), (torch.float16,))
+
+
+def _check_devices(dev, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            _bad(VG_ERR_ARG, f"{name} is on {t.device}, expected {dev}")
+
+
+def _out(y, M, N, x):
     torch = _torch()
     if y is None:
-        return torch.empty((M, N), dtype=torch.float32, device=device)
-    return y
+        return torch.empty((M, N), dtype=torch.float32, device=x.device)
+    return _tensor(y, "y", (M, N), (torch.float32,))
+
+
+def _gemm_args(fmt, x, w, scales, biases, y):
+    """Validated (M, K, N, y) of a plain verify call."""
+    torch = _torch()
+    M, K = _x(x)
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        _bad(VG_ERR_SHAPE, "w must be a 2-D tensor [N, K / (codes per word)]")
+    N = w.shape[0]
+    _weights(fmt, w, scales, biases, N, K)
+    if y is not None:
+        _tensor(y, "y", (M, N), (torch.float32,))
+    dev = _device(x)
+    _check_devices(dev, w=w, scales=scales, biases=biases if _HAS_BIAS[fmt] else None, y=y)
+    return M, K, N, _out(y, M, N, x)
 
 
 def verify_gemm_sign1(x, wbits, scales, y=None, stream=None):
     """y[M, N] = x[M, K] @ W^T, W 1-bit sign g128 (wbits int32 [N, K/32], scales fp16 [N, K/128])."""
-    M, K = x.shape
-    N = wbits.shape[0]
-    y = _out(y, M, N, x.device)
+    M, K, N, y = _gemm_args(FMT_SIGN1, x, wbits, scales, None, y)
     _check(lib().verify_gemm_sign1(_ptr(x), _xdtype(x), M, K, _ptr(wbits), _ptr(scales), N,
                                    _ptr(y), _stream(stream)))
     return y
@@ -126,9 +207,7 @@ def verify_gemm_sign1(x, wbits, scales, y=None, stream=None):
 
 def verify_gemm_affine2(x, wq, scales, biases, y=None, stream=None):
     """y[M, N] = x[M, K] @ W^T, W 2-bit affine g64 (wq int32 [N, K/16], scales/biases fp16 [N, K/64])."""
-    M, K = x.shape
-    N = wq.shape[0]
-    y = _out(y, M, N, x.device)
+    M, K, N, y = _gemm_args(FMT_AFFINE2, x, wq, scales, biases, y)
     _check(lib().verify_gemm_affine2(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
                                      _ptr(biases), N, _ptr(y), _stream(stream)))
     return y
@@ -136,9 +215,7 @@ def verify_gemm_affine2(x, wq, scales, biases, y=None, stream=None):
 
 def verify_gemm_affine1(x, wbits, scales, biases, y=None, stream=None):
     """y[M, N] = x[M, K] @ W^T, W MLX 1-bit affine g128 (wbits int32 [N, K/32], scales/biases fp16 [N, K/128])."""
-    M, K = x.shape
-    N = wbits.shape[0]
-    y = _out(y, M, N, x.device)
+    M, K, N, y = _gemm_args(FMT_AFFINE1, x, wbits, scales, biases, y)
     _check(lib().verify_gemm_affine1(_ptr(x), _xdtype(x), M, K, _ptr(wbits), _ptr(scales),
                                      _ptr(biases), N, _ptr(y), _stream(stream)))
     return y
@@ -148,9 +225,11 @@ def verify_gemm_had2(x, wq, scales, biases, had_block=128, y=None, stream=None, 
     """y = ((x * D) @ blockdiag(H_B/sqrt(B))) @ W^T with W 2-bit affine g64, B = had_block;
     D = diag(+-1) from the sign bits `signs` (int32 [K/32], bit set: negate), or the
     identity when signs is None."""
-    M, K = x.shape
-    N = wq.shape[0]
-    y = _out(y, M, N, x.device)
+    torch = _torch()
+    if signs is not None:
+        _tensor(signs, "signs", (_x(x)[1] // 32,), (torch.int32,))
+    M, K, N, y = _gemm_args(FMT_HAD2, x, wq, scales, biases, y)
+    _check_devices(x.device, signs=signs)
     if signs is None:
         _check(lib().verify_gemm_had2(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
                                       _ptr(biases), N, had_block, _ptr(y), _stream(stream)))
@@ -179,16 +258,24 @@ def verify_gemm_argmax(fmt: str, x, w, scales, biases=None, y=None, idx=None, dr
     the GEMM where the plan allows).  Returns (y, idx), or (y, idx, accepted) when draft
     (int32 [M] on the device) is given."""
     torch = _torch()
-    M, K = x.shape
-    N = w.shape[0]
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    code = FORMATS[fmt]
+    M = _x(x)[0]
+    if idx is not None:
+        _tensor(idx, "idx", (M,), (torch.int32,))
+    if draft is not None:
+        _tensor(draft, "draft", (M,), (torch.int32,))
+    if accepted is not None:
+        if draft is None:
+            _bad(VG_ERR_ARG, "accepted needs draft")
+        _tensor(accepted, "accepted", (1,), (torch.int32,))
+    M, K, N, y = _gemm_args(code, x, w, scales, biases, y)
+    _check_devices(x.device, idx=idx, draft=draft, accepted=accepted)
     if idx is None:
         idx = torch.empty((M,), dtype=torch.int32, device=x.device)
     if draft is not None and accepted is None:
         accepted = torch.empty((1,), dtype=torch.int32, device=x.device)
     null = ctypes.c_void_p(0)
-    _check(lib().verify_gemm_argmax(FORMATS[fmt], _ptr(x), _xdtype(x), M, K, _ptr(w), _ptr(scales),
+    _check(lib().verify_gemm_argmax(code, _ptr(x), _xdtype(x), M, K, _ptr(w), _ptr(scales),
                                     null if biases is None else _ptr(biases), N, _ptr(y), _ptr(idx),
                                     null if draft is None else _ptr(draft),
                                     null if accepted is None else _ptr(accepted), _stream(stream)))
@@ -201,20 +288,37 @@ def verify_gemm_experts(fmt: str, x, route, w, scales, biases=None, y=None, stre
     not written).  w, scales, biases: the E experts' packed weights stacked on dim 0.
     Returns y, fp32 [M, topk, N]."""
     torch = _torch()
-    M, K = x.shape
+    code = FORMATS[fmt]
+    M, K = _x(x)
+    if not isinstance(route, torch.Tensor) or route.dim() != 2:
+        _bad(VG_ERR_SHAPE, "route must be a 2-D tensor [M, topk]")
+    if not isinstance(w, torch.Tensor) or w.dim() != 3:
+        _bad(VG_ERR_SHAPE, "w must be a 3-D tensor [E, N, K / (codes per word)]")
     topk = route.shape[1]
     E, N = w.shape[0], w.shape[1]
+    _tensor(route, "route", (M, topk), (torch.int32,))
+    _weights(code, w, scales, biases, N, K, lead=(E,))
+    if y is not None:
+        _tensor(y, "y", (M, topk, N), (torch.float32,))
+    dev = _device(x)
+    _check_devices(dev, route=route, w=w, scales=scales, biases=biases if _HAS_BIAS[code] else None, y=y)
     if y is None:
         y = torch.empty((M, topk, N), dtype=torch.float32, device=x.device)
     b = ctypes.c_void_p(0) if biases is None else _ptr(biases)
-    _check(lib().verify_gemm_experts(FORMATS[fmt], _ptr(x), _xdtype(x), M, K, E, topk, _ptr(route),
+    _check(lib().verify_gemm_experts(code, _ptr(x), _xdtype(x), M, K, E, topk, _ptr(route),
                                      _ptr(w), _ptr(scales), b, N, _ptr(y), _stream(stream)))
     return y
 
 
 def hadamard_rotate(x, block=128, out=None, stream=None, signs=None):
     torch = _torch()
-    M, K = x.shape
+    M, K = _x(x)
+    if out is not None:
+        _tensor(out, "out", (M, K), (torch.float32,))
+    if signs is not None:
+        _tensor(signs, "signs", (K // 32,), (torch.int32,))
+    dev = _device(x)
+    _check_devices(dev, out=out, signs=signs)
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=x.device)
     if signs is None:
@@ -225,9 +329,21 @@ def hadamard_rotate(x, block=128, out=None, stream=None, signs=None):
     return out
 
 
+def _logits(y):
+    torch = _torch()
+    if not isinstance(y, torch.Tensor) or y.dim() != 2:
+        _bad(VG_ERR_SHAPE, "y must be a 2-D tensor [M, N]")
+    _tensor(y, "y", y.shape, (torch.float32,))
+    return y.shape
+
+
 def verify_argmax_rows(y, idx=None, stream=None):
     torch = _torch()
-    M, N = y.shape
+    M, N = _logits(y)
+    if idx is not None:
+        _tensor(idx, "idx", (M,), (torch.int32,))
+    dev = _device(y)
+    _check_devices(dev, idx=idx)
     if idx is None:
         idx = torch.empty((M,), dtype=torch.int32, device=y.device)
     _check(lib().verify_argmax_rows(_ptr(y), M, N, _ptr(idx), _stream(stream)))
@@ -238,7 +354,14 @@ def verify_accept_greedy(y, draft, idx=None, accepted=None, stream=None):
     """(idx, accepted): per-row argmax of the logits y [M, N] and the number of leading rows
     whose argmax equals draft[m] (draft: int32 [M] on the device)."""
     torch = _torch()
-    M, N = y.shape
+    M, N = _logits(y)
+    _tensor(draft, "draft", (M,), (torch.int32,))
+    if idx is not None:
+        _tensor(idx, "idx", (M,), (torch.int32,))
+    if accepted is not None:
+        _tensor(accepted, "accepted", (1,), (torch.int32,))
+    dev = _device(y)
+    _check_devices(dev, draft=draft, idx=idx, accepted=accepted)
     if idx is None:
         idx = torch.empty((M,), dtype=torch.int32, device=y.device)
     if accepted is None:
@@ -247,23 +370,46 @@ def verify_accept_greedy(y, draft, idx=None, accepted=None, stream=None):
     return idx, accepted
 
 
-def stream_read(buf, nbytes: int, sink=None, stream=None):
-    """Measurement aid: read nbytes of the device tensor buf once (vg_stream_read)."""
+def stream_read(buf, nbytes: int, sink=None, stream=None, loads_in_flight: int = 4, wgs_per_cu: int = 8):
+    """Measurement aid: read nbytes of the device tensor buf once (vg_stream_read_config)."""
     torch = _torch()
+    if not isinstance(buf, torch.Tensor) or not buf.is_contiguous():
+        _bad(VG_ERR_ARG, "buf must be a contiguous tensor")
+    if nbytes > buf.numel() * buf.element_size():
+        _bad(VG_ERR_SHAPE, f"nbytes={nbytes} exceeds the buffer's {buf.numel() * buf.element_size()} bytes")
     if sink is None:
         sink = torch.empty((lib().vg_stream_read_blocks(),), dtype=torch.int32, device=buf.device)
-    _check(lib().vg_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
+    _tensor(sink, "sink", (lib().vg_stream_read_blocks(),), (torch.int32,))
+    dev = _device(buf)
+    _check_devices(dev, sink=sink)
+    _check(lib().vg_stream_read_config(_ptr(buf), nbytes, _ptr(sink), loads_in_flight, wgs_per_cu,
+                                       _stream(stream)))
     return sink
 
 
-def debug_unpack(fmt: str, w, K, codes=None, stream=None):
+def debug_unpack(fmt: str, w, K, codes=None, stream=None, x_dtype: str = "f16"):
+    """Codes uint8 [N, K] decoded by the GEMM's register decode for (fmt, x_dtype)."""
     torch = _torch()
+    code = FORMATS[fmt]
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        _bad(VG_ERR_SHAPE, "w must be a 2-D tensor [N, K / (codes per word)]")
     N = w.shape[0]
+    if K % _WORD_K[code]:
+        _bad(VG_ERR_SHAPE, f"K={K} is not a multiple of {_WORD_K[code]}")
+    _tensor(w, "w", (N, K // _WORD_K[code]), (torch.int32,))
+    if codes is not None:
+        _tensor(codes, "codes", (N, K), (torch.uint8,))
+    dev = _device(w)
+    _check_devices(dev, codes=codes)
     if codes is None:
         codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
-    fn = lib().vg_debug_unpack_sign1 if fmt == "sign1" else lib().vg_debug_unpack_affine2
-    _check(fn(_ptr(w), N, K, _ptr(codes), _stream(stream)))
+    _check(lib().vg_debug_unpack(code, DTYPES[x_dtype], _ptr(w), N, K, _ptr(codes), _stream(stream)))
     return codes
+
+
+def release_stream_workspace(stream=None) -> None:
+    """Free the library's workspace of a stream (torch's current stream by default)."""
+    _check(lib().vg_release_stream_workspace(_stream(stream)))
 
 
 def plan_variant(fmt: str, x_dtype: str, M: int, N: int, K: int) -> int:

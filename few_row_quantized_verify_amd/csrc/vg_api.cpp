@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/verify_gemm.h"
 #include "vg_device.h"
@@ -102,20 +103,24 @@ bool variant_supports(int var, int fmt, int xt, int M, int N, int K, const vg::D
   return vg::plan_mfma(fmt, var, M, K, N, dev, g_forced_ks, &p);
 }
 
-// Workspaces of the calls that split K across workgroups, one per (device, stream): the
-// partial outputs and one arrival counter per row group.  Allocated on the first such call
-// on a stream, grown when a larger call needs it, kept until the process ends.  The
-// kernels leave the counters at zero, so consecutive calls on one stream share them; calls
-// on different streams never share a workspace.
+// Workspaces of the calls that split K across workgroups and of the argmax calls, one per
+// (device, stream): the partial outputs, the arrival counters and the argmax keys.  Created
+// on the first such call on a stream and replaced by a larger one when a call needs more.
+// A replaced buffer is never freed while the process runs (it goes on a retired list):
+// work already enqueued, or a graph captured earlier, may still use it.  Creating or
+// growing needs hipMalloc and a clear of the counters, so a call under stream capture
+// that would need either is refused (VG_ERR_UNSUPPORTED) before anything is enqueued.
+// The kernels leave counters and keys zero, so consecutive calls on one stream share them;
+// calls on different streams never share a workspace.
 struct Workspace {
   int dev;
   hipStream_t stream;
   char* ptr;
   size_t bytes;
+  std::vector<void*> retired;
 };
 std::mutex g_ws_mu;
-Workspace g_ws[64];
-int g_ws_count = 0;
+std::vector<Workspace> g_ws;
 // Counter area (zeroed at allocation, left zero by every call), u32 indices, each counter and
 // key on its own 128-byte line:
 //   [0, 24576)       split-K arrival counters, row group r at r * 32 (r < 768)
@@ -128,37 +133,66 @@ constexpr int kFusedCountIndex = kFusedKeyBase + 32 * 16 * VG_MAX_ROWS;
 constexpr size_t kCounterBytes = 116736;
 static_assert((kFusedCountIndex + 32) * 4 <= (int)kCounterBytes, "counter area too small");
 
+// Whether work enqueued on `stream` now would be captured into a graph.
+bool capturing(hipStream_t stream, bool* cap) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) return false;
+  *cap = st != hipStreamCaptureStatusNone;
+  return true;
+}
+
 vg_status workspace(int dev, hipStream_t stream, size_t part_bytes, float** part, uint32_t** counters) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
   Workspace* w = nullptr;
-  for (int k = 0; k < g_ws_count; ++k)
-    if (g_ws[k].dev == dev && g_ws[k].stream == stream) w = &g_ws[k];
-  if (!w) {
-    if (g_ws_count == 64) return fail(VG_ERR_HIP, "too many streams with split-K calls");
-    w = &g_ws[g_ws_count++];
-    *w = Workspace{dev, stream, nullptr, 0};
-  }
+  for (auto& e : g_ws)
+    if (e.dev == dev && e.stream == stream) w = &e;
   const size_t need = kCounterBytes + part_bytes;
-  if (w->bytes < need) {
-    if (w->ptr) {
-      // earlier calls on this stream may still read the old workspace
-      if (hipStreamSynchronize(stream) != hipSuccess || hipFree(w->ptr) != hipSuccess)
-        return fail(VG_ERR_HIP, "releasing the split-K workspace failed");
-      w->ptr = nullptr;
-      w->bytes = 0;
-    }
+  if (!w || w->bytes < need) {
+    bool cap = false;
+    if (!capturing(stream, &cap)) return fail(VG_ERR_HIP, "querying the stream's capture status failed");
+    if (cap)
+      return fail(VG_ERR_UNSUPPORTED,
+                  "this call needs a %zu-byte workspace on the capturing stream, which has %s: make one "
+                  "eager call of this size on the stream before capturing it",
+                  need, w ? "a smaller one" : "none");
     const size_t bytes = need + need / 2;
     void* p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) return fail(VG_ERR_HIP, "split-K workspace allocation of %zu bytes failed", bytes);
+    if (hipMalloc(&p, bytes) != hipSuccess) return fail(VG_ERR_HIP, "workspace allocation of %zu bytes failed", bytes);
     if (hipMemsetAsync(p, 0, kCounterBytes, stream) != hipSuccess) {
       (void)hipFree(p);
-      return fail(VG_ERR_HIP, "clearing the split-K counters failed");
+      return fail(VG_ERR_HIP, "clearing the workspace counters failed");
     }
+    if (!w) {
+      g_ws.push_back(Workspace{dev, stream, nullptr, 0, {}});
+      w = &g_ws.back();
+    }
+    if (w->ptr) w->retired.push_back(w->ptr);   // earlier calls on the stream may still use it
     w->ptr = static_cast<char*>(p);
     w->bytes = bytes;
   }
   *counters = reinterpret_cast<uint32_t*>(w->ptr);
   *part = reinterpret_cast<float*>(w->ptr + kCounterBytes);
+  return VG_OK;
+}
+
+// Frees the current device's workspace of `stream` (after synchronizing the stream).
+vg_status release_workspace(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(VG_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (size_t k = 0; k < g_ws.size(); ++k) {
+    Workspace& w = g_ws[k];
+    if (w.dev != dev || w.stream != stream) continue;
+    bool cap = false;
+    if (!capturing(stream, &cap)) return fail(VG_ERR_HIP, "querying the stream's capture status failed");
+    if (cap) return fail(VG_ERR_UNSUPPORTED, "the stream is capturing a graph");
+    if (hipStreamSynchronize(stream) != hipSuccess) return fail(VG_ERR_HIP, "synchronizing the stream failed");
+    bool ok = hipFree(w.ptr) == hipSuccess;
+    for (void* r : w.retired) ok = hipFree(r) == hipSuccess && ok;
+    g_ws.erase(g_ws.begin() + (long)k);
+    if (!ok) return fail(VG_ERR_HIP, "freeing the workspace failed");
+    return VG_OK;
+  }
   return VG_OK;
 }
 
@@ -404,6 +438,12 @@ vg_status verify_gemm_experts(int format, const void* x, int x_dtype, int M, int
 
 const char* vg_last_error(void) { return g_err; }
 
+vg_status vg_release_stream_workspace(void* stream) {
+  const vg_status s = release_workspace(static_cast<hipStream_t>(stream));
+  if (s == VG_OK) g_err[0] = '\0';
+  return s;
+}
+
 int vg_plan_variant(int format, int x_dtype, int M, int N, int K) {
   if (format < 0 || format > 3) return -1;
   if (x_dtype < 0 || x_dtype > 2 || M < 1 || M > VG_MAX_ROWS || N < 1 || K < 1) return -1;
@@ -455,35 +495,52 @@ int vg_stream_read_blocks(void) {
   return vg::stream_read_blocks(dev);
 }
 
-vg_status vg_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+vg_status vg_stream_read_config(const void* buf, size_t bytes, uint32_t* sink, int loads_in_flight, int wgs_per_cu,
+                                void* stream) {
   if (vg_status s = check_ptr(buf, "buf")) return s;
   if (bytes == 0 || bytes % 16 != 0) return fail(VG_ERR_SHAPE, "bytes=%zu is not a positive multiple of 16", bytes);
   if (!sink) return fail(VG_ERR_ARG, "sink is null");
   if (reinterpret_cast<uintptr_t>(sink) & 3u) return fail(VG_ERR_ALIGN, "sink is not 4-byte aligned");
+  if (loads_in_flight != 1 && loads_in_flight != 2 && loads_in_flight != 4 && loads_in_flight != 8 &&
+      loads_in_flight != 16)
+    return fail(VG_ERR_ARG, "loads in flight %d is not 1, 2, 4, 8 or 16", loads_in_flight);
+  if (wgs_per_cu < 1 || wgs_per_cu > 32) return fail(VG_ERR_ARG, "workgroups per CU %d outside 1..32", wgs_per_cu);
   vg::DeviceInfo dev;
   if (vg_status s = device_info(&dev)) return s;
-  const hipError_t e = vg::launch_stream_read(buf, bytes, sink, dev, static_cast<hipStream_t>(stream));
+  const hipError_t e = vg::launch_stream_read(buf, bytes, sink, loads_in_flight, wgs_per_cu, dev,
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return VG_OK;
+}
+
+vg_status vg_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  return vg_stream_read_config(buf, bytes, sink, 4, 8, stream);
+}
+
+vg_status vg_debug_unpack(int format, int x_dtype, const uint32_t* w, int N, int K, uint8_t* codes,
+                          void* stream) {
+  if (format < VG_FMT_SIGN1 || format > VG_FMT_AFFINE1) return fail(VG_ERR_ARG, "unknown format %d", format);
+  if (x_dtype == VG_F32)
+    return fail(VG_ERR_UNSUPPORTED, "fp32 activations take the VALU kernel, which has no register decode");
+  if (x_dtype != VG_F16 && x_dtype != VG_BF16) return fail(VG_ERR_DTYPE, "unknown activation dtype %d", x_dtype);
+  const int wk = vg::fmt_one_bit(format) ? 32 : 16;
+  if (N < 1 || K < wk || K % wk != 0) return fail(VG_ERR_SHAPE, "bad shape N=%d K=%d", N, K);
+  if ((long long)N * (K / wk) > (1ll << 38)) return fail(VG_ERR_SHAPE, "N=%d K=%d is too large", N, K);
+  if (vg_status s = check_ptr(w, "w")) return s;
+  if (!codes) return fail(VG_ERR_ARG, "codes is null");
+  const hipError_t e = vg::launch_debug_decode(format, x_dtype, w, N, K, codes, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return VG_OK;
 }
 
 vg_status vg_debug_unpack_sign1(const uint32_t* wbits, int N, int K, uint8_t* codes, void* stream) {
-  if (N < 1 || K < 32 || K % 32 != 0) return fail(VG_ERR_SHAPE, "bad shape N=%d K=%d", N, K);
-  if (vg_status s = check_ptr(wbits, "wbits")) return s;
-  if (!codes) return fail(VG_ERR_ARG, "codes is null");
-  const hipError_t e = vg::launch_debug_unpack(vg::SIGN1, wbits, N, K, codes, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  return VG_OK;
+  return vg_debug_unpack(VG_FMT_SIGN1, VG_F16, wbits, N, K, codes, stream);
 }
 
 vg_status vg_debug_unpack_affine2(const uint32_t* wq, int N, int K, uint8_t* codes, void* stream) {
-  if (N < 1 || K < 16 || K % 16 != 0) return fail(VG_ERR_SHAPE, "bad shape N=%d K=%d", N, K);
-  if (vg_status s = check_ptr(wq, "wq")) return s;
-  if (!codes) return fail(VG_ERR_ARG, "codes is null");
-  const hipError_t e = vg::launch_debug_unpack(vg::AFFINE2, wq, N, K, codes, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  return VG_OK;
+  return vg_debug_unpack(VG_FMT_AFFINE2, VG_F16, wq, N, K, codes, stream);
 }
 
 }  // extern "C"

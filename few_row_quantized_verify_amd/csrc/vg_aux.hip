@@ -1,5 +1,5 @@
 // vg_aux.hip -- the VALU verify kernel (fp32 activations, any row count), the standalone
-// block-Hadamard rotation, the output-head argmax and the code-decoding debug kernel.
+// block-Hadamard rotation, the output-head argmax and the streaming-read reference.
 #include "vg_device.h"
 #include "vg_launch.h"
 
@@ -393,21 +393,23 @@ hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32
 
 // ---------------------------------------------------------------------------------------
 // Streaming read of a buffer, for the measurement's achievable-bandwidth reference: every
-// byte is read once with 16-byte non-temporal loads, four in flight per thread, and folded
-// into one word per workgroup so the loads cannot be elided.
+// byte is read once with 16-byte non-temporal loads, U in flight per thread, and folded
+// into one word per workgroup so the loads cannot be elided.  The loads in flight per
+// thread and the workgroups per CU are parameters, so the reference can be swept.
 constexpr int STREAM_THREADS = 256;
-constexpr int STREAM_UNROLL = 4;
+constexpr int STREAM_MAX_WGS_PER_CU = 32;
+template <int U>
 __global__ __launch_bounds__(STREAM_THREADS) void vg_stream_read_kernel(const u32x4* buf, size_t n16, uint32_t* sink) {
   __shared__ uint32_t part[STREAM_THREADS / 64];
   const size_t stride = (size_t)gridDim.x * STREAM_THREADS;
   uint32_t acc = 0;
   size_t i = (size_t)blockIdx.x * STREAM_THREADS + threadIdx.x;
-  for (; i + (STREAM_UNROLL - 1) * stride < n16; i += STREAM_UNROLL * stride) {
-    u32x4 v[STREAM_UNROLL];
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < STREAM_UNROLL; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
 #pragma unroll
-    for (int u = 0; u < STREAM_UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   for (; i < n16; i += stride) {
     const u32x4 v = __builtin_nontemporal_load(buf + i);
@@ -419,49 +421,22 @@ __global__ __launch_bounds__(STREAM_THREADS) void vg_stream_read_kernel(const u3
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
-int stream_read_blocks(const DeviceInfo& dev) { return dev.cu_count * 8; }
+int stream_read_blocks(const DeviceInfo& dev) { return dev.cu_count * STREAM_MAX_WGS_PER_CU; }
 
-hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, const DeviceInfo& dev, hipStream_t s) {
-  hipLaunchKernelGGL(vg_stream_read_kernel, dim3(stream_read_blocks(dev)), dim3(STREAM_THREADS), 0, s,
-                     static_cast<const u32x4*>(buf), bytes / 16, sink);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------------------
-// Decode codes through the GEMM's register extraction: a register half holds
-// BETA + DELTA * code, so code = (half - BETA) / DELTA exactly.
-__global__ __launch_bounds__(256) void vg_debug_unpack_kernel(int fmt, const uint32_t* w, int N, int K, uint8_t* codes) {
-  const size_t wpr = fmt == SIGN1 ? K / 32 : K / 16;
-  const size_t gw = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (gw >= (size_t)N * wpr) return;
-  const size_t n = gw / wpr, wi = gw - n * wpr;
-  const uint32_t word = w[gw];
-  uint8_t* out = codes + n * (size_t)K;
-  if (fmt == SIGN1) {
-    uint32_t pr[16];
-    unpack_sign1_word(word, pr);
-#pragma unroll
-    for (int b0 = 0; b0 < 16; ++b0) {
-      const float beta = sign1_beta(b0);
-      out[32 * wi + b0] = (uint8_t)((h2f(pr[b0] & 0xFFFFu) - beta) / SIGN1_DELTA);
-      out[32 * wi + b0 + 16] = (uint8_t)((h2f(pr[b0] >> 16) - beta) / SIGN1_DELTA);
-    }
-  } else {
-    uint32_t pr[8];
-    unpack_affine2_word(word, pr);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float beta = affine2_beta(j);
-      out[16 * wi + j] = (uint8_t)((h2f(pr[j] & 0xFFFFu) - beta) / AFFINE2_DELTA);
-      out[16 * wi + j + 8] = (uint8_t)((h2f(pr[j] >> 16) - beta) / AFFINE2_DELTA);
-    }
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int loads_in_flight, int wgs_per_cu,
+                              const DeviceInfo& dev, hipStream_t s) {
+  if (wgs_per_cu < 1 || wgs_per_cu > STREAM_MAX_WGS_PER_CU) return hipErrorInvalidValue;
+  const dim3 grid(dev.cu_count * wgs_per_cu), block(STREAM_THREADS);
+  const u32x4* b = static_cast<const u32x4*>(buf);
+  const size_t n16 = bytes / 16;
+  switch (loads_in_flight) {
+    case 1: hipLaunchKernelGGL(vg_stream_read_kernel<1>, grid, block, 0, s, b, n16, sink); break;
+    case 2: hipLaunchKernelGGL(vg_stream_read_kernel<2>, grid, block, 0, s, b, n16, sink); break;
+    case 4: hipLaunchKernelGGL(vg_stream_read_kernel<4>, grid, block, 0, s, b, n16, sink); break;
+    case 8: hipLaunchKernelGGL(vg_stream_read_kernel<8>, grid, block, 0, s, b, n16, sink); break;
+    case 16: hipLaunchKernelGGL(vg_stream_read_kernel<16>, grid, block, 0, s, b, n16, sink); break;
+    default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_debug_unpack(int fmt, const uint32_t* w, int N, int K, uint8_t* codes, hipStream_t s) {
-  const size_t words = (size_t)N * (fmt == SIGN1 ? K / 32 : K / 16);
-  hipLaunchKernelGGL(vg_debug_unpack_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
-                     fmt, w, N, K, codes);
   return hipGetLastError();
 }
 

@@ -70,32 +70,4 @@ __host__ __device__ constexpr uint32_t half_magic_affine2(int p) { return (uint3
 __host__ __device__ constexpr float affine2_beta(int j) { return (float)(1 << (10 - affine2_pos(j))); }
 constexpr float AFFINE2_DELTA = 1.0f;
 
-__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
-  return (w & mask) | magic;  // one v_and_or_b32
-}
-
-// 16 operand registers of one 1-bit word, in b0 order.
-__device__ __forceinline__ void unpack_sign1_word(uint32_t w, uint32_t out[16]) {
-  const uint32_t src[3] = {w, w << 5, w >> 6};
-#pragma unroll
-  for (int b0 = 0; b0 < 16; ++b0) {
-    const int p = sign1_pos(b0);
-    const uint32_t mask = (1u << p) | (1u << (p + 16));
-    const uint32_t mg = half_magic_sign1(p) | (half_magic_sign1(p) << 16);
-    out[b0] = and_or(src[sign1_src(b0)], mask, mg);
-  }
-}
-
-// 8 operand registers of one 2-bit word, in j order.
-__device__ __forceinline__ void unpack_affine2_word(uint32_t w, uint32_t out[8]) {
-  const uint32_t src[3] = {w, w << 6, w >> 6};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int p = affine2_pos(j);
-    const uint32_t mask = (3u << p) | (3u << (p + 16));
-    const uint32_t mg = half_magic_affine2(p) | (half_magic_affine2(p) << 16);
-    out[j] = and_or(src[affine2_src(j)], mask, mg);
-  }
-}
-
 }  // namespace vg

@@ -688,6 +688,50 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
   }
 }
 
+// Debug decode of packed codes through the GEMM's own register extraction:
+// unpack_word_rt with the masks and magics decode_consts builds for the call's format and
+// activation dtype.  Every operand half holds BETA + DELTA * code, so the code is
+// (half - BETA) / DELTA, written as one byte per weight; a half that is not exactly
+// BETA + DELTA * c for a code c in range gives 0xFF, which no code equals.  Register j
+// holds the codes at K offsets j and j + WORD_K / 2 of its word.
+struct DecodeArgs {
+  const uint32_t* w;
+  uint8_t* codes;
+  int N, K;
+  uint32_t mask[8], magic[8];
+};
+
+template <int FMT, bool BF>
+__global__ __launch_bounds__(256) void vg_debug_decode(DecodeArgs D) {
+  using F = Fmt<FMT>;
+  constexpr int WK = F::WORD_K, NREG = F::PAIRS;
+  constexpr float DELTA = F::ONE_BIT ? SIGN1_DELTA : AFFINE2_DELTA;
+  constexpr int CMAX = F::ONE_BIT ? 1 : 3;
+  const size_t wpr = (size_t)(D.K / WK);
+  const size_t gw = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (gw >= (size_t)D.N * wpr) return;
+  const size_t n = gw / wpr, wi = gw - n * wpr;
+  uint32_t mk[8], mg[8], r[16];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    mk[k] = D.mask[k];
+    mg[k] = D.magic[k];
+  }
+  unpack_word_rt<FMT, BF>(D.w[gw], r, mk, mg);
+  uint8_t* out = D.codes + n * (size_t)D.K + (size_t)WK * wi;
+#pragma unroll
+  for (int j = 0; j < NREG; ++j) {
+    const float beta = BF ? sign1_beta_bf16(j) : (F::ONE_BIT ? sign1_beta(j) : affine2_beta(j));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t bits = h ? r[j] >> 16 : r[j] & 0xFFFFu;
+      const float c = ((BF ? bf16_to_f32(bits) : f16_to_f32(bits)) - beta) / DELTA;
+      const int ci = (int)c;
+      out[j + h * (WK / 2)] = ((float)ci == c && ci >= 0 && ci <= CMAX) ? (uint8_t)ci : (uint8_t)0xFF;
+    }
+  }
+}
+
 // Finishes a wave's contribution to tile t for the current window: undo the row scaling,
 // sum the lane-groups holding the same rows (register swaps between lane rows), then
 // either add into the tile accumulator (sole contributor; the first window stores, so the
@@ -1157,6 +1201,29 @@ __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
 
 // ---------------------------------------------------------------------------------------
 // Host side of the MFMA variants.
+
+// The code-extraction masks and magics of unpack_word_rt for a (format, activation dtype)
+// pair, built once per call on the host and held in registers by the kernels.  The GEMM
+// and the debug decode below take them from here, so the decode the tests check bit for
+// bit is the one the GEMM runs.
+static void decode_consts(int fmt, int xt, uint32_t mask[8], uint32_t magic[8]) {
+  for (int k = 0; k < 8; ++k) {
+    if (bf16_codes(fmt, xt)) {
+      mask[k] = (1u << k) | (1u << (k + 16));   // positions 0..7
+      magic[k] = bf16_magic_sign1(k) | (bf16_magic_sign1(k) << 16);
+    } else if (k >= 6) {
+      mask[k] = magic[k] = 0u;
+    } else if (fmt_one_bit(fmt)) {
+      const int q = 5 + k;   // positions 5..10
+      mask[k] = (1u << q) | (1u << (q + 16));
+      magic[k] = half_magic_sign1(q) | (half_magic_sign1(q) << 16);
+    } else {
+      const int q = 4 + 2 * (k < 3 ? k : 2);   // positions 4, 6, 8
+      mask[k] = (3u << q) | (3u << (q + 16));
+      magic[k] = half_magic_affine2(q) | (half_magic_affine2(q) << 16);
+    }
+  }
+}
 // Packed-weight bytes of a call (codes, scales and biases).
 static double packed_bytes(int fmt, int K, int N) {
   if (fmt == SIGN1) return (double)N * K / 8 + 2.0 * N * K / 128;
@@ -1316,22 +1383,7 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.had_stages = c.had_block == 64 ? 1 : (c.had_block == 256 ? 3 : 2);
   A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
   A.signs = c.signs;
-  for (int k = 0; k < 8; ++k) {
-    if (bf16_codes(FMT, XT)) {
-      A.mask[k] = (1u << k) | (1u << (k + 16));   // positions 0..7
-      A.magic[k] = bf16_magic_sign1(k) | (bf16_magic_sign1(k) << 16);
-    } else if (k >= 6) {
-      A.mask[k] = A.magic[k] = 0u;
-    } else if (fmt_one_bit(FMT)) {
-      const int q = 5 + k;   // positions 5..10
-      A.mask[k] = (1u << q) | (1u << (q + 16));
-      A.magic[k] = half_magic_sign1(q) | (half_magic_sign1(q) << 16);
-    } else {
-      const int q = 4 + 2 * (k < 3 ? k : 2);   // positions 4, 6, 8
-      A.mask[k] = (3u << q) | (3u << (q + 16));
-      A.magic[k] = half_magic_affine2(q) | (half_magic_affine2(q) << 16);
-    }
-  }
+  decode_consts(FMT, XT, A.mask, A.magic);
   if constexpr (fmt_one_bit(FMT)) return launch_kern<FMT, MODE, XT, 2>(A, p, c.stream, dev);
   else return launch_kern<FMT, MODE, XT, 1>(A, p, c.stream, dev);
 }
@@ -1356,6 +1408,33 @@ hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float*
   }
 #undef VG_DISPATCH_MODE
 #undef VG_DISPATCH_XT
+}
+
+hipError_t launch_debug_decode(int fmt, int xt, const uint32_t* w, int N, int K, uint8_t* codes, hipStream_t s) {
+  DecodeArgs D;
+  D.w = w;
+  D.codes = codes;
+  D.N = N;
+  D.K = K;
+  decode_consts(fmt, xt, D.mask, D.magic);
+  const size_t words = (size_t)N * (size_t)(K / fmt_word_k(fmt));
+  if (words == 0 || (words + 255) / 256 > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((words + 255) / 256));
+  const bool bf = bf16_codes(fmt, xt);
+  switch (fmt) {
+    case SIGN1:
+      if (bf) hipLaunchKernelGGL((vg_debug_decode<SIGN1, true>), grid, dim3(256), 0, s, D);
+      else hipLaunchKernelGGL((vg_debug_decode<SIGN1, false>), grid, dim3(256), 0, s, D);
+      break;
+    case AFFINE1:
+      if (bf) hipLaunchKernelGGL((vg_debug_decode<AFFINE1, true>), grid, dim3(256), 0, s, D);
+      else hipLaunchKernelGGL((vg_debug_decode<AFFINE1, false>), grid, dim3(256), 0, s, D);
+      break;
+    case AFFINE2: hipLaunchKernelGGL((vg_debug_decode<AFFINE2, false>), grid, dim3(256), 0, s, D); break;
+    case HAD2: hipLaunchKernelGGL((vg_debug_decode<HAD2, false>), grid, dim3(256), 0, s, D); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace vg

@@ -86,10 +86,16 @@ int argmax_chunks(int N);
 hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
                          unsigned long long* pkey, uint32_t* counters, hipStream_t s);
 constexpr int ARG_KEY_BYTES = 128;   // workspace bytes per parked key (one line each)
-// Streaming read of `bytes` (a multiple of 16) from buf; one word per workgroup to sink.
+// Streaming read of `bytes` (a multiple of 16) from buf with loads_in_flight (1, 2, 4, 8 or
+// 16) 16-byte loads per thread and wgs_per_cu (1..32) workgroups of 256 threads per CU; one
+// word per workgroup to sink, which holds stream_read_blocks(dev) words.
 int stream_read_blocks(const DeviceInfo& dev);
-hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, const DeviceInfo& dev, hipStream_t s);
-hipError_t launch_debug_unpack(int fmt, const uint32_t* w, int N, int K, uint8_t* codes,
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int loads_in_flight, int wgs_per_cu,
+                              const DeviceInfo& dev, hipStream_t s);
+// Codes of packed words as one byte per weight [N, K], decoded with the GEMM's register
+// extraction for (fmt, xt) (xt F16 or BF16: the 1-bit formats decode to bf16 against bf16
+// activations); 0xFF marks a half that is not an exact code.
+hipError_t launch_debug_decode(int fmt, int xt, const uint32_t* w, int N, int K, uint8_t* codes,
                                hipStream_t s);
 
 }  // namespace vg

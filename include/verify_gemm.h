@@ -19,13 +19,23 @@
  *     first use.  The GEMM calls allocate no device memory, except that a call whose K
  *     the dispatch splits across workgroups (see vg_plan_ksplit), and the argmax and
  *     acceptance calls, use a workspace owned by the library: one per device and stream,
- *     allocated on the first such call on that stream (hipMalloc), grown when a larger
- *     call needs it (after synchronizing that stream) and kept until the process ends.
- *     Calls on one stream are ordered by the stream; calls on different streams use
- *     different workspaces.  The kernels leave the workspace's counters and keys zero,
- *     so once a stream's workspace exists (one earlier call of the same kind and no
- *     larger size on that stream), its calls allocate nothing, enqueue kernel launches
- *     only and can be captured in a HIP graph and replayed.
+ *     created on the first such call on that stream (hipMalloc, and a clear of its
+ *     counters enqueued on the stream) and replaced by a larger one when a call needs
+ *     more.  A replaced workspace is not freed while the process runs (enqueued work or a
+ *     captured graph may still use it); vg_release_stream_workspace frees a stream's
+ *     workspaces.  The kernels leave the workspace's counters and keys zero, so calls on
+ *     one stream share it in stream order; calls on different streams use different
+ *     workspaces.  There is no limit on the number of streams.
+ *   - HIP graph capture: a call whose workspace already exists at the size it needs (one
+ *     earlier eager call of the same kind and no smaller size on the stream) enqueues
+ *     kernel launches only and can be captured and replayed.  A call under capture that
+ *     would need to create or grow its workspace is refused with VG_ERR_UNSUPPORTED
+ *     before anything is enqueued.  A replay uses the workspace of the stream the call was
+ *     captured on: replays must be ordered with each other and with eager calls on that
+ *     stream (replay on that stream, or synchronize), since overlapping calls would share
+ *     its counters.
+ *   - Host threads: calls may come from any thread; calls that share a stream are ordered
+ *     by that stream.
  *   - Activations x are row-major [M, K] of dtype VG_F32, VG_F16 or VG_BF16 (raw IEEE bits);
  *     outputs y are row-major fp32 [M, N]; rows >= M are never read or written.
  *     VG_BF16 activations against the 1-bit formats enter the matrix cores unscaled,
@@ -219,6 +229,16 @@ vg_status verify_gemm_experts(int format, const void* x, int x_dtype, int M, int
 const char* vg_last_error(void);
 
 /*
+ * Frees the current device's workspace(s) of `stream` (the split-K partials, arrival
+ * counters and argmax keys described above), after synchronizing the stream; VG_OK when
+ * the stream has none.  A later call on the stream creates a new one.  Must not be
+ * called while work that uses them may still run elsewhere (a graph captured on the
+ * stream and replayed later would use freed memory), and is refused (VG_ERR_UNSUPPORTED)
+ * while the stream is capturing.  For callers that create and destroy many streams.
+ */
+vg_status vg_release_stream_workspace(void* stream);
+
+/*
  * Kernel variant the per-shape dispatch picks for (format, x_dtype, M, N, K), or -1 if the
  * shape is invalid.  vg_variant_name() gives its name, which is also the kernel's name
  * prefix in a rocprofv3 trace.
@@ -256,18 +276,38 @@ vg_status vg_force_ksplit(int ksplit);
  * 16-byte aligned device buffer `buf`, every byte read once with 16-byte non-temporal
  * loads.  Not part of the method: timed at the byte count of a verify call, it shows the
  * bandwidth a kernel doing nothing but reading those bytes reaches on this device, the
- * ceiling beside which the verify GEMM's fraction of the HBM peak is read.  Writes one word
- * per workgroup to sink (uint32 [vg_stream_read_blocks()], device, 4-byte aligned).
- * Validation as elsewhere: VG_ERR_ARG, VG_ERR_ALIGN, VG_ERR_SHAPE.
+ * ceiling beside which the verify GEMM's fraction of the HBM peak is read.
+ * vg_stream_read_config takes the loads in flight per thread (1, 2, 4, 8 or 16) and the
+ * workgroups of 256 threads per CU (1..32), so the ceiling can be swept; vg_stream_read is
+ * the configuration (4, 8).  Each writes one word per workgroup to sink (uint32, device,
+ * 4-byte aligned, vg_stream_read_blocks() words).  Validation as elsewhere: VG_ERR_ARG,
+ * VG_ERR_ALIGN, VG_ERR_SHAPE.
  */
 int vg_stream_read_blocks(void);
 vg_status vg_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+vg_status vg_stream_read_config(const void* buf, size_t bytes, uint32_t* sink, int loads_in_flight,
+                                int wgs_per_cu, void* stream);
 
 /*
- * Debug: decode the packed codes on the GPU into one byte per weight, codes[N, K] uint8
- * (0/1 for sign bits, 0..3 for 2-bit codes), using the same bit extraction as the GEMM
- * kernels, so tests can compare codes bit for bit.
+ * Debug: decode packed codes on the GPU into one byte per weight, codes[N, K] uint8 (0/1
+ * for the 1-bit formats, 0..3 for the 2-bit ones), with the register decode the verify
+ * GEMM itself runs for (format, x_dtype): the same extraction routine, fed the same masks
+ * and magic constants the GEMM's launch builds (the 1-bit formats decode to bf16 operand
+ * halves against VG_BF16 activations, to fp16 halves otherwise).  Each operand half holds
+ * BETA + DELTA * code; the byte is (half - BETA) / DELTA with the same BETA the GEMM's
+ * offset sums subtract, or 0xFF when the half is not exactly such a value, so tests can
+ * compare the decoded codes with the packed words bit for bit ("Bonsai-27B-mlx-1bit" model
+ * card, binary weight format: one bit per weight; the code-to-half construction:
+ * "Ishizuki" README, credits).
+ *   format   VG_FMT_SIGN1, VG_FMT_AFFINE2, VG_FMT_HAD2 or VG_FMT_AFFINE1; w holds [N, K/32]
+ *            (1-bit) or [N, K/16] (2-bit) words, 16-byte aligned.
+ *   x_dtype  VG_F16 or VG_BF16; VG_F32 -> VG_ERR_UNSUPPORTED (fp32 activations take the VALU
+ *            kernel, which extracts each code with a shift and a mask instead).
+ * Requires N >= 1 and K a positive multiple of 32 (1-bit) or 16 (2-bit).
+ * vg_debug_unpack_sign1 and vg_debug_unpack_affine2 are this call with VG_F16.
  */
+vg_status vg_debug_unpack(int format, int x_dtype, const uint32_t* w, int N, int K, uint8_t* codes,
+                          void* stream);
 vg_status vg_debug_unpack_sign1(const uint32_t* wbits, int N, int K, uint8_t* codes,
                                 void* stream);
 vg_status vg_debug_unpack_affine2(const uint32_t* wq, int N, int K, uint8_t* codes,

@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
                "vg_force_variant", "vg_variant_count", "vg_debug_unpack_sign1", "vg_debug_unpack_affine2",
                "vg_plan_ksplit", "vg_force_ksplit", "verify_accept_greedy", "verify_gemm_affine1",
                "verify_gemm_had2_signed", "hadamard_rotate_signed", "verify_gemm_experts",
-               "verify_gemm_argmax"):
+               "verify_gemm_argmax", "vg_debug_unpack", "vg_release_stream_workspace", "vg_stream_read_config"):
         assert fn in names, fn
 
 
@@ -214,3 +214,103 @@ def test_stream_read_validation():
     assert L.vg_stream_read(ALIGNED, 1000, ALIGNED, None) == B.VG_ERR_SHAPE
     assert L.vg_stream_read(ALIGNED, 1024, None, None) == B.VG_ERR_ARG
     assert L.vg_stream_read(ALIGNED, 1024, ALIGNED + 2, None) == B.VG_ERR_ALIGN
+    for lif, wgs in ((3, 8), (0, 8), (32, 8), (4, 0), (4, 33)):
+        assert L.vg_stream_read_config(ALIGNED, 1024, ALIGNED, lif, wgs, None) == B.VG_ERR_ARG
+
+
+# ----------------------------------------------------------------------------- binding checks
+# The C ABI sees raw pointers and cannot check what they point to, so the Python binding
+# checks shape, dtype, contiguity and device before any call into the library.  Each case
+# below is caught on the host; CPU tensors of the right shape reach the device check last.
+def _affine2_tensors(torch, M=2, K=1024, N=48, xdt=None):
+    x = torch.zeros((M, K), dtype=xdt or torch.float16)
+    w = torch.zeros((N, K // 16), dtype=torch.int32)
+    s = torch.zeros((N, K // 64), dtype=torch.float16)
+    b = torch.zeros((N, K // 64), dtype=torch.float16)
+    return x, w, s, b
+
+
+def _raises(status, fn, *a, **kw):
+    with pytest.raises(vgm.VerifyGemmError) as e:
+        fn(*a, **kw)
+    assert e.value.status == status, str(e.value)
+    return str(e.value)
+
+
+def test_binding_checks_weight_shapes_against_the_format():
+    torch = pytest.importorskip("torch")
+    x, w, s, b = _affine2_tensors(torch)
+    # 1-bit words handed to the 2-bit call (half the words a row needs), and the reverse
+    w1 = torch.zeros((48, 1024 // 32), dtype=torch.int32)
+    assert "w has shape" in _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, w1, s, b)
+    s1 = torch.zeros((48, 1024 // 128), dtype=torch.float16)
+    assert "w has shape" in _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_sign1, x, w, s1)
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, w, s1, b)           # scales of the wrong group
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, w, s, b[:40])       # biases of too few rows
+    _raises(B.VG_ERR_DTYPE, vgm.verify_gemm_affine2, x, w, s.float(), b)    # scales not fp16
+    _raises(B.VG_ERR_DTYPE, vgm.verify_gemm_affine2, x, w.long(), s, b)     # words not int32
+    _raises(B.VG_ERR_ARG, vgm.verify_gemm_affine2, x, w, s, None)           # affine needs biases
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x[:, :1000], w, s, b)  # K not a group multiple
+
+
+def test_binding_checks_outputs_and_layout():
+    torch = pytest.importorskip("torch")
+    x, w, s, b = _affine2_tensors(torch)
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, w, s, b, y=torch.zeros((1, 48)))  # too few rows
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, w, s, b, y=torch.zeros((2, 47)))
+    _raises(B.VG_ERR_DTYPE, vgm.verify_gemm_affine2, x, w, s, b, y=torch.zeros((2, 48), dtype=torch.float16))
+    xt = torch.zeros((1024, 2), dtype=torch.float16).t()   # [2, 1024] view, not row-major
+    assert "contiguous" in _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, xt, w, s, b)
+    wt = torch.zeros((64, 48), dtype=torch.int32).t()
+    assert "contiguous" in _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, wt, s, b)
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x[0], w, s, b)         # 1-D activations
+    _raises(B.VG_ERR_DTYPE, vgm.verify_gemm_affine2, x.to(torch.int16), w, s, b)
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    x, w, s, b = _affine2_tensors(torch)
+    assert "GPU" in _raises(B.VG_ERR_ARG, vgm.verify_gemm_affine2, x, w, s, b)
+    assert "GPU" in _raises(B.VG_ERR_ARG, vgm.verify_gemm_had2, x, w, s, b)
+    assert "GPU" in _raises(B.VG_ERR_ARG, vgm.verify_argmax_rows, torch.zeros((2, 10)))
+    assert "GPU" in _raises(B.VG_ERR_ARG, vgm.hadamard_rotate, x)
+
+
+def test_binding_checks_argmax_experts_and_aux_arguments():
+    torch = pytest.importorskip("torch")
+    x, w, s, b = _affine2_tensors(torch, M=3)
+    i32 = torch.int32
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_argmax, "affine2", x, w, s, b, idx=torch.zeros(2, dtype=i32))
+    _raises(B.VG_ERR_DTYPE, vgm.verify_gemm_argmax, "affine2", x, w, s, b, idx=torch.zeros(3, dtype=torch.int64))
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_argmax, "affine2", x, w, s, b, idx=torch.zeros(3, dtype=i32),
+            draft=torch.zeros(2, dtype=i32))
+    _raises(B.VG_ERR_ARG, vgm.verify_gemm_argmax, "affine2", x, w, s, b, idx=torch.zeros(3, dtype=i32),
+            accepted=torch.zeros(1, dtype=i32))
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_had2, x, w, s, b, signs=torch.zeros(31, dtype=i32))
+    # routed experts: w [E, N, words], route int32 [M, topk]
+    we = torch.zeros((4, 48, 64), dtype=i32)
+    se = torch.zeros((4, 48, 16), dtype=torch.float16)
+    route = torch.zeros((3, 2), dtype=i32)
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_experts, "affine2", x, route, w, s, b)          # 2-D weights
+    _raises(B.VG_ERR_DTYPE, vgm.verify_gemm_experts, "affine2", x, route.long(), we, se, se)
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_experts, "affine2", x, route[:2], we, se, se)
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_experts, "affine2", x, route, we, se[:, :, :8], se)
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_experts, "affine2", x, route, we, se, se,
+            y=torch.zeros((3, 2, 47)))
+    assert "GPU" in _raises(B.VG_ERR_ARG, vgm.verify_gemm_experts, "affine2", x, route, we, se, se)
+    _raises(B.VG_ERR_SHAPE, vgm.verify_accept_greedy, torch.zeros((3, 10)), torch.zeros(2, dtype=i32))
+    _raises(B.VG_ERR_DTYPE, vgm.verify_argmax_rows, torch.zeros((3, 10), dtype=torch.float16))
+    _raises(B.VG_ERR_DTYPE, vgm.debug_unpack, "affine2", w, 1024, codes=torch.zeros((48, 1024), dtype=i32))
+    _raises(B.VG_ERR_SHAPE, vgm.debug_unpack, "sign1", w, 1024)          # 2-bit words as 1-bit codes
+    _raises(B.VG_ERR_SHAPE, vgm.stream_read, torch.zeros(16, dtype=i32), 128)
+
+
+def test_debug_unpack_abi_validation():
+    L = B.lib()
+    assert L.vg_debug_unpack(9, B.VG_F16, ALIGNED, 4, 64, ALIGNED, None) == B.VG_ERR_ARG
+    assert L.vg_debug_unpack(B.FMT_SIGN1, B.VG_F32, ALIGNED, 4, 64, ALIGNED, None) == B.VG_ERR_UNSUPPORTED
+    assert L.vg_debug_unpack(B.FMT_SIGN1, 5, ALIGNED, 4, 64, ALIGNED, None) == B.VG_ERR_DTYPE
+    assert L.vg_debug_unpack(B.FMT_SIGN1, B.VG_BF16, ALIGNED, 4, 48, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.vg_debug_unpack(B.FMT_AFFINE2, B.VG_F16, ALIGNED, 4, 40, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.vg_debug_unpack(B.FMT_AFFINE1, B.VG_BF16, ALIGNED + 4, 4, 64, ALIGNED, None) == B.VG_ERR_ALIGN
+    assert L.vg_debug_unpack(B.FMT_HAD2, B.VG_F16, ALIGNED, 4, 64, None, None) == B.VG_ERR_ARG

@@ -39,7 +39,16 @@ def run(vg, case, M, y=None):
     return out.cpu().numpy().astype(np.float64)
 
 
-def check(case, M, y_gpu, cols=None, tol=TOL, label="", had=None):
+def reference(case, M, cols=None, had=None):
+    """(y_ref, mag) of the oracle for the first M rows over `cols` (all when None)."""
+    args = (case.fmt, case.x(M), case.x_dtype, case.words, case.scales, case.biases)
+    if cols is None:
+        cols = np.arange(case.N)
+    had = had or {}
+    return oracle.verify_columns(*args, cols, **had), oracle.magnitude_columns(*args, cols, **had)
+
+
+def check(case, M, y_gpu, cols=None, tol=TOL, label="", had=None, ref=None):
     """Two bars, both against the fp64 oracle on the same inputs.
 
     Componentwise, every output: |y - y_ref| <= (2^-11 + K 2^-24) * mag + slack, with
@@ -49,13 +58,14 @@ def check(case, M, y_gpu, cols=None, tol=TOL, label="", had=None):
     2^-30 K max|a| max|w| covers activations that fall into the fp16 subnormal range.
     Normwise, per row, when at least 16 columns are compared: the 2e-3 bar.  Over fewer
     columns the normwise ratio is the relative error of a handful of dot products, which
-    has no bound when one of them happens to be close to zero."""
-    args = (case.fmt, case.x(M), case.x_dtype, case.words, case.scales, case.biases)
+    has no bound when one of them happens to be close to zero.
+
+    ref: (y_ref, mag) of the oracle for at least the first M rows over `cols` (output rows
+    depend only on their own activation row, so one reference at M = 8 serves every M)."""
     if cols is None:
         cols = np.arange(case.N)
     had = had or {}
-    y_ref = oracle.verify_columns(*args, cols, **had)
-    mag = oracle.magnitude_columns(*args, cols, **had)
+    y_ref, mag = reference(case, M, cols, had) if ref is None else (ref[0][:M], ref[1][:M])
     got = y_gpu[:, cols]
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"
     K = case.K
@@ -82,18 +92,51 @@ def check(case, M, y_gpu, cols=None, tol=TOL, label="", had=None):
 
 
 # ----------------------------------------------------------------------------- codes
-@pytest.mark.parametrize("fmt,K", [("sign1", 512), ("affine2", 256), ("sign1", 1024), ("affine2", 640)])
-def test_debug_unpack_is_bit_exact(vg, fmt, K):
-    rng = np.random.default_rng(K)
-    WK = 32 if fmt == "sign1" else 16
+DECODES = [("sign1", "f16"), ("sign1", "bf16"), ("affine1", "f16"), ("affine1", "bf16"),
+           ("affine2", "f16"), ("affine2", "bf16"), ("had2", "f16"), ("had2", "bf16")]
+
+
+def hand_words(fmt, K, seed):
+    rng = np.random.default_rng(seed)
+    WK = 32 if fmt in ("sign1", "affine1") else 16
     words = rng.integers(0, 1 << 32, size=(37, K // WK), dtype=np.uint64).astype(np.uint32)
     words[0, :4] = [0x00000001, 0x80000000, 0xAAAAAAAA, 0xE4E4E4E4]
     words[1, :] = 0xFFFFFFFF
     words[2, :] = 0
-    codes = vg.debug_unpack(fmt, words_tensor(words), K)
+    return words
+
+
+def oracle_codes(fmt, words, K):
+    return oracle.unpack_sign1(words, K) if fmt in ("sign1", "affine1") else oracle.unpack_affine2(words, K)
+
+
+@pytest.mark.parametrize("fmt,x_dtype", DECODES)
+@pytest.mark.parametrize("K", [1024, 2048])
+def test_debug_unpack_is_bit_exact(vg, fmt, x_dtype, K):
+    """The GEMM's register decode for each (format, activation dtype) pair -- the runtime
+    masks and magics its launch builds, the bf16 operand halves of the 1-bit formats against
+    bf16 activations included -- recovers every code exactly."""
+    words = hand_words(fmt, K, K + len(fmt))
+    codes = vg.debug_unpack(fmt, words_tensor(words), K, x_dtype=x_dtype)
     torch.cuda.synchronize()
-    ref = oracle.unpack_sign1(words, K) if fmt == "sign1" else oracle.unpack_affine2(words, K)
-    assert np.array_equal(codes.cpu().numpy(), ref)
+    got = codes.cpu().numpy()
+    assert not np.any(got == 0xFF), "a decoded half is not BETA + DELTA * code"
+    assert np.array_equal(got, oracle_codes(fmt, words, K))
+
+
+@pytest.mark.parametrize("name,x_dtype", [("mlp_up_affine2_k5120_n17408", "f16"),
+                                          ("mlp_up_sign1_k5120_n17408", "bf16"),
+                                          ("mlp_down_sign1_k17408_n5120", "bf16"),
+                                          ("attn_had2_k5120_n6144", "f16"),
+                                          ("mlp_up_affine1_k5120_n17408", "bf16")])
+def test_debug_unpack_full_workloads(vg, name, x_dtype):
+    """Every packed word of the full-size workloads through the GEMM's decode for that
+    workload's activation dtype, against the oracle's unpack."""
+    case = workload_case(name, seed=0)
+    codes = vg.debug_unpack(case.fmt, words_tensor(case.words), case.K, x_dtype=x_dtype)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    assert np.array_equal(got, oracle_codes(case.fmt, case.words, case.K))
 
 
 # ----------------------------------------------------------------------------- small shapes
@@ -250,39 +293,53 @@ def sample_cols(N, k=384, seed=0):
     return cols
 
 
-@pytest.mark.parametrize("name,Ms", [
-    ("mlp_up_affine2_k5120_n17408", (1, 2, 4, 5, 8)),
-    ("mlp_up_sign1_k5120_n17408", (1, 4, 8)),
-    ("mlp_down_sign1_k17408_n5120", (1, 5, 8)),
-    ("attn_had2_k5120_n6144", (1, 3, 8)),
-    ("tiny_sign1_k512_n256", tuple(range(1, 9))),
-    ("mlp_up_affine1_k5120_n17408", (1, 4, 8)),
-])
-def test_full_workload_sampled(vg, name, Ms):
-    case = workload_case(name, seed=0)
-    cols = sample_cols(case.N) if case.N > 1024 else None
-    for M in Ms:
-        check(case, M, run(vg, case, M), cols=cols, label=name)
+_REFS = {}
 
 
-def test_head_argmax_matches_oracle(vg):
+def workload_ref(name):
+    """The workload's case and its oracle reference at M = 8 over every column (cached)."""
+    if name not in _REFS:
+        case = workload_case(name, seed=0)
+        _REFS.clear()   # one full-size reference held at a time
+        _REFS[name] = (case, reference(case, 8))
+    return _REFS[name]
+
+
+@pytest.mark.parametrize("name", ["tiny_sign1_k512_n256", "mlp_up_affine2_k5120_n17408",
+                                  "mlp_up_sign1_k5120_n17408", "mlp_down_sign1_k17408_n5120",
+                                  "attn_had2_k5120_n6144", "mlp_up_affine1_k5120_n17408"])
+def test_full_workload_every_row_count(vg, name):
+    """The full-size workloads at every row count M = 1..8, every output column, in the
+    launch configuration the benchmark times (the per-shape dispatch), against the oracle."""
+    case, ref = workload_ref(name)
+    for M in range(1, 9):
+        check(case, M, run(vg, case, M), ref=ref,
+              label=f"{name}[{vg.variant_name(vg.plan_variant(case.fmt, case.x_dtype, M, case.N, case.K))}]")
+
+
+def test_head_every_column_and_argmax(vg):
+    """The output head at M = 1 and the ragged short drafts M = 5..8: every logit against
+    the oracle, and each row's argmax, from the call the benchmark times (the GEMM with the
+    argmax fused into it), equal to the oracle's stored argmax."""
     with open(os.path.join(GOLDEN, "head_affine2_k5120_n151936_argmax.json")) as f:
         gold = json.load(f)
-    case = workload_case(gold["workload"], seed=gold["seed"])
-    cols = sample_cols(case.N, k=256)
-    for M in (5, 6, 7, 8):
+    case, ref = workload_ref(gold["workload"])
+    assert case.N == 151936 and gold["seed"] == 0
+    for M in (1, 5, 6, 7, 8):
         x, w, s, b = case_tensors(case, M)
-        y = vg.verify_gemm_affine2(x, w, s, b)
-        idx = vg.verify_argmax_rows(y).cpu().numpy()
+        y, idx = vg.verify_gemm_argmax("affine2", x, w, s, b)
+        idx = idx.cpu().numpy()
         y_np = y.cpu().numpy().astype(np.float64)
-        err = check(case, M, y_np, cols=cols, label="head")
+        err = check(case, M, y_np, ref=ref, label="head")
         for m in range(M):
             if idx[m] != gold["argmax"][m]:
                 # a flip is only acceptable as a diagnosed near-tie, and none is expected
                 # at these gaps; report it loudly either way
                 raise AssertionError(f"row {m}: argmax {idx[m]} != oracle {gold['argmax'][m]} "
                                      f"(oracle top-2 gap {gold['top2_gap'][m]:.3e}, err {err:.2e})")
-        assert np.array_equal(idx, np.argmax(y_np, axis=1))
+        assert np.array_equal(idx, np.argmax(ref[0][:M], axis=1))
+        # the standalone argmax kernel on the same logits agrees
+        assert np.array_equal(vg.verify_argmax_rows(y).cpu().numpy(), idx)
 
 
 @pytest.mark.parametrize("fmt,x_dtype", [("affine2", "f16"), ("sign1", "bf16"), ("had2", "bf16")])
@@ -466,13 +523,16 @@ def test_had2_blocks_and_signs(vg, block, K, N, x_dtype):
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096, 1 << 20, (1 << 24) + 48])
-def test_stream_read_reads_every_word(vg, nbytes):
-    """The measurement's streaming read touches every word once: the XOR of its per-
-    workgroup results equals the XOR of all words of the buffer."""
+@pytest.mark.parametrize("lif,wgs", [(4, 8), (1, 1), (2, 3), (8, 16), (16, 32)])
+def test_stream_read_reads_every_word(vg, nbytes, lif, wgs):
+    """The measurement's streaming read touches every word once in every configuration the
+    ceiling sweep uses: the XOR of its per-workgroup results equals the XOR of all words of
+    the buffer."""
     rng = np.random.default_rng(nbytes)
     words = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
     buf = torch.from_numpy(words.view(np.int32)).cuda()
-    sink = vg.stream_read(buf, nbytes)
+    sink = torch.zeros((vg.lib().vg_stream_read_blocks(),), dtype=torch.int32, device="cuda")
+    vg.stream_read(buf, nbytes, sink, loads_in_flight=lif, wgs_per_cu=wgs)
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(words)
