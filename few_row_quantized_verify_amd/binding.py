@@ -44,6 +44,7 @@ _SIGS = {
     "verify_argmax_rows": (_I, [_P, _I, _I, _P, _P]),
     "verify_accept_greedy": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "verify_gemm_argmax": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
+    "verify_gemm_argmax_noalloc": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P]),
     "verify_gemm_experts": (_I, [_I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P]),
     "vg_last_error": (ctypes.c_char_p, []),
     "vg_release_stream_workspace": (_I, [_P]),
@@ -279,6 +280,38 @@ def verify_gemm_argmax(fmt: str, x, w, scales, biases=None, y=None, idx=None, dr
                                     null if biases is None else _ptr(biases), N, _ptr(y), _ptr(idx),
                                     null if draft is None else _ptr(draft),
                                     null if accepted is None else _ptr(accepted), _stream(stream)))
+    return (y, idx) if draft is None else (y, idx, accepted)
+
+
+def verify_gemm_argmax_noalloc(fmt: str, x, w, scales, biases, y, idx=None, draft=None, accepted=None,
+                               stream=None):
+    """verify_gemm_argmax with the library's static scratch: nothing is allocated, by the
+    library or here, so y (and idx, and accepted with draft) must be given.  With idx None
+    only y is computed.  Returns y, (y, idx) or (y, idx, accepted) like the allocating call."""
+    torch = _torch()
+    code = FORMATS[fmt]
+    M = _x(x)[0]
+    if y is None:
+        _bad(VG_ERR_ARG, "y must be given: this call allocates nothing")
+    if idx is not None:
+        _tensor(idx, "idx", (M,), (torch.int32,))
+    if (draft is None) != (accepted is None):
+        _bad(VG_ERR_ARG, "draft and accepted go together")
+    if draft is not None:
+        if idx is None:
+            _bad(VG_ERR_ARG, "draft needs idx")
+        _tensor(draft, "draft", (M,), (torch.int32,))
+        _tensor(accepted, "accepted", (1,), (torch.int32,))
+    M, K, N, y = _gemm_args(code, x, w, scales, biases, y)
+    _check_devices(x.device, idx=idx, draft=draft, accepted=accepted)
+    null = ctypes.c_void_p(0)
+    _check(lib().verify_gemm_argmax_noalloc(code, _ptr(x), _xdtype(x), M, K, _ptr(w), _ptr(scales),
+                                            null if biases is None else _ptr(biases), N, _ptr(y),
+                                            null if idx is None else _ptr(idx),
+                                            null if draft is None else _ptr(draft),
+                                            null if accepted is None else _ptr(accepted), _stream(stream)))
+    if idx is None:
+        return y
     return (y, idx) if draft is None else (y, idx, accepted)
 
 

@@ -196,17 +196,47 @@ vg_status release_workspace(hipStream_t stream) {
   return VG_OK;
 }
 
-vg_status run_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
-                     void* stream);
+// Where a call's workspace comes from: the stream's workspace above (created on first
+// use), or a fixed region given by the caller of run_gemm (the static scratch of
+// verify_gemm_argmax_noalloc), which is refused when the call needs more than it holds.
+struct Fixed {
+  size_t bytes;   // the static scratch's size; its address is looked up on first use
+};
 
+vg_status get_workspace(const Fixed* fixed, int dev, hipStream_t stream, size_t part_bytes, float** part,
+                        uint32_t** counters) {
+  if (!fixed) return workspace(dev, stream, part_bytes, part, counters);
+  if (kCounterBytes + part_bytes > fixed->bytes)
+    return fail(VG_ERR_UNSUPPORTED, "the call needs %zu bytes of scratch, above the static maximum of %zu",
+                kCounterBytes + part_bytes, fixed->bytes);
+  char* base = nullptr;
+  const hipError_t e = vg::static_scratch(dev, kCounterBytes, stream, &base);
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "static scratch set-up failed: %s", hipGetErrorString(e));
+  *counters = reinterpret_cast<uint32_t*>(base);
+  *part = reinterpret_cast<float*>(base + kCounterBytes);
+  return VG_OK;
+}
+
+// The argmax kernel's parked keys (bytes in the workspace's partial area).
+size_t argmax_key_bytes(int M, int N) { return (size_t)vg::argmax_chunks(N) * M * vg::ARG_KEY_BYTES; }
+
+vg_status launch_argmax_ws(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
+                           float* part, uint32_t* counters, hipStream_t st) {
+  const hipError_t e = vg::launch_argmax(y, M, N, idx, draft, accepted, reinterpret_cast<unsigned long long*>(part),
+                                         counters + kArgmaxCounterBase, st);
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return VG_OK;
+}
 
 // The verify GEMM; with idx non-null also the argmax of every row (and the accepted prefix
 // when draft is non-null): fused into the GEMM's epilogue when the plan runs the MFMA
 // kernels with one K slice, else the argmax kernel after it (same results either way).
+// Everything the call needs (split-K partials, counters, argmax keys) is acquired before
+// the first launch, so a refused call enqueues nothing.
 vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint32_t* w,
                    const uint16_t* scales, const uint16_t* biases, int N, float* y, void* stream,
                    int had_block = 128, const uint32_t* signs = nullptr, int32_t* idx = nullptr,
-                   const int32_t* draft = nullptr, int32_t* accepted = nullptr) {
+                   const int32_t* draft = nullptr, int32_t* accepted = nullptr, const Fixed* fixed = nullptr) {
   std::call_once(g_env_once, read_env);
   vg::DeviceInfo dev;
   if (vg_status s = device_info(&dev)) return s;
@@ -219,34 +249,38 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   }
   vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, static_cast<hipStream_t>(stream),
                  had_block, signs};
-  hipError_t e;
-  bool fused = false;
-  if (var == vg::VAR_VALU) {
-    e = vg::launch_valu(c, dev);
-  } else {
-    vg::MfmaPlan p;
+  vg::MfmaPlan p{};
+  if (var != vg::VAR_VALU) {
     if (!vg::plan_mfma(fmt, var, M, K, N, dev, g_forced_ks, &p))
       return fail(VG_ERR_UNSUPPORTED, "M=%d K=%d does not fit the MFMA staging", M, K);
-    float* part = nullptr;
-    uint32_t* counters = nullptr;
-    if (p.ks > 1) {
-      if (p.rg > vg::MAX_SPLIT_ROW_GROUPS) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
-      if (vg_status s = workspace(dev.id, c.stream, vg::mfma_workspace_bytes(M, N, p), &part, &counters)) return s;
-    } else if (idx) {
-      if (vg_status s = workspace(dev.id, c.stream, 0, &part, &counters)) return s;
-      part = nullptr;
-      c.idx = idx;
-      c.draft = draft;
-      c.accepted = accepted;
-      c.amax_key = reinterpret_cast<unsigned long long*>(counters + kFusedKeyBase);
-      c.amax_count = counters + kFusedCountIndex;
-      counters = nullptr;
-      fused = true;
-    }
-    e = vg::launch_mfma(c, var, p, part, counters, dev);
+    if (p.ks > 1 && p.rg > vg::MAX_SPLIT_ROW_GROUPS) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
+  }
+  const bool split = var != vg::VAR_VALU && p.ks > 1;
+  const bool fused = idx && var != vg::VAR_VALU && !split;
+  const bool argmax_after = idx && !fused;
+  float* part = nullptr;
+  uint32_t* counters = nullptr;
+  if (split || idx) {
+    size_t part_bytes = split ? vg::mfma_workspace_bytes(M, N, p) : 0;
+    if (argmax_after && argmax_key_bytes(M, N) > part_bytes) part_bytes = argmax_key_bytes(M, N);
+    if (vg_status s = get_workspace(fixed, dev.id, c.stream, part_bytes, &part, &counters)) return s;
+  }
+  hipError_t e;
+  if (var == vg::VAR_VALU) {
+    e = vg::launch_valu(c, dev);
+  } else if (fused) {
+    c.idx = idx;
+    c.draft = draft;
+    c.accepted = accepted;
+    c.amax_key = reinterpret_cast<unsigned long long*>(counters + kFusedKeyBase);
+    c.amax_count = counters + kFusedCountIndex;
+    e = vg::launch_mfma(c, var, p, nullptr, nullptr, dev);
+  } else {
+    e = vg::launch_mfma(c, var, p, split ? part : nullptr, split ? counters : nullptr, dev);
   }
   if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  if (idx && !fused) return run_argmax(y, M, N, idx, draft, accepted, stream);
+  if (argmax_after)
+    if (vg_status s = launch_argmax_ws(y, M, N, idx, draft, accepted, part, counters, c.stream)) return s;
   g_err[0] = '\0';
   return VG_OK;
 }
@@ -309,13 +343,10 @@ vg_status run_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* 
   vg::DeviceInfo dev;
   if (vg_status s = device_info(&dev)) return s;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const size_t parts = (size_t)vg::argmax_chunks(N) * M;
   float* part = nullptr;
   uint32_t* counters = nullptr;
-  if (vg_status s = workspace(dev.id, st, parts * vg::ARG_KEY_BYTES, &part, &counters)) return s;
-  const hipError_t e = vg::launch_argmax(y, M, N, idx, draft, accepted, reinterpret_cast<unsigned long long*>(part),
-                                         counters + kArgmaxCounterBase, st);
-  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  if (vg_status s = workspace(dev.id, st, argmax_key_bytes(M, N), &part, &counters)) return s;
+  if (vg_status s = launch_argmax_ws(y, M, N, idx, draft, accepted, part, counters, st)) return s;
   g_err[0] = '\0';
   return VG_OK;
 }
@@ -417,6 +448,27 @@ vg_status verify_gemm_argmax(int format, const void* x, int x_dtype, int M, int 
   if ((draft == nullptr) != (accepted == nullptr)) return fail(VG_ERR_ARG, "draft and accepted go together");
   return run_gemm(format, x, x_dtype, M, K, w, scales, format == vg::SIGN1 ? nullptr : biases, N, y, stream, 128,
                   nullptr, idx, draft, accepted);
+}
+
+vg_status verify_gemm_argmax_noalloc(int format, const void* x, int x_dtype, int M, int K, const uint32_t* w,
+                                     const uint16_t* scales, const uint16_t* biases, int N, float* y,
+                                     int32_t* idx, const int32_t* draft, int32_t* accepted, void* stream) {
+  if (format != vg::SIGN1 && format != vg::AFFINE2 && format != vg::HAD2 && format != vg::AFFINE1)
+    return fail(VG_ERR_ARG, "unknown format %d", format);
+  if (vg_status s = check_common(x, x_dtype, M, K, N)) return s;
+  const int G = vg::fmt_one_bit(format) || format == vg::HAD2 ? 128 : 64;
+  if (K % G != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of %d", K, G);
+  if (vg_status s = check_ptr(w, "w")) return s;
+  if (vg_status s = check_ptr(scales, "scales")) return s;
+  if (format != vg::SIGN1)
+    if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_ptr(y, "y")) return s;
+  if (idx && (reinterpret_cast<uintptr_t>(idx) & 3u)) return fail(VG_ERR_ALIGN, "idx is not 4-byte aligned");
+  if ((draft == nullptr) != (accepted == nullptr)) return fail(VG_ERR_ARG, "draft and accepted go together");
+  if (draft && !idx) return fail(VG_ERR_ARG, "draft needs idx");
+  const Fixed fixed{vg::STATIC_SCRATCH_BYTES};
+  return run_gemm(format, x, x_dtype, M, K, w, scales, format == vg::SIGN1 ? nullptr : biases, N, y, stream, 128,
+                  nullptr, idx, draft, accepted, &fixed);
 }
 
 vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* stream) {

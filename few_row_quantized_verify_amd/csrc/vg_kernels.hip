@@ -35,6 +35,7 @@
 //   * The output-head epilogue (verify_gemm_argmax, one K slice): every row's argmax over
 //     the workgroups' columns as one 64-bit maximum per row (fused_argmax).
 #include <atomic>
+#include <mutex>
 
 #include "vg_device.h"
 #include "vg_launch.h"
@@ -1435,6 +1436,43 @@ hipError_t launch_debug_decode(int fmt, int xt, const uint32_t* w, int N, int K,
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Static scratch of the allocation-free entry point (verify_gemm_argmax_noalloc): the
+// split-K partials, arrival counters and argmax keys of a call in a fixed device array,
+// one copy per GPU the library runs on, held until the process ends.  In host code the
+// array's name is a host-side stand-in, not a device address: its address on a device is
+// taken once per device with hipGetSymbolAddress (that device current), and only that
+// address reaches kernels.  Calls on one GPU share the array, so calls that overlap on one
+// GPU race; the kernels leave the counters zero for the next call.
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void vg_clear_words(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) p[i] = 0u;
+}
+
+hipError_t static_scratch(int dev, size_t clear_bytes, hipStream_t s, char** out) {
+  static std::mutex mu;
+  static char* ptr[64] = {};
+  if (dev < 0 || dev >= 64 || clear_bytes > STATIC_SCRATCH_BYTES || clear_bytes % 4) return hipErrorInvalidValue;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    // The counters must read zero before the first call.  The array is zero when the code
+    // object loads and every call leaves its counters zero; they are cleared once here
+    // regardless, by a kernel (no memset node, should the first call be captured).
+    hipLaunchKernelGGL(vg_clear_words, dim3(64), dim3(256), 0, s, static_cast<uint32_t*>(p),
+                       (uint32_t)(clear_bytes / 4));
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    ptr[dev] = static_cast<char*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace vg

@@ -95,6 +95,12 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int
 // Codes of packed words as one byte per weight [N, K], decoded with the GEMM's register
 // extraction for (fmt, xt) (xt F16 or BF16: the 1-bit formats decode to bf16 against bf16
 // activations); 0xFF marks a half that is not an exact code.
+// Static scratch of the allocation-free entry point: STATIC_SCRATCH_BYTES of device memory
+// per GPU.  static_scratch returns its address on device `dev` (the current device), taken
+// with hipGetSymbolAddress on the first call for that device, which also clears its first
+// clear_bytes (the counter area) with a kernel on stream s.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)4 << 20;
+hipError_t static_scratch(int dev, size_t clear_bytes, hipStream_t s, char** ptr);
 hipError_t launch_debug_decode(int fmt, int xt, const uint32_t* w, int N, int K, uint8_t* codes,
                                hipStream_t s);
 

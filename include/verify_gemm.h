@@ -191,6 +191,29 @@ vg_status verify_gemm_argmax(int format, const void* x, int x_dtype, int M, int 
                              const int32_t* draft, int32_t* accepted, void* stream);
 
 /*
+ * verify_gemm_argmax for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, same
+ * kernels and plan, so y, idx and accepted are bit for bit those of verify_gemm_argmax;
+ * with idx NULL (and draft, accepted NULL) only y is computed, bit for bit the plain
+ * verify_gemm_<format> call.  Differences:
+ *   - The call's scratch (split-K partial outputs, arrival counters, argmax keys) lives in
+ *     a static device array of 4 MiB per GPU, held until the process ends, instead of a
+ *     per-stream workspace.  A call that needs more -- 116736 bytes of counters plus the
+ *     larger of (K slices) * M * N * 4 bytes of partials (vg_plan_ksplit; none when 1) and,
+ *     when the argmax runs as its own kernel after the GEMM, 128 * M * ceil(N / 2048)
+ *     bytes of keys -- is refused with VG_ERR_UNSUPPORTED before anything is enqueued.
+ *   - Nothing is allocated and no memset is enqueued.  The first call on a device that
+ *     uses the array looks up its address and enqueues one small kernel that clears its
+ *     counters; every call leaves them zero for the next.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ *     other streams, or graph replays running beside them) race and give wrong results,
+ *     so order them.
+ */
+vg_status verify_gemm_argmax_noalloc(int format, const void* x, int x_dtype, int M, int K, const uint32_t* w,
+                                     const uint16_t* scales, const uint16_t* biases, int N, float* y,
+                                     int32_t* idx, const int32_t* draft, int32_t* accepted, void* stream);
+
+/*
  * Greedy acceptance of a drafted block: idx[m] = argmax_n y[m, n] as verify_argmax_rows,
  * and accepted[0] = the number of leading rows m with idx[m] == draft[m] (0..M), i.e. the
  * length of the drafted prefix the target model agrees with; when it is below M,
