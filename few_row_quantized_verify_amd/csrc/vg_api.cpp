@@ -98,6 +98,10 @@ int plan(int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev) {
 bool variant_supports(int var, int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev) {
   if (var == vg::VAR_VALU) return true;
   if (xt == VG_F32 || K % kstep_of(fmt) != 0) return false;
+  if (var == vg::VAR_GEMV) {
+    vg::MfmaPlan p;
+    return vg::plan_gemv(fmt, M, K, N, dev, &p);
+  }
   if (var == vg::VAR_MFMA_Q && M > 4) return false;
   vg::MfmaPlan p;
   return vg::plan_mfma(fmt, var, M, K, N, dev, g_forced_ks, &p);
@@ -250,13 +254,17 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, static_cast<hipStream_t>(stream),
                  had_block, signs};
   vg::MfmaPlan p{};
-  if (var != vg::VAR_VALU) {
+  const bool mfma = var == vg::VAR_MFMA_Q || var == vg::VAR_MFMA_H;
+  if (mfma) {
     if (!vg::plan_mfma(fmt, var, M, K, N, dev, g_forced_ks, &p))
       return fail(VG_ERR_UNSUPPORTED, "M=%d K=%d does not fit the MFMA staging", M, K);
     if (p.ks > 1 && p.rg > vg::MAX_SPLIT_ROW_GROUPS) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
+  } else if (var == vg::VAR_GEMV) {
+    if (!vg::plan_gemv(fmt, M, K, N, dev, &p))
+      return fail(VG_ERR_UNSUPPORTED, "M=%d K=%d does not fit the dot2 kernel's staging", M, K);
   }
-  const bool split = var != vg::VAR_VALU && p.ks > 1;
-  const bool fused = idx && var != vg::VAR_VALU && !split;
+  const bool split = mfma && p.ks > 1;
+  const bool fused = idx && mfma && !split;
   const bool argmax_after = idx && !fused;
   float* part = nullptr;
   uint32_t* counters = nullptr;
@@ -268,6 +276,8 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   hipError_t e;
   if (var == vg::VAR_VALU) {
     e = vg::launch_valu(c, dev);
+  } else if (var == vg::VAR_GEMV) {
+    e = vg::launch_gemv(c, p, dev);
   } else if (fused) {
     c.idx = idx;
     c.draft = draft;
@@ -512,6 +522,7 @@ const char* vg_variant_name(int variant) {
     case vg::VAR_MFMA_Q: return "vg_mfma_q";
     case vg::VAR_MFMA_H: return "vg_mfma_h";
     case vg::VAR_VALU: return "vg_valu";
+    case vg::VAR_GEMV: return "vg_gemv";
     default: return "";
   }
 }
@@ -534,7 +545,7 @@ vg_status vg_force_ksplit(int ksplit) {
 int vg_plan_ksplit(int format, int x_dtype, int M, int N, int K) {
   const int var = vg_plan_variant(format, x_dtype, M, N, K);
   if (var < 0) return -1;
-  if (var == vg::VAR_VALU) return 1;
+  if (var == vg::VAR_VALU || var == vg::VAR_GEMV) return 1;
   vg::DeviceInfo dev;
   if (device_info(&dev) != VG_OK) return -1;
   vg::MfmaPlan p;

@@ -911,7 +911,7 @@ __device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, 
   if (A.accepted) A.accepted[0] = agreed;
 }
 
-template <int FMT, int MODE, int XT, int PREF, bool AMASK>
+template <int FMT, int MODE, int XT, int PREF, bool AMASK, int EARLY>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, GPS = 4 * GL;
@@ -1036,12 +1036,25 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       }
     };
 
-    // Activations are staged before any weight load is issued: loads leave a CU in order
-    // and a wave stalls at issue once the memory queues are full, so weight loads issued
-    // first would hold back the staging (and every MFMA after it) by the whole burst.
+    // The activation loads go first: loads leave a CU in order, so weight loads ahead of
+    // them would hold back the staging (and every MFMA after it) by the whole burst.  With
+    // EARLY the wave's first PREF units are issued right behind them, so the weight stream
+    // runs while the activations arrive and are staged; the issue is unconditional (a wave
+    // with fewer units re-loads its last one, in bounds), so the wait for the activations
+    // counts exactly the loads issued after them.
     XStage xs;
     stage_load<XT>(A, M, xmap, ws0 * KSTEP, ns * KSTEP, xs);
+    Unit<FMT> ring[PREF];
+    if constexpr (EARLY == 1) {
+#pragma unroll
+      for (int d = 0; d < PREF; ++d) issue(ring[d]);
+    }
     lds_barrier();  // previous window's readers are done with the LDS
+    if constexpr (EARLY == 2) {
+      // behind every wave's activation loads (the barrier), ahead of the staging
+#pragma unroll
+      for (int d = 0; d < PREF; ++d) issue(ring[d]);
+    }
     // The tiles split between waves in this window, for the reduction after it: wave
     // boundary bw (lanes 0..NW-2 of wave 0) records, when it falls strictly inside a tile
     // and is that tile's first such boundary, the tile, the waves whose unit range meets
@@ -1070,10 +1083,11 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       reinterpret_cast<uint32_t*>(smem + L.red_off)[lane] = rec;
     }
     stage_compute<FMT, XT>(A, M, smem, L, ws0 * KSTEP, ns * KSTEP, xs);
-    Unit<FMT> ring[PREF];
+    if constexpr (EARLY == 0) {
 #pragma unroll
-    for (int d = 0; d < PREF; ++d)
-      if (d < nu) issue(ring[d]);
+      for (int d = 0; d < PREF; ++d)
+        if (d < nu) issue(ring[d]);
+    }
     lds_barrier();
 
     // The waves carrying one unit more than the others finish last; giving them issue
@@ -1188,16 +1202,294 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   if (tid == 0) __hip_atomic_store(A.counters + rgi * SPLIT_CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------------------
+// vg_gemv: the verify GEMM on the vector ALUs for one or two rows, with the activations
+// held in registers.  Wave w of a workgroup owns K-step w (1024 columns); lane (rho, gam)
+// owns the 64 columns gam*64.. of that step and output row rho of each 4-row block, so a
+// wave's load instruction reads 4 rows x 256 contiguous bytes (2-bit) or 4 x 128 (1-bit)
+// and every lane multiplies its own 64 activations, loaded once per call and kept in
+// registers as the operand pairs the register decode produces (no activation staging
+// through LDS).  Each lane also forms its own offset sum (sum of a * BETA, plus the group
+// sum for affine codes) from those registers.  Products are v_dot2 into fp32 (fp16, or
+// bf16 for 1-bit codes against bf16 rows); bf16 rows against 2-bit codes and rotated rows
+// are scaled by a power of two per row into fp16 as in the MFMA kernels (the row maximum
+// over the whole K comes from all waves of the workgroup), and the rotation runs in
+// registers (a 64-point transform per lane, then lane pairs for blocks of 128 and 256).
+// The 16 lanes of a row are added in a fixed order (xor 1, 2, 4, 8), and the K-steps'
+// partials of a row through LDS in step order, so results do not depend on timing.
+constexpr int GV_RPW = 4;     // output rows per wave instruction (16 lanes each)
+constexpr int GV_MAXS = 16;   // K-steps (waves) per workgroup: K <= 16384
+
+template <int CTRL>
+__device__ __forceinline__ float gv_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+template <int FMT, int XT, int MM, int PREF>
+__global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
+  using F = Fmt<FMT>;
+  constexpr bool ONE = F::ONE_BIT;
+  constexpr bool HAD = FMT == HAD2;
+  constexpr bool NORM = x_rescaled(FMT, XT);
+  constexpr bool BF = bf16_codes(FMT, XT);
+  constexpr int NMK = BF ? 8 : 6;
+  constexpr int NWORD = ONE ? 2 : 4;      // code words per lane and unit (64 codes)
+  constexpr int HALF = F::WORD_K / 2;     // operand pairs per word
+  constexpr float SCALE_MUL = FMT == AFFINE1 ? 0.5f : 1.0f;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* rowmax = reinterpret_cast<float*>(smem);          // [MAXM]
+  float* part = reinterpret_cast<float*>(smem) + 2 * MAXM; // [blocks][4][S][MM]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int st = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = (int)(blockDim.x >> 6);
+  const int rho = lane >> 4, gam = lane & 15;
+  const int kl = st * KSTEP + gam * 64;   // the lane's first column
+  uint32_t mk[NMK], mg[NMK];
+#pragma unroll
+  for (int k = 0; k < NMK; ++k) {
+    mk[k] = A.mask[k];
+    asm volatile("v_mov_b32 %0, %1" : "=v"(mg[k]) : "s"(A.magic[k]));
+  }
+
+  // ---- the lane's activations: 64 columns of each row, raw 16-bit values, loaded one row
+  // at a time (a first pass finds the row maxima when the rows are rescaled)
+  auto load_row = [&](int m, u32x4 (&xr)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      xr[q] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.x) + (size_t)m * A.K + kl + 8 * q);
+  };
+  float f[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) f[m] = 1.0f;
+  if constexpr (NORM) {
+    // per-row power of two from the row's largest magnitude over the whole K
+    if (tid < MAXM) rowmax[tid] = 0.0f;
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      u32x4 xr[8];
+      load_row(m, xr);
+      u16x2 mx2 = {0, 0};
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, xr[q][e] & 0x7FFF7FFFu));
+      float mx = half_bits_to_f32<XT>(mx2[0] > mx2[1] ? mx2[0] : mx2[1]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      if (lane == 0) atomicMax(reinterpret_cast<uint32_t*>(rowmax) + m, __float_as_uint(mx));
+    }
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const float mx = rowmax[m];
+      if (mx > 0.0f && mx == mx) {
+        int ex = 0;
+        frexpf(mx, &ex);
+        int e = 14 - ex - (HAD ? 4 : 0);
+        e = e < -120 ? -120 : (e > 120 ? 120 : e);
+        f[m] = ldexpf(1.0f, e);
+      }
+    }
+  }
+
+  // ---- operand pairs: pair P = wi * HALF + j is (x[WORD_K wi + j], x[WORD_K wi + j + HALF])
+  uint32_t xp[MM][32];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+    u32x4 xr[8];
+    load_row(m, xr);
+    auto raw = [&](int a) -> uint32_t { return xr[a >> 3][(a >> 1) & 3]; };   // dword holding column a
+    if constexpr (HAD) {
+      float v[64];
+#pragma unroll
+      for (int a = 0; a < 64; ++a) {
+        const uint32_t d = raw(a);
+        v[a] = half_bits_to_f32<XT>((a & 1) ? (d >> 16) : (d & 0xFFFFu));
+      }
+      if (A.signs) {
+        const uint32_t s0 = A.signs[kl >> 5], s1 = A.signs[(kl >> 5) + 1];
+#pragma unroll
+        for (int a = 0; a < 64; ++a) {
+          const uint32_t bit = ((a < 32 ? s0 : s1) >> (a & 31)) & 1u;
+          v[a] = __uint_as_float(__float_as_uint(v[a]) ^ (bit << 31));
+        }
+      }
+#pragma unroll
+      for (int h = 1; h < 64; h <<= 1)
+#pragma unroll
+        for (int a = 0; a < 64; ++a)
+          if ((a & h) == 0) {
+            const float p0 = v[a], p1 = v[a + h];
+            v[a] = p0 + p1;
+            v[a + h] = p0 - p1;
+          }
+      // blocks of 128 and 256 span lane pairs (gam ^ 1) and quads (gam ^ 2); each stage
+      // leaves the upper lane's results negated, undone by the lane's final sign
+      const int cross = A.had_stages - 1;
+      if (cross >= 1) {
+        const float c1 = (gam & 1) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int a = 0; a < 64; ++a) v[a] = __builtin_fmaf(c1, gv_dpp<0xB1>(v[a]), v[a]);
+      }
+      if (cross >= 2) {
+        const float c2 = (gam & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int a = 0; a < 64; ++a) v[a] = __builtin_fmaf(c2, gv_dpp<0x4E>(v[a]), v[a]);
+      }
+      const float sg = (__builtin_popcount(gam & ((1 << (cross > 0 ? cross : 0)) - 1)) & 1) ? -1.0f : 1.0f;
+      const float sc = sg * A.had_scale * f[m];
+#pragma unroll
+      for (int wi = 0; wi < NWORD; ++wi)
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) {
+          const int a = F::WORD_K * wi + j;
+          xp[m][wi * HALF + j] = f32_to_f16_bits(v[a] * sc) | (f32_to_f16_bits(v[a + HALF] * sc) << 16);
+        }
+    } else {
+#pragma unroll
+      for (int wi = 0; wi < NWORD; ++wi)
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) {
+          const int a = F::WORD_K * wi + j, b = a + HALF;
+          const uint32_t da = raw(a), db = raw(b);
+          if constexpr (NORM) {
+            const float fa = __uint_as_float((a & 1) ? (da & 0xFFFF0000u) : (da << 16));
+            const float fb = __uint_as_float((b & 1) ? (db & 0xFFFF0000u) : (db << 16));
+            xp[m][wi * HALF + j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fa * f[m], fb * f[m]));
+          } else {
+            xp[m][wi * HALF + j] = __builtin_amdgcn_perm(db, da, (a & 1) ? 0x07060302u : 0x05040100u);
+          }
+        }
+    }
+  }
+  // ---- the lane's offset and group sums from the same operand values
+  float off[MM], xs[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+    float e = 0.0f, t = 0.0f;
+#pragma unroll
+    for (int P = 0; P < NWORD * HALF; ++P) {
+      const int j = P % HALF;
+      if constexpr (BF) {
+        const __bf16 cb = (__bf16)sign1_beta_bf16(j), one = (__bf16)1.0f;
+        e = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xp[m][P]), bf16x2{cb, cb}, e, false);
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xp[m][P]), bf16x2{one, one}, t, false);
+      } else {
+        const float beta = ONE ? sign1_beta(j) : affine2_beta(j);
+        const _Float16 cf = (_Float16)beta;
+        e = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, xp[m][P]), f16x2{cf, cf}, e, false);
+        t = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, xp[m][P]), f16x2{(_Float16)1.0f, (_Float16)1.0f}, t, false);
+      }
+    }
+    // sign bits decode to BETA + 1 + sign: the offset is sum a (BETA + 1); the affine
+    // codes' is sum a BETA
+    off[m] = FMT == SIGN1 ? -(e + t) : -e;
+    xs[m] = t;
+  }
+
+  // ---- the weight stream: this wave's K-step of the workgroup's 4-row blocks
+  const int RB = (A.N + GV_RPW - 1) / GV_RPW;
+  const int b0 = (int)(((long long)RB * blockIdx.x) / gridDim.x);
+  const int b1 = (int)(((long long)RB * (blockIdx.x + 1)) / gridDim.x);
+  const int nb = b1 - b0;
+  const uint32_t wrow = (uint32_t)(A.K / F::WORD_K) * 4u;
+  const uint32_t srow = (uint32_t)(A.K / F::G) * 2u;
+  const uint32_t woff = (uint32_t)kl / (ONE ? 8u : 4u);   // the lane's code bytes within a row
+  const uint32_t soff = (uint32_t)(kl / F::G) * 2u;         // its group's scale within a row
+  const char* wq = reinterpret_cast<const char*>(A.w);
+  const char* sc = reinterpret_cast<const char*>(A.scales);
+  const char* bi = reinterpret_cast<const char*>(A.biases);
+  struct GUnit {
+    uint32_t w[NWORD];
+    uint32_t s, b;
+  };
+  auto issue = [&](int k, GUnit& R) {
+    const int blk = b0 + min(k, nb - 1);
+    const int row = min(blk * GV_RPW + rho, A.N - 1);
+    const char* p = wq + (size_t)row * wrow + woff;
+    if constexpr (ONE) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      R.w[0] = v.x;
+      R.w[1] = v.y;
+    } else {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R.w[i] = v[i];
+    }
+    R.s = *reinterpret_cast<const uint16_t*>(sc + (size_t)row * srow + soff);
+    if constexpr (F::AFFINE) R.b = *reinterpret_cast<const uint16_t*>(bi + (size_t)row * srow + soff);
+  };
+  GUnit ring[PREF];
+  if (nb > 0) {
+#pragma unroll
+    for (int d = 0; d < PREF; ++d) issue(d, ring[d]);
+  }
+  for (int base = 0; base < nb; base += PREF) {
+#pragma unroll
+    for (int d = 0; d < PREF; ++d) {
+      const int k = base + d;
+      if (k < nb) {
+        const GUnit R = ring[d];
+        if (k + PREF < nb) issue(k + PREF, ring[d]);
+        float dot[MM];
+#pragma unroll
+        for (int m = 0; m < MM; ++m) dot[m] = off[m];
+#pragma unroll
+        for (int wi = 0; wi < NWORD; ++wi) {
+          uint32_t pw[HALF];
+          unpack_word_rt<FMT, BF>(R.w[wi], pw, mk, mg);
+#pragma unroll
+          for (int m = 0; m < MM; ++m)
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) {
+              if constexpr (BF)
+                dot[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[j]),
+                                                         __builtin_bit_cast(bf16x2, xp[m][wi * HALF + j]), dot[m], false);
+              else
+                dot[m] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[j]),
+                                                __builtin_bit_cast(f16x2, xp[m][wi * HALF + j]), dot[m], false);
+            }
+        }
+        const float s_ = half_of(R.s, 0) * SCALE_MUL;
+        const float b_ = F::AFFINE ? half_of(R.b, 0) : 0.0f;
+        float y[MM];
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+          y[m] = __builtin_fmaf(s_, dot[m], b_ * xs[m]);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) y[m] += __shfl_xor(y[m], o);
+        }
+        if (gam == 0) {
+#pragma unroll
+          for (int m = 0; m < MM; ++m) part[((k * GV_RPW + rho) * S + st) * MM + m] = y[m];
+        }
+      }
+    }
+  }
+  lds_barrier();
+  // ---- each row's K-steps added in step order
+  for (int e = tid; e < nb * GV_RPW * MM; e += blockDim.x) {
+    const int rl = e / MM, m = e - rl * MM;
+    const int row = b0 * GV_RPW + rl;
+    if (row < A.N) {
+      float sum = 0.0f;
+      for (int t = 0; t < S; ++t) sum += part[(rl * S + t) * MM + m];
+      A.y[(size_t)m * A.N + row] = sum / f[m];
+    }
+  }
+}
+
 // The kernel names carry the variant name, so a trace shows which variant ran.
-template <int FMT, int XT, int PREF>
+template <int FMT, int XT, int PREF, int EARLY>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_q(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false>(A, smem);
+  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY>(A, smem);
 }
-template <int FMT, int XT, int PREF, bool AMASK>
+template <int FMT, int XT, int PREF, bool AMASK, int EARLY>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK>(A, smem);
+  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY>(A, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1328,20 +1620,21 @@ static hipError_t allow_lds(void (*kern)(MfmaArgs), std::atomic<uint64_t>& done,
   return e;
 }
 
-template <int FMT, int MODE, int XT, int PREF>
+template <int FMT, int MODE, int XT, int PREF, int EARLY>
 static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t stream, const DeviceInfo& dev) {
   // 1-bit codes at 8 rows: the A-operand reads of the lanes without a drafted row are
   // masked off (AMASK).  With the zero row those reads carry 4 * 8 + 4 distinct addresses,
   // one more LDS pass per read than the 32 of the drafted rows; the masking costs three
   // scalar instructions per read group, which pays at 8 rows only (measured on MI355X).
   constexpr bool MASKABLE = MODE == VAR_MFMA_H && fmt_one_bit(FMT);
-  void (*kern)(MfmaArgs) = MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT, PREF> : vg_mfma_h<FMT, XT, PREF, false>;
+  void (*kern)(MfmaArgs) =
+      MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT, PREF, EARLY> : vg_mfma_h<FMT, XT, PREF, false, EARLY>;
   static std::atomic<uint64_t> attr_done{0};
   static std::atomic<uint64_t> attr_done_mask{0};
   std::atomic<uint64_t>* done = &attr_done;
   if constexpr (MASKABLE) {
     if (A.M == 8) {
-      kern = vg_mfma_h<FMT, XT, PREF, true>;
+      kern = vg_mfma_h<FMT, XT, PREF, true, EARLY>;
       done = &attr_done_mask;
     }
   }
@@ -1385,8 +1678,8 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
   A.signs = c.signs;
   decode_consts(FMT, XT, A.mask, A.magic);
-  if constexpr (fmt_one_bit(FMT)) return launch_kern<FMT, MODE, XT, 2>(A, p, c.stream, dev);
-  else return launch_kern<FMT, MODE, XT, 1>(A, p, c.stream, dev);
+  if constexpr (fmt_one_bit(FMT)) return launch_kern<FMT, MODE, XT, 2, 0>(A, p, c.stream, dev);
+  else return launch_kern<FMT, MODE, XT, 1, 0>(A, p, c.stream, dev);
 }
 
 hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float* part, uint32_t* counters,
@@ -1409,6 +1702,73 @@ hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float*
   }
 #undef VG_DISPATCH_MODE
 #undef VG_DISPATCH_XT
+}
+
+// The dot2 kernel: one wave per 1024-wide K-step (K <= 16384), rows one or two (one for the
+// rotated format, whose transform needs the registers); enough
+// workgroups for about 20 waves per CU, each a balanced range of 4-row blocks whose
+// per-step partials fit the LDS.
+bool plan_gemv(int fmt, int M, int K, int N, const DeviceInfo& dev, MfmaPlan* p) {
+  if (M < 1 || M > (fmt == HAD2 ? 1 : 2) || K % KSTEP != 0 || N < 1) return false;
+  const int S = K / KSTEP;
+  if (S > GV_MAXS) return false;
+  const int rb = (N + GV_RPW - 1) / GV_RPW;
+  int grid = (dev.cu_count * 20 + S - 1) / S;
+  if (grid > rb) grid = rb;
+  const int nb_max = (rb + grid - 1) / grid;
+  const size_t lds = (size_t)2 * MAXM * 4 + (size_t)nb_max * GV_RPW * S * M * 4;
+  if (lds > (size_t)dev.max_lds) return false;
+  p->grid = grid;
+  p->rg = grid;
+  p->ks = 1;
+  p->win_steps = S;
+  p->tiles_max = 0;
+  p->pref = 3;
+  p->lds = lds;
+  return true;
+}
+
+template <int FMT, int XT, int MM>
+static hipError_t launch_gemv_m(const MfmaArgs& A, const MfmaPlan& p, hipStream_t stream, const DeviceInfo& dev) {
+  void (*kern)(MfmaArgs) = vg_gemv<FMT, XT, MM, 3>;
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t e = allow_lds(kern, attr_done, dev);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * p.win_steps), p.lds, stream, A);
+  return hipGetLastError();
+}
+
+template <int FMT, int XT>
+static hipError_t launch_gemv_x(const GemmCall& c, const MfmaPlan& p, const DeviceInfo& dev) {
+  MfmaArgs A{};
+  A.x = c.x; A.w = c.w; A.scales = c.scales; A.biases = c.biases; A.y = c.y;
+  A.M = c.M; A.K = c.K; A.N = c.N;
+  A.had_stages = c.had_block == 64 ? 1 : (c.had_block == 256 ? 3 : 2);
+  A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
+  A.signs = c.signs;
+  decode_consts(FMT, XT, A.mask, A.magic);
+  if (c.M == 1) return launch_gemv_m<FMT, XT, 1>(A, p, c.stream, dev);
+  if constexpr (FMT != HAD2) {   // two rotated rows do not fit the kernel's registers
+    if (c.M == 2) return launch_gemv_m<FMT, XT, 2>(A, p, c.stream, dev);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(const GemmCall& c, const MfmaPlan& p, const DeviceInfo& dev) {
+#define VG_GEMV_XT(FMT)                                                  \
+  switch (c.xt) {                                                        \
+    case XF16: return launch_gemv_x<FMT, XF16>(c, p, dev);               \
+    case XBF16: return launch_gemv_x<FMT, XBF16>(c, p, dev);             \
+    default: return hipErrorInvalidValue;                                \
+  }
+  switch (c.fmt) {
+    case SIGN1: VG_GEMV_XT(SIGN1)
+    case AFFINE2: VG_GEMV_XT(AFFINE2)
+    case HAD2: VG_GEMV_XT(HAD2)
+    case AFFINE1: VG_GEMV_XT(AFFINE1)
+    default: return hipErrorInvalidValue;
+  }
+#undef VG_GEMV_XT
 }
 
 hipError_t launch_debug_decode(int fmt, int xt, const uint32_t* w, int N, int K, uint8_t* codes, hipStream_t s) {

@@ -11,7 +11,8 @@ enum Variant : int {
   VAR_MFMA_Q = 0,   // MFMA 16x16x32 f16, 16 rows = 4 row-blocks of 4 (M <= 4)
   VAR_MFMA_H = 1,   // MFMA 16x16x32 f16, 16 rows = 2 row-blocks of 8 (M <= 8)
   VAR_VALU = 2,     // plain fp32 VALU kernel (any dtype, any M; fp32 activations)
-  VAR_COUNT = 3
+  VAR_GEMV = 3,     // fp16/bf16 dot2 VALU kernel, M <= 2, activations in registers
+  VAR_COUNT = 4
 };
 
 // Split-K arrival counters in the workspace: one per row group (at most 768), each on its
@@ -68,6 +69,10 @@ bool plan_mfma(int fmt, int variant, int M, int K, int N, const DeviceInfo& dev,
                MfmaPlan* p);
 // Plans a grouped expert verify of up to `jobs` jobs of at most M rows each (one K slice).
 bool plan_mfma_grouped(int fmt, int M, int K, int N, int jobs, const DeviceInfo& dev, MfmaPlan* p);
+// Plans the VALU dot2 kernel (vg_gemv): false when the call does not fit it (M > 2, K not a
+// multiple of 1024 or above 16384, or the per-step partials do not fit the LDS).
+bool plan_gemv(int fmt, int M, int K, int N, const DeviceInfo& dev, MfmaPlan* p);
+hipError_t launch_gemv(const GemmCall& c, const MfmaPlan& p, const DeviceInfo& dev);
 // Device workspace a planned call needs (partial outputs; 0 when K is not split).
 size_t mfma_workspace_bytes(int M, int N, const MfmaPlan& p);
 

@@ -105,7 +105,7 @@ def test_debug_unpack_validation():
 
 def test_variants_and_forcing():
     names = [vgm.variant_name(i) for i in range(vgm.variant_count())]
-    assert names == ["vg_mfma_q", "vg_mfma_h", "vg_valu"]
+    assert names == ["vg_mfma_q", "vg_mfma_h", "vg_valu", "vg_gemv"]
     assert vgm.variant_name(99) == ""
     with pytest.raises(vgm.VerifyGemmError) as e:
         vgm.force_variant(99)

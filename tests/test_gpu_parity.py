@@ -182,6 +182,44 @@ def test_every_variant(vg, fmt, K, N):
         vg.force_variant(-1)
 
 
+GEMV = 3
+
+
+@pytest.mark.parametrize("fmt", ["sign1", "affine2", "had2", "affine1"])
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("K,N", [(1024, 1), (1024, 13), (2048, 100), (3072, 517), (5120, 4099), (16384, 77)])
+def test_gemv_every_row_count(vg, fmt, K, N, x_dtype):
+    """The dot2 VALU kernel at every row count it takes (one or two; one for the rotated
+    format): one output row up to thousands, ragged 4-row blocks, one to five K-steps (one
+    wave each), workgroups with no row block."""
+    case = draw_case(fmt, K, N, x_dtype, seed=80 + K % 7 + N % 5)
+    rows = 1 if fmt == "had2" else 2
+    vg.force_variant(GEMV)
+    try:
+        for M in range(1, rows + 1):
+            assert vg.plan_variant(fmt, x_dtype, M, N, K) == GEMV
+            check(case, M, run(vg, case, M), label="gemv")
+        assert vg.plan_variant(fmt, x_dtype, rows + 1, N, K) == -1
+    finally:
+        vg.force_variant(-1)
+
+
+def test_gemv_is_deterministic_and_keeps_rows_beyond_m(vg):
+    case = draw_case("affine2", 2048, 333, "f16", seed=85)
+    vg.force_variant(GEMV)
+    try:
+        y1 = run(vg, case, 2)
+        assert np.array_equal(y1, run(vg, case, 2))
+        y = torch.full((8, 333), 7.25, dtype=torch.float32, device="cuda")
+        x, w, s, b = case_tensors(case, 2)
+        vg.verify_gemm_affine2(x, w, s, b, y=y[:2])
+        torch.cuda.synchronize()
+        assert torch.all(y[2:] == 7.25)
+        assert np.array_equal(y[:2].cpu().numpy().astype(np.float64), y1)
+    finally:
+        vg.force_variant(-1)
+
+
 def test_forced_variant_refuses_unsupported_rows(vg):
     case = draw_case("sign1", 1024, 32, "f16", seed=4)
     vg.force_variant(0)  # the 4-row variant
