@@ -86,10 +86,21 @@ int kstep_of(int fmt) { (void)fmt; return 1024; }   // K per MFMA-kernel unit, b
 
 // Per-shape dispatch.  fp32 activations take the exact fp32 VALU kernel.  fp16/bf16 take
 // the MFMA kernels when K is a whole number of 4-group steps: mode Q up to 4 rows, mode H
-// up to 8.  Shapes the MFMA kernels cannot stage fall back to the VALU kernel.
+// up to 8.  One row of an affine format (2-bit, or 1-bit with biases) on up to 64 MiB of
+// codes takes the dot2 kernel instead: timed against mode Q on the 5120 x 17408 projections
+// it finishes first (its set-up before the first weight load is shorter), while on the
+// 151936-row output head, where that set-up no longer matters, its steadier but slower
+// stream loses, as it does for the sign format and the rotated format at every size timed.
+// Shapes the MFMA kernels cannot stage fall back to the VALU kernel.
+constexpr double kGemvMaxCodeBytes = 64.0 * 1024 * 1024;
 int plan(int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev) {
   if (xt == VG_F32) return vg::VAR_VALU;
   if (K % kstep_of(fmt) != 0) return vg::VAR_VALU;
+  if (M == 1 && (fmt == vg::AFFINE2 || fmt == vg::AFFINE1) &&
+      (double)N * K / (fmt == vg::AFFINE2 ? 4.0 : 8.0) <= kGemvMaxCodeBytes) {
+    vg::MfmaPlan g;
+    if (vg::plan_gemv(fmt, M, K, N, dev, &g)) return vg::VAR_GEMV;
+  }
   const int var = M <= 4 ? vg::VAR_MFMA_Q : vg::VAR_MFMA_H;
   vg::MfmaPlan p;
   return vg::plan_mfma(fmt, var, M, K, N, dev, g_forced_ks, &p) ? var : vg::VAR_VALU;

@@ -34,6 +34,7 @@
 //     slice order.
 //   * The output-head epilogue (verify_gemm_argmax, one K slice): every row's argmax over
 //     the workgroups' columns as one 64-bit maximum per row (fused_argmax).
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -1215,7 +1216,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
 // are scaled by a power of two per row into fp16 as in the MFMA kernels (the row maximum
 // over the whole K comes from all waves of the workgroup), and the rotation runs in
 // registers (a 64-point transform per lane, then lane pairs for blocks of 128 and 256).
-// The 16 lanes of a row are added in a fixed order (xor 1, 2, 4, 8), and the K-steps'
+// The 16 lanes of a row are added in a fixed order (DPP within the row), and the K-steps'
 // partials of a row through LDS in step order, so results do not depend on timing.
 constexpr int GV_RPW = 4;     // output rows per wave instruction (16 lanes each)
 constexpr int GV_MAXS = 16;   // K-steps (waves) per workgroup: K <= 16384
@@ -1251,13 +1252,78 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
     asm volatile("v_mov_b32 %0, %1" : "=v"(mg[k]) : "s"(A.magic[k]));
   }
 
-  // ---- the lane's activations: 64 columns of each row, raw 16-bit values, loaded one row
-  // at a time (a first pass finds the row maxima when the rows are rescaled)
-  auto load_row = [&](int m, u32x4 (&xr)[8]) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      xr[q] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.x) + (size_t)m * A.K + kl + 8 * q);
+  // ---- the weight stream: this wave's K-step of the workgroup's 4-row blocks
+  const int RB = (A.N + GV_RPW - 1) / GV_RPW;
+  const int b0 = (int)(((long long)RB * blockIdx.x) / gridDim.x);
+  const int b1 = (int)(((long long)RB * (blockIdx.x + 1)) / gridDim.x);
+  const int nb = b1 - b0;
+  const uint32_t wrow = (uint32_t)(A.K / F::WORD_K) * 4u;
+  const uint32_t srow = (uint32_t)(A.K / F::G) * 2u;
+  const uint32_t woff = (uint32_t)kl / (ONE ? 8u : 4u);   // the lane's code bytes within a row
+  const uint32_t soff = (uint32_t)(kl / F::G) * 2u;         // its group's scale within a row
+  const char* wq = reinterpret_cast<const char*>(A.w);
+  const char* sc = reinterpret_cast<const char*>(A.scales);
+  const char* bi = reinterpret_cast<const char*>(A.biases);
+  struct GUnit {
+    uint32_t w[NWORD];
+    uint32_t s, b;
   };
+  auto issue = [&](int k, GUnit& R) {
+    const int blk = b0 + min(k, nb - 1);
+    const int row = min(blk * GV_RPW + rho, A.N - 1);
+    const char* p = wq + (size_t)row * wrow + woff;
+    if constexpr (ONE) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      R.w[0] = v.x;
+      R.w[1] = v.y;
+    } else {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R.w[i] = v[i];
+    }
+    R.s = *reinterpret_cast<const uint16_t*>(sc + (size_t)row * srow + soff);
+    if constexpr (F::AFFINE) R.b = *reinterpret_cast<const uint16_t*>(bi + (size_t)row * srow + soff);
+  };
+  GUnit ring[PREF];
+  // the first units' loads go out right behind the activations', so their latency
+  // overlaps the activation set-up below
+  auto start_ring = [&]() {
+    if (nb > 0) {
+#pragma unroll
+      for (int d = 0; d < PREF; ++d) issue(d, ring[d]);
+    }
+  };
+
+  // ---- the lane's activations: 64 columns of each row as raw 16-bit values.  The four lane
+  // rows (rho) of a wave need the same columns, so each loads one quarter (32 bytes) and the
+  // quarters are exchanged across lane rows afterwards.
+  auto load_quarter = [&](int m, u32x4 (&xq)[2]) {
+    const uint16_t* p = static_cast<const uint16_t*>(A.x) + (size_t)m * A.K + kl + 16 * rho;
+    xq[0] = *reinterpret_cast<const u32x4*>(p);
+    xq[1] = *reinterpret_cast<const u32x4*>(p + 8);
+  };
+  // xr[q] = columns 8q .. 8q+7 of the lane's 64, quarter r = xr[2r], xr[2r+1]: a permlane32
+  // swap leaves quarter (rho & 1) in [0] and 2 + (rho & 1) in [1]; a permlane16 swap of each
+  // splits those into the even and odd quarters
+  auto gather_row = [&](const u32x4 (&xq)[2], u32x4 (&xr)[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t v = xq[h][e];
+        const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        const auto lo = __builtin_amdgcn_permlane16_swap(s32[0], s32[0], false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(s32[1], s32[1], false, false);
+        xr[0 + h][e] = lo[0];
+        xr[2 + h][e] = lo[1];
+        xr[4 + h][e] = hi[0];
+        xr[6 + h][e] = hi[1];
+      }
+  };
+  u32x4 xq[MM][2];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) load_quarter(m, xq[m]);
+  start_ring();
   float f[MM];
 #pragma unroll
   for (int m = 0; m < MM; ++m) f[m] = 1.0f;
@@ -1267,13 +1333,11 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
     lds_barrier();
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
-      u32x4 xr[8];
-      load_row(m, xr);
-      u16x2 mx2 = {0, 0};
+      u16x2 mx2 = {0, 0};   // over the lane's quarter; the wave's lanes cover every column
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, xr[q][e] & 0x7FFF7FFFu));
+        for (int e = 0; e < 4; ++e) mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, xq[m][q][e] & 0x7FFF7FFFu));
       float mx = half_bits_to_f32<XT>(mx2[0] > mx2[1] ? mx2[0] : mx2[1]);
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -1298,7 +1362,7 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
 #pragma unroll
   for (int m = 0; m < MM; ++m) {
     u32x4 xr[8];
-    load_row(m, xr);
+    gather_row(xq[m], xr);
     auto raw = [&](int a) -> uint32_t { return xr[a >> 3][(a >> 1) & 3]; };   // dword holding column a
     if constexpr (HAD) {
       float v[64];
@@ -1388,43 +1452,6 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
     xs[m] = t;
   }
 
-  // ---- the weight stream: this wave's K-step of the workgroup's 4-row blocks
-  const int RB = (A.N + GV_RPW - 1) / GV_RPW;
-  const int b0 = (int)(((long long)RB * blockIdx.x) / gridDim.x);
-  const int b1 = (int)(((long long)RB * (blockIdx.x + 1)) / gridDim.x);
-  const int nb = b1 - b0;
-  const uint32_t wrow = (uint32_t)(A.K / F::WORD_K) * 4u;
-  const uint32_t srow = (uint32_t)(A.K / F::G) * 2u;
-  const uint32_t woff = (uint32_t)kl / (ONE ? 8u : 4u);   // the lane's code bytes within a row
-  const uint32_t soff = (uint32_t)(kl / F::G) * 2u;         // its group's scale within a row
-  const char* wq = reinterpret_cast<const char*>(A.w);
-  const char* sc = reinterpret_cast<const char*>(A.scales);
-  const char* bi = reinterpret_cast<const char*>(A.biases);
-  struct GUnit {
-    uint32_t w[NWORD];
-    uint32_t s, b;
-  };
-  auto issue = [&](int k, GUnit& R) {
-    const int blk = b0 + min(k, nb - 1);
-    const int row = min(blk * GV_RPW + rho, A.N - 1);
-    const char* p = wq + (size_t)row * wrow + woff;
-    if constexpr (ONE) {
-      const uint2 v = *reinterpret_cast<const uint2*>(p);
-      R.w[0] = v.x;
-      R.w[1] = v.y;
-    } else {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) R.w[i] = v[i];
-    }
-    R.s = *reinterpret_cast<const uint16_t*>(sc + (size_t)row * srow + soff);
-    if constexpr (F::AFFINE) R.b = *reinterpret_cast<const uint16_t*>(bi + (size_t)row * srow + soff);
-  };
-  GUnit ring[PREF];
-  if (nb > 0) {
-#pragma unroll
-    for (int d = 0; d < PREF; ++d) issue(d, ring[d]);
-  }
   for (int base = 0; base < nb; base += PREF) {
 #pragma unroll
     for (int d = 0; d < PREF; ++d) {
@@ -1432,9 +1459,12 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
       if (k < nb) {
         const GUnit R = ring[d];
         if (k + PREF < nb) issue(k + PREF, ring[d]);
-        float dot[MM];
+        float dot[MM][2];   // two chains per row (even and odd pairs), added at the end
 #pragma unroll
-        for (int m = 0; m < MM; ++m) dot[m] = off[m];
+        for (int m = 0; m < MM; ++m) {
+          dot[m][0] = off[m];
+          dot[m][1] = 0.0f;
+        }
 #pragma unroll
         for (int wi = 0; wi < NWORD; ++wi) {
           uint32_t pw[HALF];
@@ -1443,12 +1473,13 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
           for (int m = 0; m < MM; ++m)
 #pragma unroll
             for (int j = 0; j < HALF; ++j) {
+              float& d = dot[m][j & 1];
               if constexpr (BF)
-                dot[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[j]),
-                                                         __builtin_bit_cast(bf16x2, xp[m][wi * HALF + j]), dot[m], false);
+                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[j]),
+                                                    __builtin_bit_cast(bf16x2, xp[m][wi * HALF + j]), d, false);
               else
-                dot[m] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[j]),
-                                                __builtin_bit_cast(f16x2, xp[m][wi * HALF + j]), dot[m], false);
+                d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[j]),
+                                           __builtin_bit_cast(f16x2, xp[m][wi * HALF + j]), d, false);
             }
         }
         const float s_ = half_of(R.s, 0) * SCALE_MUL;
@@ -1456,9 +1487,12 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
         float y[MM];
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
-          y[m] = __builtin_fmaf(s_, dot[m], b_ * xs[m]);
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) y[m] += __shfl_xor(y[m], o);
+          y[m] = __builtin_fmaf(s_, dot[m][0] + dot[m][1], b_ * xs[m]);
+          // the row's 16 lanes: quads (xor 1, xor 2), then mirrored halves of 8 and 16
+          y[m] += gv_dpp<0xB1>(y[m]);
+          y[m] += gv_dpp<0x4E>(y[m]);
+          y[m] += gv_dpp<0x141>(y[m]);
+          y[m] += gv_dpp<0x140>(y[m]);
         }
         if (gam == 0) {
 #pragma unroll
@@ -1728,13 +1762,41 @@ bool plan_gemv(int fmt, int M, int K, int N, const DeviceInfo& dev, MfmaPlan* p)
   return true;
 }
 
+// The grid is one round of resident workgroups: the plan's wave count per CU, cut to what
+// the instance's registers allow (a second round would start after the first has drained).
 template <int FMT, int XT, int MM>
 static hipError_t launch_gemv_m(const MfmaArgs& A, const MfmaPlan& p, hipStream_t stream, const DeviceInfo& dev) {
   void (*kern)(MfmaArgs) = vg_gemv<FMT, XT, MM, 3>;
   static std::atomic<uint64_t> attr_done{0};
-  const hipError_t e = allow_lds(kern, attr_done, dev);
+  static std::atomic<int> resident[8][GV_MAXS + 1];   // workgroups per CU by device and S (0: unknown)
+  hipError_t e = allow_lds(kern, attr_done, dev);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(p.grid), dim3(64 * p.win_steps), p.lds, stream, A);
+  const int S = p.win_steps;
+  std::atomic<int>& slot = resident[dev.id & 7][S];
+  int per_cu = slot.load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    hipFuncAttributes fa;
+    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * S, p.lds);
+    if (e != hipSuccess) return e;
+    // a workgroup's waves do not always spread evenly over the 4 SIMDs: two waves of
+    // headroom per CU keep the whole grid resident at once
+    const int regs = fa.numRegs < 8 ? 8 : ((fa.numRegs + 7) / 8) * 8;
+    const int wps = std::min(8, 512 / regs);
+    while (per_cu > 1 && per_cu * S > 4 * wps - 2) --per_cu;
+    per_cu = per_cu < 1 ? 1 : per_cu;
+    slot.store(per_cu, std::memory_order_relaxed);
+  }
+  int grid = p.grid;
+  size_t lds = p.lds;
+  if (grid > per_cu * dev.cu_count) {
+    grid = per_cu * dev.cu_count;
+    const int rb = (A.N + GV_RPW - 1) / GV_RPW;
+    lds = (size_t)2 * MAXM * 4 + (size_t)((rb + grid - 1) / grid) * GV_RPW * S * MM * 4;
+    if (lds > (size_t)dev.max_lds) return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * S), lds, stream, A);
   return hipGetLastError();
 }
 
