@@ -53,6 +53,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 enum XType : int { XF32 = 0, XF16 = 1, XBF16 = 2 };
 
 constexpr int NW = 8;               // waves per workgroup
+static_assert(NW <= 16, "split-tile records hold a 16-bit wave mask");
 constexpr int NTHREADS = NW * 64;
 constexpr int MAXM = 8;
 
@@ -113,8 +114,8 @@ struct LdsLayout {
     slot_off = ytile_off + tiles_max * MAXM * 16 * 4;
     row_off = slot_off + NW * 2 * MAXM * 16 * 4;
     flag_off = row_off + 2 * MAXM * 4;
-    red_off = flag_off + 16;   // split tiles of the window, one word per wave boundary
-    total = red_off + NW * 4;
+    red_off = flag_off + 16;   // split tiles of the window, two words per wave boundary
+    total = red_off + NW * 8;
   }
 };
 
@@ -274,7 +275,7 @@ __device__ __forceinline__ void stage_load(const MfmaArgs& A, int M, const int* 
   const int nchunks = WK / 32, ntask = M * nchunks;
   // row = t / nchunks = (t / 32) / (WK / 1024) for t < MAXT * NTHREADS, by a float
   // reciprocal: (n + 1/2) / s lies at least 1/(2s) from an integer, far beyond the
-  // rounding of the product for n < 64 and s <= 64
+  // rounding of the product for n < 128 and s <= 64
   const float inv_steps = 1.0f / (float)(WK / KSTEP);
 #pragma unroll
   for (int j = 0; j < MAXT; ++j) {
@@ -912,7 +913,7 @@ __device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, 
   if (A.accepted) A.accepted[0] = agreed;
 }
 
-template <int FMT, int MODE, int XT, int PREF, bool AMASK, int EARLY>
+template <int FMT, int MODE, int XT, int PREF, bool AMASK, bool EARLY>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, GPS = 4 * GL;
@@ -1038,37 +1039,35 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     };
 
     // The activation loads go first: loads leave a CU in order, so weight loads ahead of
-    // them would hold back the staging (and every MFMA after it) by the whole burst.  With
-    // EARLY the wave's first PREF units are issued right behind them, so the weight stream
-    // runs while the activations arrive and are staged; the issue is unconditional (a wave
-    // with fewer units re-loads its last one, in bounds), so the wait for the activations
-    // counts exactly the loads issued after them.
+    // them would hold back the staging (and every MFMA after it) by the whole burst, and
+    // weight loads issued while the activations are still in flight delay them in the
+    // memory system just as much.  With EARLY a wave issues its first PREF units once its
+    // own activation data has landed, so their latency overlaps the staging arithmetic and
+    // the barrier after it; without, after the staging.
     XStage xs;
     stage_load<XT>(A, M, xmap, ws0 * KSTEP, ns * KSTEP, xs);
     Unit<FMT> ring[PREF];
-    if constexpr (EARLY == 1) {
-#pragma unroll
-      for (int d = 0; d < PREF; ++d) issue(ring[d]);
-    }
     lds_barrier();  // previous window's readers are done with the LDS
-    if constexpr (EARLY == 2) {
-      // behind every wave's activation loads (the barrier), ahead of the staging
+    if constexpr (EARLY) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's activations
 #pragma unroll
-      for (int d = 0; d < PREF; ++d) issue(ring[d]);
+      for (int d = 0; d < PREF; ++d)
+        if (d < nu) issue(ring[d]);
     }
     // The tiles split between waves in this window, for the reduction after it: wave
     // boundary bw (lanes 0..NW-2 of wave 0) records, when it falls strictly inside a tile
-    // and is that tile's first such boundary, the tile, the waves whose unit range meets
-    // it (mask) and which of them started before it (their slot 1).  Bit 31 marks a
-    // record.  Written after the barrier that ends the previous window's reduction, read
-    // after the one that follows the staging.  (Not the last wave: it carries the extra
-    // unit when the units do not divide evenly, and delaying its first load costs the
-    // whole call up to a microsecond, measured on MI355X.)
+    // and is that tile's first such boundary, the tile (first word, bit 31 marking a
+    // record), the waves whose unit range meets it (mask, low half of the second word)
+    // and which of them started before it (their slot 1; high half).  Written after the
+    // barrier that ends the previous window's reduction, read after the one that follows
+    // the staging.  (Not the last wave: it carries the extra unit when the units do not
+    // divide evenly, and delaying its first load costs the whole call up to a
+    // microsecond, measured on MI355X.)
     if (wid == 0 && lane < NW - 1) {
       const int bw = lane + 1;
       const int B = (int)(((uint32_t)UW * bw) / NW);
       const int t = B / ns, t0 = t * ns;
-      uint32_t rec = 0;
+      uint32_t rec = 0, who = 0;
       if (B > 0 && B < UW && B != t0 && !(bw > 1 && (int)(((uint32_t)UW * (bw - 1)) / NW) > t0)) {
         uint32_t mask = 0, late = 0;
 #pragma unroll
@@ -1079,12 +1078,14 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
             if (a2 < t0) late |= 1u << w2;
           }
         }
-        rec = (1u << 31) | ((uint32_t)t << 16) | (late << 8) | mask;
+        rec = (1u << 31) | (uint32_t)t;
+        who = (late << 16) | mask;
       }
-      reinterpret_cast<uint32_t*>(smem + L.red_off)[lane] = rec;
+      reinterpret_cast<uint32_t*>(smem + L.red_off)[2 * lane] = rec;
+      reinterpret_cast<uint32_t*>(smem + L.red_off)[2 * lane + 1] = who;
     }
     stage_compute<FMT, XT>(A, M, smem, L, ws0 * KSTEP, ns * KSTEP, xs);
-    if constexpr (EARLY == 0) {
+    if constexpr (!EARLY) {
 #pragma unroll
       for (int d = 0; d < PREF; ++d)
         if (d < nu) issue(ring[d]);
@@ -1118,8 +1119,10 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
         }
         // refill the slot only while units remain: a load past the last unit would still
         // be in flight after the loop, and the first reuse of its registers would wait
-        // for it
+        // for it.  Otherwise the slot is dead; saying so lets mode H's lane swaps work on
+        // its registers in place instead of on copies.
         if (base + d + PREF < nu) issue(ring[d]);
+        else ring[d] = Unit<FMT>{};
       }
     }
     lds_barrier();
@@ -1134,15 +1137,16 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       const uint32_t* red = reinterpret_cast<const uint32_t*>(smem + L.red_off);
       const int e = tid & 127;                 // element (row, col) of a tile
       for (int bw = 1 + __builtin_amdgcn_readfirstlane(tid >> 7); bw < NW; bw += NTHREADS / 128) {
-        const uint32_t rec = __builtin_amdgcn_readfirstlane(red[bw - 1]);
+        const uint32_t rec = __builtin_amdgcn_readfirstlane(red[2 * (bw - 1)]);
         if (!(rec >> 31)) continue;
-        const int t = (int)((rec >> 16) & 0x7FFFu);
+        const uint32_t who = __builtin_amdgcn_readfirstlane(red[2 * (bw - 1) + 1]);
+        const int t = (int)(rec & 0x7FFFFFFFu);
         float v[NW];
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) v[w2] = slots[(w2 * 2 + ((rec >> (8 + w2)) & 1u)) * (MAXM * 16) + e];
+        for (int w2 = 0; w2 < NW; ++w2) v[w2] = slots[(w2 * 2 + ((who >> (16 + w2)) & 1u)) * (MAXM * 16) + e];
         float sum = 0.0f;
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) sum += ((rec >> w2) & 1u) ? v[w2] : 0.0f;
+        for (int w2 = 0; w2 < NW; ++w2) sum += ((who >> w2) & 1u) ? v[w2] : 0.0f;
         float* yt = ytile + t * (MAXM * 16) + e;
         *yt = ws0 == kb0 ? sum : *yt + sum;
       }
@@ -1515,12 +1519,12 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
 }
 
 // The kernel names carry the variant name, so a trace shows which variant ran.
-template <int FMT, int XT, int PREF, int EARLY>
+template <int FMT, int XT, int PREF, bool EARLY>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_q(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY>(A, smem);
 }
-template <int FMT, int XT, int PREF, bool AMASK, int EARLY>
+template <int FMT, int XT, int PREF, bool AMASK, bool EARLY>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY>(A, smem);
@@ -1654,7 +1658,7 @@ static hipError_t allow_lds(void (*kern)(MfmaArgs), std::atomic<uint64_t>& done,
   return e;
 }
 
-template <int FMT, int MODE, int XT, int PREF, int EARLY>
+template <int FMT, int MODE, int XT, int PREF, bool EARLY>
 static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t stream, const DeviceInfo& dev) {
   // 1-bit codes at 8 rows: the A-operand reads of the lanes without a drafted row are
   // masked off (AMASK).  With the zero row those reads carry 4 * 8 + 4 distinct addresses,
@@ -1712,8 +1716,13 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
   A.signs = c.signs;
   decode_consts(FMT, XT, A.mask, A.magic);
-  if constexpr (fmt_one_bit(FMT)) return launch_kern<FMT, MODE, XT, 2, 0>(A, p, c.stream, dev);
-  else return launch_kern<FMT, MODE, XT, 1, 0>(A, p, c.stream, dev);
+  // Mode H (5 to 8 rows) issues a wave's first weight loads as soon as its own activation
+  // loads have landed, so the weight latency overlaps the staging arithmetic; mode Q, and
+  // the rotated format's longer staging, issue them after it (each order measured faster
+  // there on MI355X).
+  constexpr bool EARLY = MODE == VAR_MFMA_H && FMT != HAD2;
+  if constexpr (fmt_one_bit(FMT)) return launch_kern<FMT, MODE, XT, 2, EARLY>(A, p, c.stream, dev);
+  else return launch_kern<FMT, MODE, XT, 1, EARLY>(A, p, c.stream, dev);
 }
 
 hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float* part, uint32_t* counters,
