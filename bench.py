@@ -396,9 +396,14 @@ def _mean_counter(d: str, counter: str, kernel_prefix: str):
 def ingest_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload, M) -> int:
     """HBM bytes per launch of the row count's kernel: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for a copy of known size."""
-    import few_row_quantized_verify_amd as vg
-    fmt, K, N, x_dtype, _ = WORKLOADS[workload]
-    kern = vg.variant_name(vg.plan_variant(fmt, x_dtype, M, N, K))
+    # The verify kernel is the one GEMM variant the counter run dispatched (a `--m M` run
+    # launches exactly one); the dispatch query itself needs a GPU, which this step does not.
+    names = {r["Kernel_Name"].split("vg::", 1)[1].split("<", 1)[0] for r in _counter_rows(fetch_dir)
+             if r["Kernel_Name"].startswith("void vg::vg_") and "stream_read" not in r["Kernel_Name"]}
+    if len(names) != 1:
+        print(f"expected one verify kernel in the counter output, found {sorted(names)}", file=sys.stderr)
+        return 1
+    kern = names.pop()
     cf, _ = _mean_counter(cfetch_dir, "FETCH_SIZE", "copyBuffer")
     cw, _ = _mean_counter(cwrite_dir, "WRITE_SIZE", "copyBuffer")
     if cf is None:
@@ -408,8 +413,8 @@ def ingest_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload, M) -
     nbytes = 256 << 20
     fetch_factor = nbytes / (cf * 1024.0)
     write_factor = nbytes / (cw * 1024.0)
-    kf, nf = _mean_counter(fetch_dir, "FETCH_SIZE", "vg::" + kern)
-    kw, nw = _mean_counter(write_dir, "WRITE_SIZE", "vg::" + kern)
+    kf, nf = _mean_counter(fetch_dir, "FETCH_SIZE", "vg::" + kern + "<")
+    kw, nw = _mean_counter(write_dir, "WRITE_SIZE", "vg::" + kern + "<")
     if kf is None or kw is None:
         print(f"no {kern} dispatches in the counter output", file=sys.stderr)
         return 1

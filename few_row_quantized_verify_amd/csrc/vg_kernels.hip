@@ -965,12 +965,18 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   // carries none (rows of other row-blocks must read zeros in this lane's K slots)
   const int am = MODE == VAR_MFMA_Q ? i - 4 * g : (g < 2 ? i : i - 8);
   const bool av = am >= 0 && am < M && (MODE == VAR_MFMA_H || am < 4);
-  const int arow = av ? am : M;
   const int m0 = MODE == VAR_MFMA_Q ? 0 : 4 * (g & 1);
-  const uint32_t a_lane0 = L.a_off + (uint32_t)arow * A.a_pitch +
-                           (MODE == VAR_MFMA_Q ? GL * g * F::GS : 2 * (g >> 1) * GL * F::GS + 2 * (g & 1) * F::WB);
+  // The lanes without a drafted row all read one address of the zero row, whatever their
+  // lane-group: a single extra distinct address per LDS read instead of one per lane-group
+  // (a 128-bit read takes as many passes as the most distinct addresses any 16-byte bank
+  // slot of 128 bytes holds; at 8 rows the real rows fill every slot four deep, and four
+  // zero-row addresses made two slots six deep).
+  const uint32_t a_lane0 = av ? L.a_off + (uint32_t)am * A.a_pitch +
+                                    (MODE == VAR_MFMA_Q ? GL * g * F::GS : 2 * (g >> 1) * GL * F::GS + 2 * (g & 1) * F::WB)
+                              : L.a_off + (uint32_t)M * A.a_pitch;
   const uint32_t e_lane0 = L.e_off + ((MODE == VAR_MFMA_Q ? GL * g : 2 * (g >> 1) * GL) * MAXM + m0) * 4;
-  const uint32_t xp_lane0 = L.xp_off + (uint32_t)arow * L.xp_pitch + (uint32_t)g * 16u;
+  const uint32_t xp_lane0 = av ? L.xp_off + (uint32_t)am * L.xp_pitch + (uint32_t)g * 16u
+                               : L.xp_off + (uint32_t)M * L.xp_pitch;
 
   f16x8 abuf[2][2 * F::NQ];   // A operands, double-buffered across steps (see compute_unit)
 #pragma unroll
