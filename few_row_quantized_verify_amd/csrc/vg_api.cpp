@@ -87,16 +87,18 @@ int kstep_of(int fmt) { (void)fmt; return 1024; }   // K per MFMA-kernel unit, b
 // Per-shape dispatch.  fp32 activations take the exact fp32 VALU kernel.  fp16/bf16 take
 // the MFMA kernels when K is a whole number of 4-group steps: mode Q up to 4 rows, mode H
 // up to 8.  One row of an affine format (2-bit, or 1-bit with biases) on up to 64 MiB of
-// codes takes the dot2 kernel instead: timed against mode Q on the 5120 x 17408 projections
-// it finishes first (its set-up before the first weight load is shorter), while on the
-// 151936-row output head, where that set-up no longer matters, its steadier but slower
-// stream loses, as it does for the sign format and the rotated format at every size timed.
+// codes takes the dot2 kernel instead, for a plain call: timed against mode Q on the
+// 5120 x 17408 projections it finishes first (its set-up before the first weight load is
+// shorter), while on the 151936-row output head, where that set-up no longer matters, its
+// stream is slower, as it is for the sign format and the rotated format at every size
+// timed.  A call that also wants the rows' argmax stays on mode Q, whose epilogue fuses
+// the argmax: the dot2 kernel and the argmax kernel after it measured slower there.
 // Shapes the MFMA kernels cannot stage fall back to the VALU kernel.
 constexpr double kGemvMaxCodeBytes = 64.0 * 1024 * 1024;
-int plan(int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev) {
+int plan(int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev, bool argmax = false) {
   if (xt == VG_F32) return vg::VAR_VALU;
   if (K % kstep_of(fmt) != 0) return vg::VAR_VALU;
-  if (M == 1 && (fmt == vg::AFFINE2 || fmt == vg::AFFINE1) &&
+  if (!argmax && M == 1 && (fmt == vg::AFFINE2 || fmt == vg::AFFINE1) &&
       (double)N * K / (fmt == vg::AFFINE2 ? 4.0 : 8.0) <= kGemvMaxCodeBytes) {
     vg::MfmaPlan g;
     if (vg::plan_gemv(fmt, M, K, N, dev, &g)) return vg::VAR_GEMV;
@@ -255,7 +257,7 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   std::call_once(g_env_once, read_env);
   vg::DeviceInfo dev;
   if (vg_status s = device_info(&dev)) return s;
-  int var = plan(fmt, x_dtype, M, N, K, dev);
+  int var = plan(fmt, x_dtype, M, N, K, dev, idx != nullptr);
   if (g_forced >= 0) {
     if (!variant_supports(g_forced, fmt, x_dtype, M, N, K, dev))
       return fail(VG_ERR_UNSUPPORTED, "forced variant %s cannot run format %d dtype %d M=%d K=%d",

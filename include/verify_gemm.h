@@ -147,8 +147,10 @@ vg_status verify_gemm_had2_signed(const void* x, int x_dtype, int M, int K,
 
 /*
  * x_out[M, K] (fp32) = x[M, K] * H_bd, the same block-B normalized Sylvester rotation as
- * verify_gemm_had2 (B = block: 64, 128 or 256), as a standalone call.  Requires
- * 1 <= M <= 8, K % block == 0.
+ * verify_gemm_had2 (B = block: 64, 128 or 256), as a standalone call: the rotation step of
+ * the activation prep that the "dflash-mlx-bonsai2" README ("What this fork adds") fuses
+ * ahead of the rotated-weight product, here on its own for callers that rotate once and
+ * verify several times.  Requires 1 <= M <= 8, K % block == 0.
  */
 vg_status hadamard_rotate(const void* x, int x_dtype, int M, int K, int block,
                           float* x_out, void* stream);
@@ -214,10 +216,12 @@ vg_status verify_gemm_argmax_noalloc(int format, const void* x, int x_dtype, int
                                      int32_t* idx, const int32_t* draft, int32_t* accepted, void* stream);
 
 /*
- * Greedy acceptance of a drafted block: idx[m] = argmax_n y[m, n] as verify_argmax_rows,
- * and accepted[0] = the number of leading rows m with idx[m] == draft[m] (0..M), i.e. the
- * length of the drafted prefix the target model agrees with; when it is below M,
- * idx[accepted[0]] is the target's own token at the first disagreement.  draft is int32
+ * Greedy acceptance of a drafted block ("dflash-mlx-bonsai2" README, "Verify it yourself":
+ * the target's greedy argmax decides which drafted tokens stand): idx[m] = argmax_n y[m, n]
+ * as verify_argmax_rows, and accepted[0] = the number of leading rows m with
+ * idx[m] == draft[m] (0..M), i.e. the length of the drafted prefix the target model agrees
+ * with; when it is below M, idx[accepted[0]] is the target's own token at the first
+ * disagreement.  draft is int32
  * [M] on the device; accepted is int32 [1] on the device.  Same requirements as
  * verify_argmax_rows; draft and accepted must be non-null.
  */
@@ -262,9 +266,11 @@ const char* vg_last_error(void);
 vg_status vg_release_stream_workspace(void* stream);
 
 /*
- * Kernel variant the per-shape dispatch picks for (format, x_dtype, M, N, K), or -1 if the
- * shape is invalid.  vg_variant_name() gives its name, which is also the kernel's name
- * prefix in a rocprofv3 trace.
+ * Kernel variant the per-shape dispatch picks for a plain verify call of (format, x_dtype,
+ * M, N, K), or -1 if the shape is invalid.  A call that also computes the rows' argmax
+ * (verify_gemm_argmax) keeps one row on the MFMA kernel whose epilogue fuses the argmax
+ * instead of vg_gemv.  vg_variant_name() gives the variant's name, which is also the
+ * kernel's name prefix in a rocprofv3 trace.
  */
 int vg_plan_variant(int format, int x_dtype, int M, int N, int K);
 const char* vg_variant_name(int variant);

@@ -43,6 +43,22 @@ def fused(vg, case, M, draft=None):
     return vg.verify_gemm_argmax(case.fmt, x, w, s, b, draft=d)
 
 
+class same_gemm:
+    """Pins plain and argmax calls to the variant the argmax call runs, so the two run the same
+    GEMM: where the dispatch gives a plain one-row call the dot2 kernel, the argmax call runs
+    mode Q (its epilogue fuses the argmax); elsewhere both run the plain call's variant."""
+
+    def __init__(self, vg, case, M):
+        v = vg.plan_variant(case.fmt, case.x_dtype, M, case.N, case.K)
+        self.vg, self.var = vg, 0 if vg.variant_name(v) == "vg_gemv" else v   # 0: vg_mfma_q
+
+    def __enter__(self):
+        self.vg.force_variant(self.var)
+
+    def __exit__(self, *exc):
+        self.vg.force_variant(-1)
+
+
 def test_head_fused_matches_oracle_and_plain_path(vg):
     """Output-head shape (one K slice: the fused epilogue runs): y bit-identical to the plain
     call, idx equal to the oracle's argmax stored with the workload, at every ragged M."""
@@ -51,8 +67,9 @@ def test_head_fused_matches_oracle_and_plain_path(vg):
     case = workload_case(gold["workload"], seed=gold["seed"])
     assert vg.plan_ksplit("affine2", "f16", 8, case.N, case.K) == 1
     for M in (8, 5, 6, 7, 1):
-        y, idx = fused(vg, case, M)
-        y0, idx0 = plain(vg, case, M)
+        with same_gemm(vg, case, M):
+            y, idx = fused(vg, case, M)
+            y0, idx0 = plain(vg, case, M)
         torch.cuda.synchronize()
         assert torch.equal(y, y0), f"M={M}: fused call changed the logits"
         got = idx.cpu().numpy()
@@ -86,8 +103,9 @@ def test_head_fused_accept(vg):
 def test_fused_equals_separate_argmax(vg, fmt, K, N, x_dtype):
     case = draw_case(fmt, K, N, x_dtype, seed=60)
     for M in (1, 4, 8):
-        y, idx = fused(vg, case, M)
-        y0, idx0 = plain(vg, case, M)
+        with same_gemm(vg, case, M):
+            y, idx = fused(vg, case, M)
+            y0, idx0 = plain(vg, case, M)
         torch.cuda.synchronize()
         assert torch.equal(y, y0)
         got = idx.cpu().numpy()
@@ -132,3 +150,18 @@ def test_fused_consecutive_calls_reset_state(vg):
     for case, M in ((a, 8), (b, 3), (a, 8), (b, 8)):
         y, idx = fused(vg, case, M)
         assert np.array_equal(idx.cpu().numpy(), np.argmax(y.cpu().numpy(), axis=1))
+
+
+def test_one_row_argmax_call_keeps_the_fused_kernel(vg):
+    """A plain one-row call of an affine shape runs vg_gemv; the same call with the argmax runs
+    mode Q, whose epilogue fuses it.  The two logits agree to the verify bar, and idx is the
+    argmax of the call's own logits."""
+    for fmt, x_dtype in (("affine2", "f16"), ("affine1", "bf16")):
+        case = draw_case(fmt, 2048, 5000, x_dtype, seed=61)
+        assert vg.variant_name(vg.plan_variant(fmt, x_dtype, 1, case.N, case.K)) == "vg_gemv"
+        y, idx = fused(vg, case, 1)
+        y0, _ = plain(vg, case, 1)
+        torch.cuda.synchronize()
+        a, b = y.cpu().numpy().astype(np.float64), y0.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(a - b)) <= 2e-3 * np.max(np.abs(b)), fmt
+        assert int(idx.cpu()[0]) == int(np.argmax(y.cpu().numpy()[0])), fmt
