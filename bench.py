@@ -200,20 +200,26 @@ def bench_experts(args, vg, torch, dev) -> dict:
         for j in range(args.warmup):
             call(M, j)
     torch.cuda.synchronize()
-    ev = {M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
+    # the same protocol as the plain workloads: a gate holds the GPU while the host enqueues
+    # each (trial, M) block, so the event pair times the calls back to back on the device
+    gate = Gate(vg, torch, dev, torch.cuda.current_stream().cuda_stream)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < CLOCK_SETTLE_S:
+        gate.hold(4)
+        torch.cuda.synchronize()
+    gate.calibrate(torch)
     t_wall = time.perf_counter()
-    nbytes = {M: 0 for M in Ms}
-    j = 0
-    for M in Ms:
-        ev[M][0].record()
-        for i in range(args.steps):
-            call(M, j)
-            nbytes[M] += uniq[M][j % NR] * per_expert
-            j += 1
-        ev[M][1].record()
-    torch.cuda.synchronize()
+    calls = {M: [] for M in Ms}
+
+    def timed_call(M, j):
+        call(M, j)
+        calls[M].append(j)
+
+    trial_us, _, _ = timed_blocks(torch, timed_call, Ms, trial_sizes(args.steps, args.trials), gate)
     wall = time.perf_counter() - t_wall
-    us = {M: ev[M][0].elapsed_time(ev[M][1]) * 1e3 / args.steps for M in Ms}
+    us = {M: float(np.median(trial_us[M])) for M in Ms}
+    # routed packed bytes per call at M, over the routings the timed calls used
+    nbytes = {M: args.steps * float(np.mean([uniq[M][j % NR] for j in calls[M]])) * per_expert for M in Ms}
 
     # the same routed products as one plain verify call per (row, slot), on routing 0
     Mtop = max(Ms)

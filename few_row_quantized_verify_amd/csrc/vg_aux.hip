@@ -73,8 +73,10 @@ __device__ void lds_fwht(float* xs, int rows, int len, int block) {
 //
 // The kernel is latency-bound at the sizes it serves (few workgroups, one wave per SIMD), so
 // every thread issues all of its loads of a window at once: its weight words, scales and
-// biases, then its share of the activation window.  MM is the row count rounded up to
-// 1, 2, 4 or 8; staged rows M..MM-1 are zeros, so the row loops carry no run-time bounds.
+// biases, then its share of the activation window.  A workgroup computes MM rows, rows
+// m0 = MM * blockIdx.y onward: all M rows (MM = M rounded up to 1, 2, 4 or 8) or, when the
+// grid leaves CUs idle, two rows each with the row pairs spread over blockIdx.y.  Staged
+// rows past M are zeros, so the row loops carry no run-time bounds.
 constexpr int VALU_PARTS = 16;
 constexpr int VALU_ROWS = VALU_THREADS / VALU_PARTS;
 
@@ -86,18 +88,19 @@ __device__ __forceinline__ float load_x(const void* x, size_t idx) {
   return h2f(h);
 }
 
-// A thread's share of an activation window: elements k = tid + i * VALU_THREADS of every row,
-// all loads issued back to back (rows M..MM-1 and k >= len read as zeros, without a load).
+// A thread's share of an activation window: elements k = tid + i * VALU_THREADS of rows
+// m0 .. m0 + MM - 1, all loads issued back to back (rows past M and k >= len read as zeros,
+// without a load).
 constexpr int VALU_NI = VALU_WK / VALU_THREADS;
 template <int XT, int MM>
-__device__ __forceinline__ void load_window(const void* x, int M, int K, int k0, int len,
+__device__ __forceinline__ void load_window(const void* x, int M, int m0, int K, int k0, int len,
                                             float (&v)[MM][VALU_NI]) {
 #pragma unroll
   for (int m = 0; m < MM; ++m)
 #pragma unroll
     for (int i = 0; i < VALU_NI; ++i) {
       const int k = threadIdx.x + i * VALU_THREADS;
-      v[m][i] = (m < M && k < len) ? load_x<XT>(x, (size_t)m * K + k0 + k) : 0.0f;
+      v[m][i] = (m0 + m < M && k < len) ? load_x<XT>(x, (size_t)(m0 + m) * K + k0 + k) : 0.0f;
     }
 }
 
@@ -121,6 +124,7 @@ __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
   constexpr int NWJ = VALU_WK / WK / VALU_PARTS;         // words per thread per full window
   constexpr bool BIAS = FMT != SIGN1;
   const int part = threadIdx.x % VALU_PARTS, lr = threadIdx.x / VALU_PARTS;
+  const int m0 = (int)blockIdx.y * MM;                   // this workgroup's first row
   const int n = blockIdx.x * VALU_ROWS + lr;
   const int nl = min(n, A.N - 1);                        // rows past N compute row N-1, unstored
   const size_t wrow = (size_t)nl * (A.K / WK), grow = (size_t)nl * (A.K / G);
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
       bib[j] = BIAS ? A.biases[grow + k / G] : 0u;
     }
     float xv[MM][VALU_NI];
-    load_window<XT, MM>(A.x, A.M, A.K, k0, len, xv);
+    load_window<XT, MM>(A.x, A.M, m0, A.K, k0, len, xv);
     __syncthreads();                                     // the previous window is consumed
     store_window<WK, MM>(xv, len, xs);
     __syncthreads();
@@ -189,44 +193,53 @@ __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
 #pragma unroll
   for (int m = 0; m < MM; ++m) red[lr][part][m] = acc[m];
   __syncthreads();
-  // Thread (lr, m) adds row m's parts in part order.
-  if (part < A.M && n < A.N) {
+  // Thread (lr, m) adds row m0 + m's parts in part order.
+  if (part < MM && m0 + part < A.M && n < A.N) {
     float sum = 0.0f;
 #pragma unroll
     for (int q = 0; q < VALU_PARTS; ++q) sum += red[lr][q][part];
-    A.y[(size_t)part * A.N + n] = sum;
+    A.y[(size_t)(m0 + part) * A.N + n] = sum;
   }
 }
 
+// rows_per_wg: 2 when the row pairs go to separate workgroups, else 0 (all rows in one)
 template <int FMT, int XT>
-static void launch_valu_m(const ValuArgs& A, dim3 grid, hipStream_t s) {
+static void launch_valu_m(const ValuArgs& A, dim3 grid, int rows_per_wg, hipStream_t s) {
   if (A.M <= 1) hipLaunchKernelGGL((vg_valu<FMT, XT, 1>), grid, dim3(VALU_THREADS), 0, s, A);
-  else if (A.M <= 2) hipLaunchKernelGGL((vg_valu<FMT, XT, 2>), grid, dim3(VALU_THREADS), 0, s, A);
+  else if (A.M <= 2 || rows_per_wg == 2) hipLaunchKernelGGL((vg_valu<FMT, XT, 2>), grid, dim3(VALU_THREADS), 0, s, A);
   else if (A.M <= 4) hipLaunchKernelGGL((vg_valu<FMT, XT, 4>), grid, dim3(VALU_THREADS), 0, s, A);
   else hipLaunchKernelGGL((vg_valu<FMT, XT, 8>), grid, dim3(VALU_THREADS), 0, s, A);
 }
 
 template <int FMT>
-static hipError_t launch_valu_x(const ValuArgs& A, dim3 grid, hipStream_t s) {
+static hipError_t launch_valu_x(const ValuArgs& A, dim3 grid, int rows_per_wg, hipStream_t s) {
   switch (A.xt) {
-    case 0: launch_valu_m<FMT, 0>(A, grid, s); break;
-    case 1: launch_valu_m<FMT, 1>(A, grid, s); break;
-    case 2: launch_valu_m<FMT, 2>(A, grid, s); break;
+    case 0: launch_valu_m<FMT, 0>(A, grid, rows_per_wg, s); break;
+    case 1: launch_valu_m<FMT, 1>(A, grid, rows_per_wg, s); break;
+    case 2: launch_valu_m<FMT, 2>(A, grid, rows_per_wg, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// A grid too small to fill the CUs with all rows per workgroup (the kernel is latency-bound
+// there, and a workgroup's time grows with its rows) gives each row pair its own
+// workgroups: the packed words are then read once per pair, a small cost at these sizes.
 hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev) {
-  (void)dev;
   if (c.M < 1 || c.M > MAXM || c.N < 1) return hipErrorInvalidValue;
   ValuArgs A{c.x, c.xt, c.w, c.scales, c.biases, c.y, c.M, c.K, c.N, c.had_block, c.signs};
-  const dim3 grid((c.N + VALU_ROWS - 1) / VALU_ROWS);
+  dim3 grid((c.N + VALU_ROWS - 1) / VALU_ROWS);
+  int rows_per_wg = 0;
+  const int pairs = (c.M + 1) / 2;
+  if (c.M > 2 && (long long)grid.x * pairs <= dev.cu_count) {
+    grid.y = pairs;
+    rows_per_wg = 2;
+  }
   switch (c.fmt) {
-    case SIGN1: return launch_valu_x<SIGN1>(A, grid, c.stream);
-    case AFFINE2: return launch_valu_x<AFFINE2>(A, grid, c.stream);
-    case HAD2: return launch_valu_x<HAD2>(A, grid, c.stream);
-    case AFFINE1: return launch_valu_x<AFFINE1>(A, grid, c.stream);
+    case SIGN1: return launch_valu_x<SIGN1>(A, grid, rows_per_wg, c.stream);
+    case AFFINE2: return launch_valu_x<AFFINE2>(A, grid, rows_per_wg, c.stream);
+    case HAD2: return launch_valu_x<HAD2>(A, grid, rows_per_wg, c.stream);
+    case AFFINE1: return launch_valu_x<AFFINE1>(A, grid, rows_per_wg, c.stream);
     default: return hipErrorInvalidValue;
   }
 }
