@@ -37,6 +37,11 @@ Prints one JSON line: value = packed-weight bytes (codes + fp16 scales + fp16 bi
 moved per second over all timed calls (GB/s, 1e9), plus per-M microseconds per call,
 t(M=8)/t(M=1), a roofline object for the dominant kernel and the CPU oracle baseline.
 
+The affine formats' scales and biases are passed interleaved (each group's scale and bias
+side by side, built once before timing with vg_pack_scale_bias, as a weight load would):
+the same bytes in the library's faster layout.  --scale-bias separate times the two
+separate arrays instead; config.scale_bias names the layout.
+
 Options:
   --workload NAME    another named workload as the headline (see synthetic.inputs.WORKLOADS)
   --m LIST           only these row counts, e.g. "8" (for profiling one kernel; no
@@ -46,6 +51,7 @@ Options:
                      the median over the trials (and the min)
   --force-variant V  run every call on kernel variant V (see vg_variant_name) instead of the
                      per-shape dispatch, for A/B timing
+  --scale-bias L     "interleaved" (default) or "separate" scales and biases
   --table            one JSON line per workload (instead of per_workload entries)
   --no-per-workload  the headline workload only
   --stream-sweep     print the streaming-read sweep at every workload's byte count, then exit
@@ -184,6 +190,7 @@ def bench_experts(args, vg, torch, dev) -> dict:
     ncopy = max(2, -(-POOL_BYTES // (per_expert * E)))
     w0, s0 = words_tensor(ec.words, dev), f16_tensor(ec.scales, dev)
     b0 = f16_tensor(ec.biases, dev) if ec.biases is not None else None
+    s0, b0, layout = scale_bias_layout(args, vg, s0, b0)
     pool = [(w0.clone(), s0.clone(), None if b0 is None else b0.clone()) for _ in range(ncopy)]
     NR = 64
     routes = {M: [draw_route(M, topk, E, seed=1000 * M + r) for r in range(NR)] for M in Ms}
@@ -264,6 +271,7 @@ def bench_experts(args, vg, torch, dev) -> dict:
         "dtype": "f16" if x_dtype != "f32" else "f32", "data": "synthetic",
         "config": {"workload": name, "format": fmt, "K": K, "N": N, "E": E, "topk": topk,
                    "x_dtype": x_dtype, "M": list(Ms), "packed_bytes_per_expert": per_expert,
+                   "scale_bias": layout,
                    "routings": NR, "weight_pool_copies": ncopy},
         "per_m": per_m,
         "per_slot_calls_us": {"M": Mtop, "us": round(per_slot_us, 2),
@@ -445,6 +453,19 @@ def ingest_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir, workload, M) -
     return 0
 
 
+def scale_bias_layout(args, vg, s0, b0):
+    """The affine formats' scales and biases in the layout the run asks for: interleaved
+    (scale, bias) pairs, built once on the device like a weight load would (the library's
+    faster layout; the same bytes), or the two separate arrays.  Returns (scales, biases,
+    layout name)."""
+    if b0 is None:
+        return s0, None, "none"
+    if getattr(args, "scale_bias", "interleaved") == "separate":
+        return s0, b0, "separate"
+    sb = vg.pack_scale_bias(s0, b0)
+    return sb, None, "interleaved"
+
+
 def raw_caller(vg, fmt, x, w, s, b, y, sh, idx=None):
     """The C ABI entry point of one verify call with its arguments marshalled once (the
     binding's checked wrapper has already run the same call once): the timed loop then
@@ -452,13 +473,13 @@ def raw_caller(vg, fmt, x, w, s, b, y, sh, idx=None):
     import ctypes
     from few_row_quantized_verify_amd import binding as B
     L = B.lib()
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
     M, K = x.shape
     N = w.shape[0]
     xt = B._xdtype(x)
     st = ctypes.c_void_p(sh)
     if idx is not None:
-        args = (B.FORMATS[fmt], P(x), xt, M, K, P(w), P(s), P(b) if b is not None else None, N, P(y), P(idx),
+        args = (B.FORMATS[fmt], P(x), xt, M, K, P(w), P(s), P(b), N, P(y), P(idx),
                 None, None, st)
         fn = L.verify_gemm_argmax
     elif fmt == "sign1":
@@ -488,6 +509,7 @@ def bench_workload(args, vg, torch, dev, name, Ms, gate, sh, full_sweep=False) -
     w0 = words_tensor(case.words, dev)
     s0 = f16_tensor(case.scales, dev)
     b0 = f16_tensor(case.biases, dev) if case.biases is not None else None
+    s0, b0, layout = scale_bias_layout(args, vg, s0, b0)
     pool = [(w0.clone(), s0.clone(), None if b0 is None else b0.clone()) for _ in range(ncopy)]
     del w0, s0, b0
     ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
@@ -540,7 +562,8 @@ def bench_workload(args, vg, torch, dev, name, Ms, gate, sh, full_sweep=False) -
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if x_dtype != "f32" else "f32", "data": "synthetic",
         "config": {"workload": name, "format": fmt, "K": K, "N": N, "x_dtype": x_dtype,
-                   "M": list(Ms), "packed_bytes_per_call": pb, "weight_pool_copies": ncopy},
+                   "M": list(Ms), "packed_bytes_per_call": pb, "weight_pool_copies": ncopy,
+                   "scale_bias": layout},
         "per_m": per_m,
         "t8_over_t1": round(us[Mtop] / us[min(Ms)], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -557,7 +580,8 @@ def bench_workload(args, vg, torch, dev, name, Ms, gate, sh, full_sweep=False) -
 def summary(line) -> dict:
     """The compact per-workload entry of the headline line."""
     pm = line["per_m"]
-    return {"config": {k: line["config"][k] for k in ("format", "K", "N", "x_dtype", "packed_bytes_per_call")},
+    return {"config": {k: line["config"][k] for k in ("format", "K", "N", "x_dtype", "packed_bytes_per_call",
+                                                        "scale_bias")},
             "us_per_call": {m: v["us_per_call"] for m, v in pm.items()},
             "pct_hbm_peak": {m: v["pct_hbm_peak"] for m, v in pm.items()},
             "variant": {m: v["variant"] for m, v in pm.items()},
@@ -588,6 +612,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--m", default=None)
     ap.add_argument("--force-variant", default=None)
+    ap.add_argument("--scale-bias", choices=("interleaved", "separate"), default="interleaved",
+                    help="layout of the affine formats' scales and biases (same bytes)")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR", default=None)
     args = ap.parse_args()
     if args.ingest_counters:

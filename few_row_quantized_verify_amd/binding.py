@@ -60,6 +60,7 @@ _SIGS = {
     "vg_debug_unpack": (_I, [_I, _I, _P, _I, _I, _P, _P]),
     "vg_debug_unpack_sign1": (_I, [_P, _I, _I, _P, _P]),
     "vg_debug_unpack_affine2": (_I, [_P, _I, _I, _P, _P]),
+    "vg_pack_scale_bias": (_I, [_P, _P, ctypes.c_longlong, _P, _P]),
 }
 
 
@@ -109,6 +110,12 @@ def _xdtype(x) -> int:
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _optr(t):
+    """A device pointer, or NULL for None (the sign format's biases, or the interleaved
+    scale-and-bias layout's)."""
+    return ctypes.c_void_p(0) if t is None else ctypes.c_void_p(t.data_ptr())
 
 
 # Elements per packed uint32 word and per quantization group of each format.
@@ -163,10 +170,12 @@ def _weights(fmt, w, scales, biases, N, K, lead=()):
     if K % g:
         _bad(VG_ERR_SHAPE, f"K={K} is not a multiple of the group size {g}")
     _tensor(w, "w", (*lead, N, K // wk), (torch.int32,))
+    if _HAS_BIAS[fmt] and biases is None:
+        # the interleaved layout: each group's (scale, bias) pair side by side
+        _tensor(scales, "scales", (*lead, N, K // g, 2), (torch.float16,))
+        return
     _tensor(scales, "scales", (*lead, N, K // g), (torch.float16,))
     if _HAS_BIAS[fmt]:
-        if biases is None:
-            _bad(VG_ERR_ARG, "biases are required for this format")
         _tensor(biases, "biases", (*lead, N, K // g), (torch.float16,))
 
 
@@ -207,25 +216,29 @@ def verify_gemm_sign1(x, wbits, scales, y=None, stream=None):
 
 
 def verify_gemm_affine2(x, wq, scales, biases, y=None, stream=None):
-    """y[M, N] = x[M, K] @ W^T, W 2-bit affine g64 (wq int32 [N, K/16], scales/biases fp16 [N, K/64])."""
+    """y[M, N] = x[M, K] @ W^T, W 2-bit affine g64 (wq int32 [N, K/16], scales/biases fp16
+    [N, K/64]; or biases None and scales the interleaved pairs [N, K/64, 2] of
+    pack_scale_bias)."""
     M, K, N, y = _gemm_args(FMT_AFFINE2, x, wq, scales, biases, y)
     _check(lib().verify_gemm_affine2(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
-                                     _ptr(biases), N, _ptr(y), _stream(stream)))
+                                     _optr(biases), N, _ptr(y), _stream(stream)))
     return y
 
 
 def verify_gemm_affine1(x, wbits, scales, biases, y=None, stream=None):
-    """y[M, N] = x[M, K] @ W^T, W MLX 1-bit affine g128 (wbits int32 [N, K/32], scales/biases fp16 [N, K/128])."""
+    """y[M, N] = x[M, K] @ W^T, W MLX 1-bit affine g128 (wbits int32 [N, K/32], scales/biases
+    fp16 [N, K/128]; or biases None and scales the interleaved pairs [N, K/128, 2])."""
     M, K, N, y = _gemm_args(FMT_AFFINE1, x, wbits, scales, biases, y)
     _check(lib().verify_gemm_affine1(_ptr(x), _xdtype(x), M, K, _ptr(wbits), _ptr(scales),
-                                     _ptr(biases), N, _ptr(y), _stream(stream)))
+                                     _optr(biases), N, _ptr(y), _stream(stream)))
     return y
 
 
 def verify_gemm_had2(x, wq, scales, biases, had_block=128, y=None, stream=None, signs=None):
     """y = ((x * D) @ blockdiag(H_B/sqrt(B))) @ W^T with W 2-bit affine g64, B = had_block;
     D = diag(+-1) from the sign bits `signs` (int32 [K/32], bit set: negate), or the
-    identity when signs is None."""
+    identity when signs is None.  biases None: scales holds the interleaved pairs
+    [N, K/64, 2]."""
     torch = _torch()
     if signs is not None:
         _tensor(signs, "signs", (_x(x)[1] // 32,), (torch.int32,))
@@ -233,10 +246,10 @@ def verify_gemm_had2(x, wq, scales, biases, had_block=128, y=None, stream=None, 
     _check_devices(x.device, signs=signs)
     if signs is None:
         _check(lib().verify_gemm_had2(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
-                                      _ptr(biases), N, had_block, _ptr(y), _stream(stream)))
+                                      _optr(biases), N, had_block, _ptr(y), _stream(stream)))
     else:
         _check(lib().verify_gemm_had2_signed(_ptr(x), _xdtype(x), M, K, _ptr(wq), _ptr(scales),
-                                             _ptr(biases), N, had_block, _ptr(signs), _ptr(y),
+                                             _optr(biases), N, had_block, _ptr(signs), _ptr(y),
                                              _stream(stream)))
     return y
 
@@ -401,6 +414,26 @@ def verify_accept_greedy(y, draft, idx=None, accepted=None, stream=None):
         accepted = torch.empty((1,), dtype=torch.int32, device=y.device)
     _check(lib().verify_accept_greedy(_ptr(y), M, N, _ptr(draft), _ptr(idx), _ptr(accepted), _stream(stream)))
     return idx, accepted
+
+
+def pack_scale_bias(scales, biases, out=None, stream=None):
+    """The interleaved scale-and-bias layout of an affine format's group metadata, built on
+    the device once when the weights are loaded: scales and biases fp16 [..., G] (same
+    shape) give out fp16 [..., G, 2] with out[..., 0] = scales and out[..., 1] = biases.
+    Pass it as `scales` with biases None to any affine verify call."""
+    torch = _torch()
+    if not isinstance(scales, torch.Tensor) or not isinstance(biases, torch.Tensor):
+        _bad(VG_ERR_ARG, "scales and biases must be torch tensors")
+    _tensor(scales, "scales", scales.shape, (torch.float16,))
+    _tensor(biases, "biases", scales.shape, (torch.float16,))
+    if not scales.is_cuda:
+        _bad(VG_ERR_ARG, f"scales is on {scales.device}, expected a GPU tensor")
+    _check_devices(scales.device, biases=biases)
+    if out is None:
+        out = torch.empty((*scales.shape, 2), dtype=torch.float16, device=scales.device)
+    _tensor(out, "out", (*scales.shape, 2), (torch.float16,), scales.device)
+    _check(lib().vg_pack_scale_bias(_ptr(scales), _ptr(biases), scales.numel(), _ptr(out), _stream(stream)))
+    return out
 
 
 def stream_read(buf, nbytes: int, sink=None, stream=None, loads_in_flight: int = 4, wgs_per_cu: int = 8):

@@ -82,6 +82,13 @@ vg_status check_ptr(const void* p, const char* name) {
   return VG_OK;
 }
 
+// The biases of an affine format: a separate array, or null when scales holds the
+// interleaved (scale, bias) pairs.
+vg_status check_biases(const void* p) {
+  if (p && !aligned16(p)) return fail(VG_ERR_ALIGN, "biases is not 16-byte aligned");
+  return VG_OK;
+}
+
 int kstep_of(int fmt) { (void)fmt; return 1024; }   // K per MFMA-kernel unit, both formats
 
 // Per-shape dispatch.  fp32 activations take the exact fp32 VALU kernel.  fp16/bf16 take
@@ -266,6 +273,7 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   }
   vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, static_cast<hipStream_t>(stream),
                  had_block, signs};
+  c.sbi = fmt != vg::SIGN1 && biases == nullptr;
   vg::MfmaPlan p{};
   const bool mfma = var == vg::VAR_MFMA_Q || var == vg::VAR_MFMA_H;
   if (mfma) {
@@ -326,7 +334,7 @@ vg_status run_experts(int fmt, const void* x, int x_dtype, int M, int K, int E, 
   if (vg_status s = check_ptr(w, "w")) return s;
   if (vg_status s = check_ptr(scales, "scales")) return s;
   if (fmt != vg::SIGN1)
-    if (vg_status s = check_ptr(biases, "biases")) return s;
+    if (vg_status s = check_biases(biases)) return s;
   if (vg_status s = check_ptr(y, "y")) return s;
   std::call_once(g_env_once, read_env);
   vg::DeviceInfo dev;
@@ -346,8 +354,10 @@ vg_status run_experts(int fmt, const void* x, int x_dtype, int M, int K, int E, 
   const bool two_bit = fmt == vg::AFFINE2 || fmt == vg::HAD2;
   const long long words = (long long)N * (K / (two_bit ? 16 : 32));
   const long long groups = (long long)N * (K / (two_bit ? 64 : 128));
-  vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, biases, y, st, 128, nullptr,
-                 route, topk, E, cap, words * 4, groups * 2};
+  const bool sbi = fmt != vg::SIGN1 && biases == nullptr;
+  vg::GemmCall c{fmt, x_dtype, x, M, K, N, w, scales, sbi ? nullptr : biases, y, st, 128, nullptr,
+                 route, topk, E, cap, words * 4, groups * (sbi ? 4 : 2)};
+  c.sbi = sbi;
   const hipError_t e = vg::launch_mfma(c, var, p, nullptr, nullptr, dev);
   if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
@@ -395,7 +405,7 @@ vg_status verify_gemm_affine1(const void* x, int x_dtype, int M, int K, const ui
   if (K % 128 != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of 128 (1-bit affine group)", K);
   if (vg_status s = check_ptr(wbits, "wbits")) return s;
   if (vg_status s = check_ptr(scales, "scales")) return s;
-  if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_biases(biases)) return s;
   if (vg_status s = check_ptr(y, "y")) return s;
   return run_gemm(vg::AFFINE1, x, x_dtype, M, K, wbits, scales, biases, N, y, stream);
 }
@@ -407,7 +417,7 @@ vg_status verify_gemm_affine2(const void* x, int x_dtype, int M, int K, const ui
   if (K % 64 != 0) return fail(VG_ERR_SHAPE, "K=%d is not a multiple of 64 (2-bit group)", K);
   if (vg_status s = check_ptr(wq, "wq")) return s;
   if (vg_status s = check_ptr(scales, "scales")) return s;
-  if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_biases(biases)) return s;
   if (vg_status s = check_ptr(y, "y")) return s;
   return run_gemm(vg::AFFINE2, x, x_dtype, M, K, wq, scales, biases, N, y, stream);
 }
@@ -422,7 +432,7 @@ vg_status verify_gemm_had2_signed(const void* x, int x_dtype, int M, int K, cons
     return fail(VG_ERR_SHAPE, "K=%d is not a multiple of 128 and of the Hadamard block %d", K, had_block);
   if (vg_status s = check_ptr(wq, "wq")) return s;
   if (vg_status s = check_ptr(scales, "scales")) return s;
-  if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_biases(biases)) return s;
   if (vg_status s = check_ptr(y, "y")) return s;
   if (signs && (reinterpret_cast<uintptr_t>(signs) & 3u)) return fail(VG_ERR_ALIGN, "signs is not 4-byte aligned");
   return run_gemm(vg::HAD2, x, x_dtype, M, K, wq, scales, biases, N, y, stream, had_block, signs);
@@ -464,7 +474,7 @@ vg_status verify_gemm_argmax(int format, const void* x, int x_dtype, int M, int 
   if (vg_status s = check_ptr(w, "w")) return s;
   if (vg_status s = check_ptr(scales, "scales")) return s;
   if (format != vg::SIGN1)
-    if (vg_status s = check_ptr(biases, "biases")) return s;
+    if (vg_status s = check_biases(biases)) return s;
   if (vg_status s = check_ptr(y, "y")) return s;
   if (!idx) return fail(VG_ERR_ARG, "idx is null");
   if (reinterpret_cast<uintptr_t>(idx) & 3u) return fail(VG_ERR_ALIGN, "idx is not 4-byte aligned");
@@ -484,7 +494,7 @@ vg_status verify_gemm_argmax_noalloc(int format, const void* x, int x_dtype, int
   if (vg_status s = check_ptr(w, "w")) return s;
   if (vg_status s = check_ptr(scales, "scales")) return s;
   if (format != vg::SIGN1)
-    if (vg_status s = check_ptr(biases, "biases")) return s;
+    if (vg_status s = check_biases(biases)) return s;
   if (vg_status s = check_ptr(y, "y")) return s;
   if (idx && (reinterpret_cast<uintptr_t>(idx) & 3u)) return fail(VG_ERR_ALIGN, "idx is not 4-byte aligned");
   if ((draft == nullptr) != (accepted == nullptr)) return fail(VG_ERR_ARG, "draft and accepted go together");
@@ -509,6 +519,25 @@ vg_status verify_gemm_experts(int format, const void* x, int x_dtype, int M, int
                               const uint16_t* biases, int N, float* y, void* stream) {
   if (format < VG_FMT_SIGN1 || format > VG_FMT_AFFINE1) return fail(VG_ERR_ARG, "unknown format %d", format);
   return run_experts(format, x, x_dtype, M, K, E, topk, route, w, scales, biases, N, y, stream);
+}
+
+vg_status vg_pack_scale_bias(const uint16_t* scales, const uint16_t* biases, long long count, uint16_t* out,
+                             void* stream) {
+  if (count < 0) return fail(VG_ERR_SHAPE, "count=%lld < 0", count);
+  if (vg_status s = check_ptr(scales, "scales")) return s;
+  if (vg_status s = check_ptr(biases, "biases")) return s;
+  if (vg_status s = check_ptr(out, "out")) return s;
+  const auto overlaps = [count](const void* a, long long abytes, const void* b, long long bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return count > 0 && a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+  };
+  if (overlaps(out, 4 * count, scales, 2 * count) || overlaps(out, 4 * count, biases, 2 * count))
+    return fail(VG_ERR_ARG, "out overlaps scales or biases");
+  const hipError_t e = vg::launch_pack_scale_bias(scales, biases, count, reinterpret_cast<uint32_t*>(out),
+                                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return VG_OK;
 }
 
 const char* vg_last_error(void) { return g_err; }

@@ -39,6 +39,7 @@ struct ValuArgs {
   int M, K, N;
   int had_block;            // rotated format: 64, 128 or 256
   const uint32_t* signs;    // rotated format: optional sign bits [K/32]
+  bool sbi;                 // scales holds interleaved (scale, bias) words, biases unused
 };
 
 __device__ __forceinline__ float had_norm(int block) {
@@ -139,8 +140,14 @@ __global__ __launch_bounds__(VALU_THREADS) void vg_valu(ValuArgs A) {
       const int wi = min(part + j * VALU_PARTS, nw - 1);
       const int k = k0 + WK * wi;
       word[j] = A.w[wrow + k / WK];
-      scb[j] = A.scales[grow + k / G];
-      bib[j] = BIAS ? A.biases[grow + k / G] : 0u;
+      if (BIAS && A.sbi) {
+        const uint32_t sb = reinterpret_cast<const uint32_t*>(A.scales)[grow + k / G];
+        scb[j] = sb & 0xFFFFu;
+        bib[j] = sb >> 16;
+      } else {
+        scb[j] = A.scales[grow + k / G];
+        bib[j] = BIAS ? A.biases[grow + k / G] : 0u;
+      }
     }
     float xv[MM][VALU_NI];
     load_window<XT, MM>(A.x, A.M, m0, A.K, k0, len, xv);
@@ -227,7 +234,7 @@ static hipError_t launch_valu_x(const ValuArgs& A, dim3 grid, int rows_per_wg, h
 // workgroups: the packed words are then read once per pair, a small cost at these sizes.
 hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev) {
   if (c.M < 1 || c.M > MAXM || c.N < 1) return hipErrorInvalidValue;
-  ValuArgs A{c.x, c.xt, c.w, c.scales, c.biases, c.y, c.M, c.K, c.N, c.had_block, c.signs};
+  ValuArgs A{c.x, c.xt, c.w, c.scales, c.biases, c.y, c.M, c.K, c.N, c.had_block, c.signs, c.sbi};
   dim3 grid((c.N + VALU_ROWS - 1) / VALU_ROWS);
   int rows_per_wg = 0;
   const int pairs = (c.M + 1) / 2;
@@ -242,6 +249,26 @@ hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev) {
     case AFFINE1: return launch_valu_x<AFFINE1>(A, grid, rows_per_wg, c.stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// ---------------------------------------------------------------------------------------
+// Interleaved (scale, bias) layout of the affine formats' group metadata: one word per
+// group, the scale in the low half.  Built once when the weights are loaded; the GEMMs then
+// fetch a lane's scales and biases with one load instead of one per array.
+__global__ __launch_bounds__(256) void vg_pack_scale_bias_kernel(const uint16_t* s, const uint16_t* b,
+                                                                long long count, uint32_t* out) {
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < count; i += stride)
+    out[i] = (uint32_t)s[i] | ((uint32_t)b[i] << 16);
+}
+
+hipError_t launch_pack_scale_bias(const uint16_t* s, const uint16_t* b, long long count, uint32_t* out,
+                                  hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  const long long blocks = (count + 255) / 256;
+  hipLaunchKernelGGL(vg_pack_scale_bias_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, st,
+                     s, b, count, out);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------

@@ -505,11 +505,14 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
 
 // ---------------------------------------------------------------------------------------
 // Loaded data of one unit for one lane: GL consecutive 16-byte groups of the lane's row
-// and their fp16 scales (and biases) as packed pairs.  Nothing consumes a load where it
-// is issued, so the loads of later units stay in flight.
-template <int FMT> struct Unit {
+// and their fp16 scales (and biases) as loaded.  From separate arrays, s and b hold
+// scale pairs and bias pairs (group 2d in the low half of word d); from the interleaved
+// layout (SBI), s holds the GL (scale, bias) words of the lane's groups, one 16-byte (or
+// 8-byte) load, and b is unused.  Nothing consumes a load where it is issued, so the loads
+// of later units stay in flight.
+template <int FMT, bool SBI> struct Unit {
   u32x4 w[Fmt<FMT>::GL];
-  uint32_t s[Fmt<FMT>::GL / 2];
+  uint32_t s[SBI ? Fmt<FMT>::GL : Fmt<FMT>::GL / 2];
   uint32_t b[Fmt<FMT>::GL / 2];
 };
 
@@ -562,8 +565,8 @@ __device__ __forceinline__ void read_a(const char* smem, uint32_t addr, f16x8* d
 
 // AMASK: only the lanes whose operand row is a drafted row (a_on) read their A operands; the
 // others keep the zeros abuf was cleared to.  abuf lives across units for that reason.
-template <int FMT, int MODE, bool BF, bool AMASK>
-__device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* smem, uint32_t a_lane, uint32_t e_lane,
+template <int FMT, int MODE, bool BF, bool AMASK, bool SBI>
+__device__ __forceinline__ void compute_unit(const Unit<FMT, SBI>& U, const char* smem, uint32_t a_lane, uint32_t e_lane,
                                              uint32_t xp_lane, const uint32_t* mk, const uint32_t* mg,
                                              float yacc[4], f32x4& yb, bool a_on,
                                              f16x8 (&abuf)[2][2 * Fmt<FMT>::NQ]) {
@@ -574,6 +577,19 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
   constexpr int NSTEP = NPAIR * WPP;
   // 1-bit affine codes decode to BETA + 2 code, so their accumulators hold twice the sum
   constexpr float SCALE_MUL = FMT == AFFINE1 ? 0.5f : 1.0f;
+  // scale pairs and bias pairs of the lane's groups (group 2d in the low half of word d);
+  // from interleaved (scale, bias) words, two byte permutes per pair
+  uint32_t us[GL / 2], ub[GL / 2];
+#pragma unroll
+  for (int d = 0; d < GL / 2; ++d) {
+    if constexpr (SBI) {
+      us[d] = __builtin_amdgcn_perm(U.s[2 * d + 1], U.s[2 * d], 0x05040100u);
+      ub[d] = __builtin_amdgcn_perm(U.s[2 * d + 1], U.s[2 * d], 0x07060302u);
+    } else {
+      us[d] = U.s[d];
+      ub[d] = F::AFFINE ? U.b[d] : 0u;
+    }
+  }
 
   uint32_t wa[NPAIR][WPP], wb[NPAIR][WPP];
   float sa[NPAIR], sb[NPAIR];
@@ -586,8 +602,8 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
         wa[pi][w] = U.w[2 * pi][w];
         wb[pi][w] = U.w[2 * pi + 1][w];
       }
-      sa[pi] = half_of(U.s[pi], 0) * SCALE_MUL;
-      sb[pi] = half_of(U.s[pi], 1) * SCALE_MUL;
+      sa[pi] = half_of(us[pi], 0) * SCALE_MUL;
+      sb[pi] = half_of(us[pi], 1) * SCALE_MUL;
       ga[pi] = 2 * pi;
       gb[pi] = 2 * pi + 1;
     }
@@ -597,7 +613,7 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
     uint32_t sc[2][GL / 2];
 #pragma unroll
     for (int d = 0; d < GL / 2; ++d) {
-      const auto t = __builtin_amdgcn_permlane16_swap(U.s[d], U.s[d], false, false);
+      const auto t = __builtin_amdgcn_permlane16_swap(us[d], us[d], false, false);
       sc[0][d] = t[0];
       sc[1][d] = t[1];
     }
@@ -672,7 +688,7 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
       // bf16 (X hi, X lo) against the two fp16 biases split exactly into bf16 hi + lo
       // (11 significant bits = 8 + 3): every cross product of the parts is one K slot
       static_assert(GL == 2, "bf16 bias quads hold two groups");
-      const float f0 = half_of(U.b[0], 0), f1 = half_of(U.b[0], 1);
+      const float f0 = half_of(ub[0], 0), f1 = half_of(ub[0], 1);
       const float l0 = f0 - __uint_as_float(__float_as_uint(f0) & 0xFFFF0000u);
       const float l1 = f1 - __uint_as_float(__float_as_uint(f1) & 0xFFFF0000u);
       const uint32_t dh = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
@@ -681,8 +697,8 @@ __device__ __forceinline__ void compute_unit(const Unit<FMT>& U, const char* sme
                                                    __builtin_bit_cast(bf16x8, u32x4{dh, dh, dl, dl}), yb, 0, 0, 0);
     } else {
       u32x4 bw;
-      if constexpr (GL == 4) bw = u32x4{U.b[0], U.b[1], U.b[0], U.b[1]};
-      else bw = u32x4{U.b[0], 0u, U.b[0], 0u};
+      if constexpr (GL == 4) bw = u32x4{ub[0], ub[1], ub[0], ub[1]};
+      else bw = u32x4{ub[0], 0u, ub[0], 0u};
       yb = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, __builtin_bit_cast(f16x8, bw), yb, 0, 0, 0);
     }
   } else {
@@ -913,7 +929,7 @@ __device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, 
   if (A.accepted) A.accepted[0] = agreed;
 }
 
-template <int FMT, int MODE, int XT, int PREF, bool AMASK, bool EARLY>
+template <int FMT, int MODE, int XT, int PREF, bool AMASK, bool EARLY, bool SBI>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, GPS = 4 * GL;
@@ -997,7 +1013,8 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
 
 
   const char* wbase = reinterpret_cast<const char*>(wq) + (size_t)r0 * wrow;
-  const char* sbase = reinterpret_cast<const char*>(sc) + (size_t)r0 * srow;
+  // interleaved (scale, bias) words: twice the bytes of the scales alone at every offset
+  const char* sbase = reinterpret_cast<const char*>(sc) + (size_t)r0 * srow * (SBI ? 2 : 1);
   const char* bbase = reinterpret_cast<const char*>(bi) + (size_t)r0 * srow;
 
   for (int ws0 = kb0; ws0 < kb1; ws0 += A.win_steps) {
@@ -1019,13 +1036,24 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       ls_lane = (uint32_t)rr * srow + (uint32_t)(g * GL) * 2u;
     };
     set_load_tile(lt);
-    auto issue = [&](Unit<FMT>& U) {
+    auto issue = [&](Unit<FMT, SBI>& U) {
       const size_t tw = (size_t)(16 * lt) * wrow + (size_t)(ws0 + ls) * (GPS * 16);
       const size_t ts = (size_t)(16 * lt) * srow + (size_t)(ws0 + ls) * (GPS * 2);
       const char* wp = wbase + tw + lw_lane;
 #pragma unroll
       for (int h = 0; h < GL; ++h) U.w[h] = *reinterpret_cast<const u32x4*>(wp + 16 * h);
-      if constexpr (GL == 2) {
+      if constexpr (SBI) {
+        const char* mp = sbase + 2 * (ts + ls_lane);
+        if constexpr (GL == 4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(mp);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) U.s[j] = v[j];
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(mp);
+          U.s[0] = v.x;
+          U.s[1] = v.y;
+        }
+      } else if constexpr (GL == 2) {
         U.s[0] = *reinterpret_cast<const uint32_t*>(sbase + ts + ls_lane);
         if constexpr (F::AFFINE) U.b[0] = *reinterpret_cast<const uint32_t*>(bbase + ts + ls_lane);
       } else {
@@ -1052,7 +1080,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     // the barrier after it; without, after the staging.
     XStage xs;
     stage_load<XT>(A, M, xmap, ws0 * KSTEP, ns * KSTEP, xs);
-    Unit<FMT> ring[PREF];
+    Unit<FMT, SBI> ring[PREF];
     lds_barrier();  // previous window's readers are done with the LDS
     if constexpr (EARLY) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's activations
@@ -1112,7 +1140,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
           const uint32_t a_lane = a_lane0 + (uint32_t)cs * (GPS * F::GS);
           const uint32_t e_lane = e_lane0 + (uint32_t)cs * (GPS * MAXM * 4);
           const uint32_t xp_lane = xp_lane0 + (uint32_t)cs * 64u;   // 4 quads of groups per unit
-          compute_unit<FMT, MODE, BF, AMASK>(ring[d], smem, a_lane, e_lane, xp_lane, mk, mg, yacc, yb, av, abuf);
+          compute_unit<FMT, MODE, BF, AMASK, SBI>(ring[d], smem, a_lane, e_lane, xp_lane, mk, mg, yacc, yb, av, abuf);
           if (++cs == ns || base + d + 1 == nu) {
             const bool sole = ua <= ct * ns && ub >= (ct + 1) * ns;
             flush_tile<FMT, MODE>(smem, L, ct, sole, ws0 == kb0, ua >= ct * ns ? 0 : 1, wid, g, i, yacc, yb);
@@ -1128,7 +1156,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
         // for it.  Otherwise the slot is dead; saying so lets mode H's lane swaps work on
         // its registers in place instead of on copies.
         if (base + d + PREF < nu) issue(ring[d]);
-        else ring[d] = Unit<FMT>{};
+        else ring[d] = Unit<FMT, SBI>{};
       }
     }
     lds_barrier();
@@ -1236,7 +1264,7 @@ __device__ __forceinline__ float gv_dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
-template <int FMT, int XT, int MM, int PREF>
+template <int FMT, int XT, int MM, int PREF, bool SBI>
 __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
   using F = Fmt<FMT>;
   constexpr bool ONE = F::ONE_BIT;
@@ -1291,8 +1319,13 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) R.w[i] = v[i];
     }
-    R.s = *reinterpret_cast<const uint16_t*>(sc + (size_t)row * srow + soff);
-    if constexpr (F::AFFINE) R.b = *reinterpret_cast<const uint16_t*>(bi + (size_t)row * srow + soff);
+    if constexpr (SBI) {   // the group's (scale, bias) word of the interleaved layout
+      R.s = *reinterpret_cast<const uint32_t*>(sc + 2 * ((size_t)row * srow + soff));
+      R.b = 0;
+    } else {
+      R.s = *reinterpret_cast<const uint16_t*>(sc + (size_t)row * srow + soff);
+      if constexpr (F::AFFINE) R.b = *reinterpret_cast<const uint16_t*>(bi + (size_t)row * srow + soff);
+    }
   };
   GUnit ring[PREF];
   // the first units' loads go out right behind the activations', so their latency
@@ -1493,7 +1526,7 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
             }
         }
         const float s_ = half_of(R.s, 0) * SCALE_MUL;
-        const float b_ = F::AFFINE ? half_of(R.b, 0) : 0.0f;
+        const float b_ = F::AFFINE ? (SBI ? half_of(R.s, 1) : half_of(R.b, 0)) : 0.0f;
         float y[MM];
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
@@ -1525,15 +1558,15 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
 }
 
 // The kernel names carry the variant name, so a trace shows which variant ran.
-template <int FMT, int XT, int PREF, bool EARLY>
+template <int FMT, int XT, int PREF, bool EARLY, bool SBI>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_q(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY>(A, smem);
+  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY, SBI>(A, smem);
 }
-template <int FMT, int XT, int PREF, bool AMASK, bool EARLY>
+template <int FMT, int XT, int PREF, bool AMASK, bool EARLY, bool SBI>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY>(A, smem);
+  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY, SBI>(A, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1664,7 +1697,7 @@ static hipError_t allow_lds(void (*kern)(MfmaArgs), std::atomic<uint64_t>& done,
   return e;
 }
 
-template <int FMT, int MODE, int XT, int PREF, bool EARLY>
+template <int FMT, int MODE, int XT, int PREF, bool EARLY, bool SBI>
 static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t stream, const DeviceInfo& dev) {
   // 1-bit codes at 8 rows: the A-operand reads of the lanes without a drafted row are
   // masked off (AMASK).  With the zero row those reads carry 4 * 8 + 4 distinct addresses,
@@ -1672,13 +1705,13 @@ static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t 
   // scalar instructions per read group, which pays at 8 rows only (measured on MI355X).
   constexpr bool MASKABLE = MODE == VAR_MFMA_H && fmt_one_bit(FMT);
   void (*kern)(MfmaArgs) =
-      MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT, PREF, EARLY> : vg_mfma_h<FMT, XT, PREF, false, EARLY>;
+      MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI> : vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI>;
   static std::atomic<uint64_t> attr_done{0};
   static std::atomic<uint64_t> attr_done_mask{0};
   std::atomic<uint64_t>* done = &attr_done;
   if constexpr (MASKABLE) {
     if (A.M == 8) {
-      kern = vg_mfma_h<FMT, XT, PREF, true, EARLY>;
+      kern = vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI>;
       done = &attr_done_mask;
     }
   }
@@ -1688,7 +1721,7 @@ static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t 
   return hipGetLastError();
 }
 
-template <int FMT, int MODE, int XT>
+template <int FMT, int MODE, int XT, bool SBI>
 static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, uint32_t* counters,
                              const DeviceInfo& dev) {
   if (p.win_steps <= 0 || (p.ks > 1 && (part == nullptr || counters == nullptr))) return hipErrorInvalidValue;
@@ -1727,16 +1760,21 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   // the rotated format's longer staging, issue them after it (each order measured faster
   // there on MI355X).
   constexpr bool EARLY = MODE == VAR_MFMA_H && FMT != HAD2;
-  if constexpr (fmt_one_bit(FMT)) return launch_kern<FMT, MODE, XT, 2, EARLY>(A, p, c.stream, dev);
-  else return launch_kern<FMT, MODE, XT, 1, EARLY>(A, p, c.stream, dev);
+  if constexpr (fmt_one_bit(FMT)) return launch_kern<FMT, MODE, XT, 2, EARLY, SBI>(A, p, c.stream, dev);
+  else return launch_kern<FMT, MODE, XT, 1, EARLY, SBI>(A, p, c.stream, dev);
 }
 
 hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float* part, uint32_t* counters,
                        const DeviceInfo& dev) {
+#define VG_DISPATCH_SBI(FMT, MODE, XT)                                                         \
+  if constexpr (FMT != SIGN1) {                                                                \
+    if (c.sbi) return launch_one<FMT, MODE, XT, true>(c, p, part, counters, dev);              \
+  }                                                                                            \
+  return launch_one<FMT, MODE, XT, false>(c, p, part, counters, dev);
 #define VG_DISPATCH_XT(FMT, MODE)                                                   \
   switch (c.xt) {                                                                    \
-    case XF16: return launch_one<FMT, MODE, XF16>(c, p, part, counters, dev);        \
-    case XBF16: return launch_one<FMT, MODE, XBF16>(c, p, part, counters, dev);      \
+    case XF16: { VG_DISPATCH_SBI(FMT, MODE, XF16) }                                  \
+    case XBF16: { VG_DISPATCH_SBI(FMT, MODE, XBF16) }                                \
     default: return hipErrorInvalidValue;                                            \
   }
 #define VG_DISPATCH_MODE(FMT)                                                       \
@@ -1751,6 +1789,7 @@ hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float*
   }
 #undef VG_DISPATCH_MODE
 #undef VG_DISPATCH_XT
+#undef VG_DISPATCH_SBI
 }
 
 // The dot2 kernel: one wave per 1024-wide K-step (K <= 16384), rows one or two (one for the
@@ -1779,9 +1818,9 @@ bool plan_gemv(int fmt, int M, int K, int N, const DeviceInfo& dev, MfmaPlan* p)
 
 // The grid is one round of resident workgroups: the plan's wave count per CU, cut to what
 // the instance's registers allow (a second round would start after the first has drained).
-template <int FMT, int XT, int MM>
+template <int FMT, int XT, int MM, bool SBI>
 static hipError_t launch_gemv_m(const MfmaArgs& A, const MfmaPlan& p, hipStream_t stream, const DeviceInfo& dev) {
-  void (*kern)(MfmaArgs) = vg_gemv<FMT, XT, MM, 3>;
+  void (*kern)(MfmaArgs) = vg_gemv<FMT, XT, MM, 3, SBI>;
   static std::atomic<uint64_t> attr_done{0};
   static std::atomic<int> resident[8][GV_MAXS + 1];   // workgroups per CU by device and S (0: unknown)
   hipError_t e = allow_lds(kern, attr_done, dev);
@@ -1796,10 +1835,14 @@ static hipError_t launch_gemv_m(const MfmaArgs& A, const MfmaPlan& p, hipStream_
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * S, p.lds);
     if (e != hipSuccess) return e;
     // a workgroup's waves do not always spread evenly over the 4 SIMDs: two waves of
-    // headroom per CU keep the whole grid resident at once
+    // headroom per CU keep the whole grid resident at once.  At most 16 waves per CU: at
+    // K = 5120 (5 waves a workgroup) 3 workgroups per CU ran 0.4-0.6 us ahead of 2 and of
+    // 4 (measured on MI355X), and the interleaved-metadata instances, with fewer
+    // registers, would otherwise get 4.
     const int regs = fa.numRegs < 8 ? 8 : ((fa.numRegs + 7) / 8) * 8;
     const int wps = std::min(8, 512 / regs);
-    while (per_cu > 1 && per_cu * S > 4 * wps - 2) --per_cu;
+    const int waves_max = std::min(4 * wps - 2, 16);
+    while (per_cu > 1 && per_cu * S > waves_max) --per_cu;
     per_cu = per_cu < 1 ? 1 : per_cu;
     slot.store(per_cu, std::memory_order_relaxed);
   }
@@ -1815,7 +1858,7 @@ static hipError_t launch_gemv_m(const MfmaArgs& A, const MfmaPlan& p, hipStream_
   return hipGetLastError();
 }
 
-template <int FMT, int XT>
+template <int FMT, int XT, bool SBI>
 static hipError_t launch_gemv_x(const GemmCall& c, const MfmaPlan& p, const DeviceInfo& dev) {
   MfmaArgs A{};
   A.x = c.x; A.w = c.w; A.scales = c.scales; A.biases = c.biases; A.y = c.y;
@@ -1824,18 +1867,23 @@ static hipError_t launch_gemv_x(const GemmCall& c, const MfmaPlan& p, const Devi
   A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
   A.signs = c.signs;
   decode_consts(FMT, XT, A.mask, A.magic);
-  if (c.M == 1) return launch_gemv_m<FMT, XT, 1>(A, p, c.stream, dev);
+  if (c.M == 1) return launch_gemv_m<FMT, XT, 1, SBI>(A, p, c.stream, dev);
   if constexpr (FMT != HAD2) {   // two rotated rows do not fit the kernel's registers
-    if (c.M == 2) return launch_gemv_m<FMT, XT, 2>(A, p, c.stream, dev);
+    if (c.M == 2) return launch_gemv_m<FMT, XT, 2, SBI>(A, p, c.stream, dev);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(const GemmCall& c, const MfmaPlan& p, const DeviceInfo& dev) {
+#define VG_GEMV_SBI(FMT, XT)                                             \
+  if constexpr (FMT != SIGN1) {                                          \
+    if (c.sbi) return launch_gemv_x<FMT, XT, true>(c, p, dev);           \
+  }                                                                      \
+  return launch_gemv_x<FMT, XT, false>(c, p, dev);
 #define VG_GEMV_XT(FMT)                                                  \
   switch (c.xt) {                                                        \
-    case XF16: return launch_gemv_x<FMT, XF16>(c, p, dev);               \
-    case XBF16: return launch_gemv_x<FMT, XBF16>(c, p, dev);             \
+    case XF16: { VG_GEMV_SBI(FMT, XF16) }                                \
+    case XBF16: { VG_GEMV_SBI(FMT, XBF16) }                              \
     default: return hipErrorInvalidValue;                                \
   }
   switch (c.fmt) {
@@ -1846,6 +1894,7 @@ hipError_t launch_gemv(const GemmCall& c, const MfmaPlan& p, const DeviceInfo& d
     default: return hipErrorInvalidValue;
   }
 #undef VG_GEMV_XT
+#undef VG_GEMV_SBI
 }
 
 hipError_t launch_debug_decode(int fmt, int xt, const uint32_t* w, int N, int K, uint8_t* codes, hipStream_t s) {

@@ -26,8 +26,8 @@ struct GemmCall {
   const void* x;
   int M, K, N;
   const uint32_t* w;
-  const uint16_t* scales;
-  const uint16_t* biases;  // null for the 1-bit format
+  const uint16_t* scales;   // [N, K/G] fp16; with sbi, interleaved (scale, bias) pairs [N, K/G, 2]
+  const uint16_t* biases;   // [N, K/G] fp16; null for the sign format and with sbi
   float* y;
   hipStream_t stream;
   int had_block;            // rotated format: 64, 128 or 256
@@ -45,6 +45,9 @@ struct GemmCall {
   int32_t* accepted = nullptr;
   unsigned long long* amax_key = nullptr;
   uint32_t* amax_count = nullptr;
+  // affine formats: scales holds each group's (scale, bias) pair as one word, the low half
+  // the scale (one load per lane instead of one per array)
+  bool sbi = false;
 };
 
 struct DeviceInfo {
@@ -82,6 +85,9 @@ size_t mfma_workspace_bytes(int M, int N, const MfmaPlan& p);
 hipError_t launch_mfma(const GemmCall& c, int variant, const MfmaPlan& p, float* part,
                        uint32_t* counters, const DeviceInfo& dev);
 hipError_t launch_valu(const GemmCall& c, const DeviceInfo& dev);
+// Interleaves count scales and biases into (scale, bias) words: out[i] = s[i] | b[i] << 16.
+hipError_t launch_pack_scale_bias(const uint16_t* s, const uint16_t* b, long long count, uint32_t* out,
+                                  hipStream_t st);
 hipError_t launch_hadamard(const void* x, int xt, int M, int K, int block, const uint32_t* signs, float* out,
                            hipStream_t s);
 // Argmax of each row over the whole chip; with draft/accepted non-null also the greedy

@@ -51,6 +51,13 @@
  *                    w = q*s + b with one fp16 scale and one fp16 bias per 64 weights,
  *                    scales[N, K/64], biases[N, K/64] (MLX grouped affine format: a scale
  *                    and a bias per group; same model card, MLX paragraph).
+ *   - The affine formats (2-bit, rotated 2-bit, 1-bit affine) also take their scales and
+ *     biases interleaved: pass biases = NULL and scales as uint16 [N, K/G, 2], each group's
+ *     (scale, bias) pair side by side, scale first (one 32-bit word per group, the scale in
+ *     its low half), built once from the two arrays by vg_pack_scale_bias.  The values and
+ *     every result are the same bit for bit; the kernels then fetch a lane's scales and
+ *     biases with one load instead of one per array, which is faster (the library's
+ *     preferred layout).  Grouped expert calls take [E, N, K/G, 2].
  *   - x, weights, scales, biases and y must be 16-byte aligned (whole-word vector loads).
  */
 #ifndef VERIFY_GEMM_H
@@ -181,7 +188,7 @@ vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* s
  * way (the argmax rule is order-independent).
  *   format  VG_FMT_SIGN1, VG_FMT_AFFINE2, VG_FMT_HAD2 (block 128, unsigned) or
  *           VG_FMT_AFFINE1; w, scales, biases as in that format's call (biases unused and
- *           may be NULL for VG_FMT_SIGN1).
+ *           may be NULL for VG_FMT_SIGN1; NULL for the interleaved layout otherwise).
  *   y       fp32 [M, N], written as by the plain call.
  *   idx     int32 [M] on the device (4-byte aligned).
  *   draft, accepted  both NULL, or int32 [M] and int32 [1] on the device.
@@ -243,7 +250,8 @@ vg_status verify_accept_greedy(const float* y, int M, int N, const int32_t* draf
  *           the host; the call never reads or writes out of bounds whatever it holds.
  *   w, scales, biases  the E experts' packed weights stacked expert-major: w[E, N, words
  *           per row], scales and biases [E, N, groups per row] (biases unused and may be
- *           NULL for VG_FMT_SIGN1).
+ *           NULL for VG_FMT_SIGN1; NULL with interleaved scales [E, N, groups per row, 2]
+ *           for the affine formats).
  *   y       fp32 [M, topk, N]; the rows of unused slots are not written.
  * Requires 1 <= M <= 8, 1 <= topk <= 8, E >= 1, N >= 1, K a multiple of 1024.  One kernel
  * launch; no workspace.
@@ -251,6 +259,19 @@ vg_status verify_accept_greedy(const float* y, int M, int N, const int32_t* draf
 vg_status verify_gemm_experts(int format, const void* x, int x_dtype, int M, int K, int E, int topk,
                               const int32_t* route, const uint32_t* w, const uint16_t* scales,
                               const uint16_t* biases, int N, float* y, void* stream);
+
+/*
+ * Builds the interleaved scale-and-bias layout described above, once, when the weights are
+ * loaded: out[2i] = scales[i], out[2i + 1] = biases[i] for 0 <= i < count (count = the
+ * number of groups, N * K / G, or E * N * K / G for stacked experts).  The pairs are the
+ * MLX grouped affine format's own scale and bias per group ("Bonsai-27B-mlx-1bit" model
+ * card, MLX paragraph) in another order; nothing is computed.  scales and biases are
+ * uint16 [count], out is uint16 [2 * count], all on the device and 16-byte aligned; out
+ * must not overlap either input.  count 0 enqueues nothing.  VG_ERR_SHAPE for count < 0,
+ * VG_ERR_ARG for a null or overlapping buffer.
+ */
+vg_status vg_pack_scale_bias(const uint16_t* scales, const uint16_t* biases, long long count, uint16_t* out,
+                             void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* vg_last_error(void);

@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
                "vg_force_variant", "vg_variant_count", "vg_debug_unpack_sign1", "vg_debug_unpack_affine2",
                "vg_plan_ksplit", "vg_force_ksplit", "verify_accept_greedy", "verify_gemm_affine1",
                "verify_gemm_had2_signed", "hadamard_rotate_signed", "verify_gemm_experts",
-               "verify_gemm_argmax", "vg_debug_unpack", "vg_release_stream_workspace", "vg_stream_read_config"):
+               "verify_gemm_argmax", "vg_debug_unpack", "vg_release_stream_workspace", "vg_stream_read_config",
+               "vg_pack_scale_bias"):
         assert fn in names, fn
 
 
@@ -70,13 +71,42 @@ def test_bad_dtype():
     assert st == B.VG_ERR_DTYPE and "dtype" in _err()
 
 
-@pytest.mark.parametrize("which", range(5))
+@pytest.mark.parametrize("which", [0, 1, 2, 4])
 def test_null_pointers(which):
     ptrs = [ALIGNED] * 5
     ptrs[which] = None
     x, w, s, b, y = ptrs
     st = B.lib().verify_gemm_affine2(x, B.VG_F16, 2, 256, w, s, b, 8, y, None)
     assert st == B.VG_ERR_ARG and "null" in _err()
+
+
+def test_null_biases_select_the_interleaved_layout():
+    """NULL biases of an affine format mean interleaved (scale, bias) pairs in scales, not an
+    error; misaligned biases are still refused.  (Bad row counts are checked first, so these
+    calls stop before touching a device.)"""
+    L = B.lib()
+    assert L.verify_gemm_affine2(ALIGNED, B.VG_F16, 9, 256, ALIGNED, ALIGNED, None, 8, ALIGNED, None) == B.VG_ERR_SHAPE
+    assert L.verify_gemm_affine2(ALIGNED, B.VG_F16, 2, 256, ALIGNED, ALIGNED, MISALIGNED, 8, ALIGNED,
+                                 None) == B.VG_ERR_ALIGN
+    assert L.verify_gemm_affine1(ALIGNED, B.VG_F16, 2, 256, ALIGNED, ALIGNED, MISALIGNED, 8, ALIGNED,
+                                 None) == B.VG_ERR_ALIGN
+    assert L.verify_gemm_had2(ALIGNED, B.VG_F16, 2, 256, ALIGNED, ALIGNED, MISALIGNED, 8, 128, ALIGNED,
+                              None) == B.VG_ERR_ALIGN
+
+
+def test_pack_scale_bias_validation():
+    L = B.lib()
+    assert L.vg_pack_scale_bias(ALIGNED, ALIGNED * 2, -1, ALIGNED * 4, None) == B.VG_ERR_SHAPE
+    assert L.vg_pack_scale_bias(None, ALIGNED * 2, 8, ALIGNED * 4, None) == B.VG_ERR_ARG
+    assert L.vg_pack_scale_bias(ALIGNED, None, 8, ALIGNED * 4, None) == B.VG_ERR_ARG
+    assert L.vg_pack_scale_bias(ALIGNED, ALIGNED * 2, 8, None, None) == B.VG_ERR_ARG
+    assert L.vg_pack_scale_bias(MISALIGNED, ALIGNED * 2, 8, ALIGNED * 4, None) == B.VG_ERR_ALIGN
+    assert L.vg_pack_scale_bias(ALIGNED, ALIGNED * 2, 8, ALIGNED * 4 + 8, None) == B.VG_ERR_ALIGN
+    # out [2 * count] uint16 overlapping either input (every call here fails validation:
+    # the fake addresses are never dereferenced)
+    assert L.vg_pack_scale_bias(ALIGNED, ALIGNED * 2, 8, ALIGNED - 16, None) == B.VG_ERR_ARG
+    assert "overlap" in _err()
+    assert L.vg_pack_scale_bias(ALIGNED * 4, ALIGNED * 2, 8, ALIGNED * 2 - 16, None) == B.VG_ERR_ARG
 
 
 @pytest.mark.parametrize("which", range(4))
@@ -163,7 +193,9 @@ def test_gemm_argmax_validation():
     assert call(M=0) == B.VG_ERR_SHAPE
     assert call(fmt=0, K=1088) == B.VG_ERR_SHAPE      # 1-bit groups of 128
     assert call(fmt=2, K=1088) == B.VG_ERR_SHAPE      # rotated blocks of 128
-    assert call(b=None) == B.VG_ERR_ARG               # 2-bit affine needs biases
+    assert call(b=A + 4) == B.VG_ERR_ALIGN
+    # null biases select the interleaved pairs: validation goes on to y
+    assert call(b=None, y=None) == B.VG_ERR_ARG and "y is null" in _err()
     assert call(xt=5) == B.VG_ERR_DTYPE
     assert call(y=None) == B.VG_ERR_ARG
 
@@ -199,9 +231,10 @@ def test_experts_validation():
     assert call(route=A + 2) == B.VG_ERR_ALIGN
     assert call(w=None) == B.VG_ERR_ARG
     assert call(s=A + 4) == B.VG_ERR_ALIGN
-    assert call(b=None) == B.VG_ERR_ARG and "biases" in _err()
-    assert call(fmt=B.FMT_HAD2, b=None) == B.VG_ERR_ARG
-    assert call(fmt=B.FMT_AFFINE1, b=None) == B.VG_ERR_ARG
+    assert call(b=A + 4) == B.VG_ERR_ALIGN and "biases" in _err()
+    # null biases select the interleaved pairs [E, N, K/G, 2]: validation goes on to y
+    for fmt in (B.FMT_AFFINE2, B.FMT_HAD2, B.FMT_AFFINE1):
+        assert call(fmt=fmt, b=None, y=None) == B.VG_ERR_ARG and "y is null" in _err()
     assert call(y=A + 8) == B.VG_ERR_ALIGN
     assert call(x=None) == B.VG_ERR_ARG
 
@@ -249,7 +282,16 @@ def test_binding_checks_weight_shapes_against_the_format():
     _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, w, s, b[:40])       # biases of too few rows
     _raises(B.VG_ERR_DTYPE, vgm.verify_gemm_affine2, x, w, s.float(), b)    # scales not fp16
     _raises(B.VG_ERR_DTYPE, vgm.verify_gemm_affine2, x, w.long(), s, b)     # words not int32
-    _raises(B.VG_ERR_ARG, vgm.verify_gemm_affine2, x, w, s, None)           # affine needs biases
+    # biases None: scales must be the interleaved pairs [N, K/G, 2]
+    assert "scales has shape" in _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, w, s, None)
+    sb = torch.zeros((48, 16, 2), dtype=torch.float16)
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, w, sb, b)            # pairs beside biases
+    _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x, w, sb[:, :8], None)  # pairs of the wrong group
+    _raises(B.VG_ERR_DTYPE, vgm.verify_gemm_affine2, x, w, sb.float(), None)
+    assert "GPU" in _raises(B.VG_ERR_ARG, vgm.verify_gemm_affine2, x, w, sb, None)   # valid: device check
+    _raises(B.VG_ERR_SHAPE, vgm.pack_scale_bias, s, b[:, :8])                # shapes differ
+    _raises(B.VG_ERR_DTYPE, vgm.pack_scale_bias, s.float(), b)
+    assert "GPU" in _raises(B.VG_ERR_ARG, vgm.pack_scale_bias, s, b)
     _raises(B.VG_ERR_SHAPE, vgm.verify_gemm_affine2, x[:, :1000], w, s, b)  # K not a group multiple
 
 
