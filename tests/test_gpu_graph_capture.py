@@ -28,15 +28,19 @@ def vg():
     return m
 
 
-@pytest.mark.parametrize("fmt,K,N,x_dtype,M,argmax", [
-    ("affine2", 2048, 3000, "f16", 8, False),    # one K slice, the 8-row variant
-    ("sign1", 17408, 5120, "bf16", 4, False),    # K split across workgroups: arrival counters
-    ("affine2", 2048, 8192, "f16", 6, True),     # the fused argmax: keys and arrival counter
-    ("sign1", 512, 256, "f32", 8, True),         # the VALU kernel, then the argmax kernel
+@pytest.mark.parametrize("fmt,K,N,x_dtype,M,argmax,sbi", [
+    ("affine2", 2048, 3000, "f16", 8, False, False),    # one K slice, the 8-row variant
+    ("sign1", 17408, 5120, "bf16", 4, False, False),    # K split across workgroups: arrival counters
+    ("affine2", 2048, 8192, "f16", 6, True, False),     # the fused argmax: keys and arrival counter
+    ("sign1", 512, 256, "f32", 8, True, False),         # the VALU kernel, then the argmax kernel
+    ("affine2", 2048, 8192, "f16", 6, True, True),      # the same, interleaved scales and biases
+    ("affine2", 5120, 4096, "f16", 1, False, True),     # one row: the dot2 kernel, interleaved
 ])
-def test_graph_replays_match_eager(vg, fmt, K, N, x_dtype, M, argmax):
+def test_graph_replays_match_eager(vg, fmt, K, N, x_dtype, M, argmax, sbi):
     case = draw_case(fmt, K, N, x_dtype, seed=80)
     x, w, s, b = case_tensors(case, M)
+    if sbi:
+        s, b = vg.pack_scale_bias(s, b), None   # packed eagerly, before any capture
     st = torch.cuda.Stream()
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     idx = torch.empty((M,), dtype=torch.int32, device="cuda")
@@ -53,7 +57,7 @@ def test_graph_replays_match_eager(vg, fmt, K, N, x_dtype, M, argmax):
     st.synchronize()
     y0 = y.clone()
     idx0 = idx.clone()
-    print(f"graph case {fmt} K={K} N={N} {x_dtype} M={M} argmax={argmax} "
+    print(f"graph case {fmt} K={K} N={N} {x_dtype} M={M} argmax={argmax} sbi={sbi} "
           f"ksplit={vg.plan_ksplit(fmt, x_dtype, M, N, K)}", flush=True)
 
     g = torch.cuda.CUDAGraph()
