@@ -68,6 +68,7 @@ import argparse
 import csv
 import glob
 import hashlib
+import re
 import json
 import os
 import sys
@@ -89,10 +90,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def kernel_source_digest() -> str:
+    """Hash of the kernel sources' code: comments and whitespace are dropped, so a comment
+    edit does not mark the stored HBM counters as stale; any change to the code does."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)   # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

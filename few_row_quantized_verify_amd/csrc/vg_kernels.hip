@@ -11,16 +11,19 @@
 //     rows are grouped in tiles of 16 (the MFMA N dimension).  A "unit" is one tile times
 //     one K-step of 1024 (8 sign groups or 16 affine groups).  Per unit each lane loads
 //     GL consecutive groups of one row in single wide loads (codes, then the scales and
-//     biases of those groups), so a row's unit is fetched by 4 lanes as 256 contiguous
-//     bytes of codes.  Every wave keeps PREF units in flight in a register ring; PREF is
-//     chosen per shape at launch (deeper only when each wave has many units to stream).
-//   * K is processed in windows.  Per window the workgroup first stages its activations
-//     into LDS, already in the operand layout the unpacked codes need (and rotated, for
-//     the Hadamard format), together with per-(group, row) correction sums; only then are
-//     the window's weight loads issued, since loads leave a CU in order and a burst of
-//     weight loads ahead of the activations would delay every MFMA behind it.  The
-//     window's units are split evenly across the 8 waves in tile-major order; partial
-//     tiles are reduced through LDS in a fixed order, so results are deterministic.
+//     biases of those groups: one load per array, or one load of the interleaved
+//     scale-and-bias pairs), so a row's unit is fetched by 4 lanes as 256 contiguous
+//     bytes of codes.  Every wave keeps PREF units in flight in a register ring (two for
+//     the 1-bit formats, whose units are half as large, one for the 2-bit formats).
+//   * K is processed in windows.  Per window the workgroup first loads its activations,
+//     then stages them into LDS, already in the operand layout the unpacked codes need
+//     (and rotated, for the Hadamard format), together with per-(group, row) correction
+//     sums.  Weight loads never go out ahead of a wave's activation loads: loads leave a
+//     CU in order, and a burst of weight loads ahead of the activations would delay every
+//     MFMA behind it.  The 8-row variant issues each wave's first units as soon as that
+//     wave's activations have landed, the others once the staging is done.  The window's
+//     units are split evenly across the 8 waves in tile-major order; partial tiles are
+//     reduced through LDS in a fixed order, so results are deterministic.
 //   * MFMA rows: the 16 A rows are split into independent row-blocks, each fed only by
 //     one lane-group's K slots.  Mode Q: 4 blocks of 4 rows (M <= 4), each lane-group
 //     decodes its own quantization group.  Mode H: 2 blocks of 8 rows (M <= 8), lane-group
@@ -29,7 +32,7 @@
 //     scale (and bias) is applied once per group in fp32.  The lanes whose A row carries
 //     no drafted row feed zeros: a zero row in LDS, or for 1-bit codes at 8 rows operand
 //     registers cleared once per launch, their reads masked off.
-//   * K split across workgroups (tall K, or the rotated format from M = 4): each slice
+//   * K split across workgroups (tall K, or the rotated format): each slice
 //     parks its partial outputs and the last slice of a row group to arrive adds them in
 //     slice order.
 //   * The output-head epilogue (verify_gemm_argmax, one K slice): every row's argmax over
