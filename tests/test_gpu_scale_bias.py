@@ -191,3 +191,31 @@ def test_pairs_of_another_draw_change_the_output(vg):
     y2 = vg.verify_gemm("affine2", x, w, sb2, None)
     torch.cuda.synchronize()
     assert not torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("fmt,x_dtype", [("affine2", "f16"), ("had2", "bf16"), ("affine1", "f16")])
+def test_long_k_several_windows(vg, fmt, x_dtype):
+    """K = 16384 in one slice (forced), so each workgroup stages its activations in several LDS
+    windows and the pairs' offsets move with the window."""
+    case = draw_case(fmt, 16384, 300, x_dtype, seed=38)
+    try:
+        vg.force_ksplit(1)
+        for M in (2, 8):
+            y_sep, y_sbi = both(vg, case, M, lambda x, w, s, b: vg.verify_gemm(fmt, x, w, s, b))
+            assert np.array_equal(y_sep, y_sbi), M
+            check(case, M, y_sbi, label="sbi-long-k")
+    finally:
+        vg.force_ksplit(0)
+
+
+@pytest.mark.parametrize("fmt,K", [("affine2", 4160), ("had2", 4224), ("affine1", 2176)])
+@pytest.mark.parametrize("x_dtype", ["f32", "f16"])
+def test_valu_windows(vg, fmt, K, x_dtype):
+    """K not a multiple of 1024: the VALU kernel, its activation windows and a narrow last one,
+    reading each group's pair as one word."""
+    case = draw_case(fmt, K, 37, x_dtype, seed=39)
+    for M in (1, 3, 8):
+        assert vg.plan_variant(fmt, x_dtype, M, 37, K) == VALU
+        y_sep, y_sbi = both(vg, case, M, lambda x, w, s, b: vg.verify_gemm(fmt, x, w, s, b))
+        assert np.array_equal(y_sep, y_sbi), M
+        check(case, M, y_sbi, label="sbi-valu-windows")
