@@ -57,6 +57,8 @@ Options:
   --stream-sweep     print the streaming-read sweep at every workload's byte count, then exit
   --no-cpu           skip the CPU oracle baseline leg
   --copy-calibration run only a device-to-device copy of known size (for HBM counters)
+  --host-overhead    run the native harness (vg_host_overhead, built by build()) that times
+                     the C ABI's host cost per call beside a bare kernel launch
   --ingest-counters FETCH WRITE CFETCH CWRITE
                      write profiles/hbm_traffic.json from four rocprofv3 --pmc output
                      directories: FETCH_SIZE and WRITE_SIZE of a `--m 8 --no-cpu` run,
@@ -71,6 +73,7 @@ import hashlib
 import re
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -620,11 +623,21 @@ def main() -> int:
     ap.add_argument("--force-variant", default=None)
     ap.add_argument("--scale-bias", choices=("interleaved", "separate"), default="interleaved",
                     help="layout of the affine formats' scales and biases (same bytes)")
+    ap.add_argument("--host-overhead", action="store_true",
+                    help="run the native harness timing the C ABI's host cost per call, then exit")
     ap.add_argument("--ingest-counters", nargs=4, metavar="DIR", default=None)
     args = ap.parse_args()
     if args.ingest_counters:
         return ingest_counters(*args.ingest_counters, args.workload,
                                int(args.m) if args.m else 8)
+    if args.host_overhead:
+        # a child process of its own (this one has not touched the GPU)
+        exe = os.path.join(ROOT, "few_row_quantized_verify_amd", "vg_host_overhead")
+        if not os.path.exists(exe):
+            print(f"{exe} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`",
+                  file=sys.stderr)
+            return 2
+        return subprocess.run([exe]).returncode
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify GEMM runs on one device here; "
               "run it with --gpus 1.", file=sys.stderr)
