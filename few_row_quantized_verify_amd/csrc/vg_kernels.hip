@@ -1191,11 +1191,17 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   }
   lds_barrier();
 
-  // write y[m, r0 .. r1) from the tile accumulators
+  // write y[m, r0 .. r1) from the tile accumulators; element e is (m, rr) with m = e / nr,
+  // taken by a float reciprocal: (e + 1/2) / nr lies at least 1/(2 nr) from an integer,
+  // beyond the product's rounding (at most 2^-20 for e < 8 nr) while nr < 2^19; the plan
+  // keeps row ranges within 2^18 (an integer division per element measured 0.06 us slower
+  // at 8 rows on MI355X)
   const int nr = r1 - r0;
+  const float inv_nr = 1.0f / (float)nr;
+  auto row_of = [&](int e) { return (int)(((float)e + 0.5f) * inv_nr); };
   if (A.ks == 1) {
     for (int e = tid; e < M * nr; e += NTHREADS) {
-      const int m = e / nr, rr = e - m * nr;
+      const int m = row_of(e), rr = e - m * nr;
       A.y[(size_t)(xmap ? xmap[MAXM + m] : m) * A.N + r0 + rr] = ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)];
     }
     if (A.idx) fused_argmax(A, smem, L, ytile, M, r0, nr, wid, lane);
@@ -1208,7 +1214,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   // whole L2 of the XCD under every other workgroup running there.
   float* part = A.part + (size_t)ksi * M * A.N;
   for (int e = tid; e < M * nr; e += NTHREADS) {
-    const int m = e / nr, rr = e - m * nr;
+    const int m = row_of(e), rr = e - m * nr;
     __hip_atomic_store(part + (size_t)m * A.N + r0 + rr, ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)],
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -1223,7 +1229,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   lds_barrier();
   if (flag[0] == 0u) return;
   for (int e = tid; e < M * nr; e += NTHREADS) {
-    const int m = e / nr, rr = e - m * nr;
+    const int m = row_of(e), rr = e - m * nr;
     const float* src = A.part + (size_t)m * A.N + r0 + rr;
     float sum = 0.0f;
     // up to 8 slices' loads in flight at once (each is a trip past the L2), added in slice
@@ -1627,6 +1633,7 @@ static bool finish_plan(int fmt, int M, int K, int N, int rg, int ks, const Devi
   p->ks = ks;
   p->rg = rg;
   const int rows_max = (N + rg - 1) / rg + 1;
+  if (rows_max > (1 << 18)) return false;   // the output store maps elements to rows by a float reciprocal
   p->tiles_max = (rows_max + 15) / 16 + 1;
   if (p->tiles_max > 32767) return false;   // the split-tile records hold 15-bit tile indices
   // the kernels divide by ks with a multiply-high, exact for n * ks < 2^32 (n <= S * ks)
