@@ -6,9 +6,9 @@ once inside the contraction.  All computation runs in the HIP library; this pack
 only marshals tensors and streams.
 """
 from .binding import (  # noqa: F401
-    DTYPES, FORMATS, VerifyGemmError, debug_unpack, force_ksplit, force_variant,
-    hadamard_rotate, lib, pack_scale_bias, plan_ksplit, plan_variant, release_stream_workspace, stream_read, variant_count,
-    variant_name,
+    DTYPES, FORMATS, VerifyGemmError, debug_unpack, force_barrier_tail, force_ksplit, force_variant,
+    hadamard_rotate, lib, pack_scale_bias, plan_direct, plan_ksplit, plan_variant, release_stream_workspace,
+    stream_read, variant_count, variant_name,
     verify_accept_greedy, verify_argmax_rows, verify_gemm, verify_gemm_argmax, verify_gemm_argmax_noalloc,
     verify_gemm_affine1, verify_gemm_affine2, verify_gemm_experts, verify_gemm_had2, verify_gemm_sign1,
 )

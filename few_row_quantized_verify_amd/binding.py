@@ -54,6 +54,8 @@ _SIGS = {
     "vg_variant_count": (_I, []),
     "vg_plan_ksplit": (_I, [_I, _I, _I, _I, _I]),
     "vg_force_ksplit": (_I, [_I]),
+    "vg_plan_direct": (_I, [_I, _I, _I, _I, _I]),
+    "vg_force_barrier_tail": (_I, [_I]),
     "vg_stream_read_blocks": (_I, []),
     "vg_stream_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
     "vg_stream_read_config": (_I, [_P, ctypes.c_size_t, _P, _I, _I, _P]),
@@ -500,3 +502,15 @@ def plan_ksplit(fmt: str, x_dtype: str, M: int, N: int, K: int) -> int:
 
 def force_ksplit(ks: int) -> None:
     _check(lib().vg_force_ksplit(ks))
+
+
+def plan_direct(fmt: str, x_dtype: str, M: int, N: int, K: int) -> int:
+    """1 when a plain verify call stores each tile from the wave that completes it (no
+    barrier after the main loop), 0 when it finishes the tiles after a barrier, -1 when no
+    call takes the arguments."""
+    return lib().vg_plan_direct(FORMATS[fmt], DTYPES[x_dtype], M, N, K)
+
+
+def force_barrier_tail(on: bool) -> None:
+    """Make later MFMA calls finish every tile after the workgroup barrier (tests)."""
+    _check(lib().vg_force_barrier_tail(1 if on else 0))

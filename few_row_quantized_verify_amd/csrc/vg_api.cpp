@@ -22,6 +22,7 @@ namespace {
 thread_local char g_err[512] = "";
 int g_forced = -1;  // forced variant (-1: dispatch)
 int g_forced_ks = 0;  // forced K slices of the MFMA variants (0: dispatch)
+bool g_barrier_tail = false;  // every MFMA call sums shared tiles after a workgroup barrier
 std::once_flag g_env_once;
 
 vg_status fail(vg_status s, const char* fmt, ...) {
@@ -279,6 +280,7 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   if (mfma) {
     if (!vg::plan_mfma(fmt, var, M, K, N, dev, g_forced_ks, &p))
       return fail(VG_ERR_UNSUPPORTED, "M=%d K=%d does not fit the MFMA staging", M, K);
+    if (g_barrier_tail) p.direct = false;
     if (p.ks > 1 && p.rg > vg::MAX_SPLIT_ROW_GROUPS) return fail(VG_ERR_UNSUPPORTED, "too many row groups");
   } else if (var == vg::VAR_GEMV) {
     if (!vg::plan_gemv(fmt, M, K, N, dev, &p))
@@ -592,6 +594,23 @@ int vg_plan_ksplit(int format, int x_dtype, int M, int N, int K) {
   if (device_info(&dev) != VG_OK) return -1;
   vg::MfmaPlan p;
   return vg::plan_mfma(format, var, M, K, N, dev, g_forced_ks, &p) ? p.ks : -1;
+}
+
+vg_status vg_force_barrier_tail(int on) {
+  if (on != 0 && on != 1) return fail(VG_ERR_ARG, "barrier tail flag %d is not 0 or 1", on);
+  g_barrier_tail = on == 1;
+  return VG_OK;
+}
+
+int vg_plan_direct(int format, int x_dtype, int M, int N, int K) {
+  const int var = vg_plan_variant(format, x_dtype, M, N, K);
+  if (var < 0) return -1;
+  if (var == vg::VAR_VALU || var == vg::VAR_GEMV) return 0;
+  vg::DeviceInfo dev;
+  if (device_info(&dev) != VG_OK) return -1;
+  vg::MfmaPlan p;
+  if (!vg::plan_mfma(format, var, M, K, N, dev, g_forced_ks, &p)) return -1;
+  return p.direct && !g_barrier_tail ? 1 : 0;
 }
 
 int vg_stream_read_blocks(void) {

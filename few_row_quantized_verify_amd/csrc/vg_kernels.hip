@@ -932,7 +932,7 @@ __device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, 
   if (A.accepted) A.accepted[0] = agreed;
 }
 
-template <int FMT, int MODE, int XT, int PREF, bool AMASK, bool EARLY, bool SBI>
+template <int FMT, int MODE, int XT, int PREF, bool AMASK, bool EARLY, bool SBI, bool DIRECT>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, GPS = 4 * GL;
@@ -1013,6 +1013,12 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     }
   }
   if (!NORM && tid < MAXM) reinterpret_cast<float*>(smem + L.row_off)[MAXM + tid] = 1.0f;
+  // One window over the slice's whole K, no K split, no argmax and no grouped job: every tile
+  // goes to y from the wave that completes it, with no barrier after the loop.  A tile that
+  // waves share is summed (in wave order, as below) by the last of them to arrive, counted in
+  // the first word of the tile's accumulator, which such a tile leaves unused.
+  if constexpr (DIRECT)
+    for (int t = tid; t < T; t += NTHREADS) reinterpret_cast<uint32_t*>(ytile)[t * (MAXM * 16)] = 0u;
 
 
   const char* wbase = reinterpret_cast<const char*>(wq) + (size_t)r0 * wrow;
@@ -1035,8 +1041,11 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     uint32_t lw_lane = 0, ls_lane = 0;
     auto set_load_tile = [&](int t) {
       const int rr = min(16 * t + i, r1 - 1 - r0) - 16 * t;   // clamp rows past the range
-      lw_lane = (uint32_t)rr * wrow + (uint32_t)(g * GL) * 16u;
-      ls_lane = (uint32_t)rr * srow + (uint32_t)(g * GL) * 2u;
+      // 24-bit products (rr < 16, row pitches below 2^24): a plain 32-bit multiply-add.  As a
+      // 32-bit product the compiler forms a 64-bit multiply-add whose unused high addend may
+      // be given the register of a load still in flight, and then waits for that load.
+      lw_lane = __umul24((uint32_t)rr, wrow) + (uint32_t)(g * GL) * 16u;
+      ls_lane = __umul24((uint32_t)rr, srow) + (uint32_t)(g * GL) * 2u;
     };
     set_load_tile(lt);
     auto issue = [&](Unit<FMT, SBI>& U) {
@@ -1089,7 +1098,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's activations
 #pragma unroll
       for (int d = 0; d < PREF; ++d)
-        if (d < nu) issue(ring[d]);
+        if (DIRECT || d < nu) issue(ring[d]);
     }
     // The tiles split between waves in this window, for the reduction after it: wave
     // boundary bw (lanes 0..NW-2 of wave 0) records, when it falls strictly inside a tile
@@ -1100,7 +1109,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     // the staging.  (Not the last wave: it carries the extra unit when the units do not
     // divide evenly, and delaying its first load costs the whole call up to a
     // microsecond, measured on MI355X.)
-    if (wid == 0 && lane < NW - 1) {
+    if (!DIRECT && wid == 0 && lane < NW - 1) {
       const int bw = lane + 1;
       const int B = (int)(((uint32_t)UW * bw) / NW);
       const int t = B / ns, t0 = t * ns;
@@ -1125,7 +1134,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     if constexpr (!EARLY) {
 #pragma unroll
       for (int d = 0; d < PREF; ++d)
-        if (d < nu) issue(ring[d]);
+        if (DIRECT || d < nu) issue(ring[d]);
     }
     lds_barrier();
 
@@ -1136,6 +1145,36 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     int ct = nu > 0 ? ua_t : 0, cs = nu > 0 ? ua - ct * ns : 0;
     float yacc[4] = {0.f, 0.f, 0.f, 0.f};
     f32x4 yb = {0.f, 0.f, 0.f, 0.f};
+    // direct: a shared tile's sum over its waves' slots, in wave order (non-waves add +0),
+    // stored to y; element e of a tile is (row e / 16, column e % 16)
+    auto reduce_store = [&](int t) {
+      const float* slots = reinterpret_cast<const float*>(smem + L.slot_off);
+      // the waves whose unit range meets the tile (mask) and which of them began before it
+      // (late: their part sits in slot 1)
+      const int t0 = t * ns;
+      uint32_t mask = 0, late = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const int a2 = (int)(((uint32_t)UW * w2) / NW), b2 = (int)(((uint32_t)UW * (w2 + 1)) / NW);
+        if (a2 < b2 && b2 > t0 && a2 < t0 + ns) {
+          mask |= 1u << w2;
+          if (a2 < t0) late |= 1u << w2;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && M <= 4) break;
+        const int e = lane + 64 * h, m = e >> 4, rr = 16 * t + (e & 15);
+        float v[NW];
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) v[w2] = slots[(w2 * 2 + ((late >> w2) & 1u)) * (MAXM * 16) + e];
+        float sum = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) sum += ((mask >> w2) & 1u) ? v[w2] : 0.0f;
+        if (m < M && rr < r1 - r0) A.y[(size_t)m * A.N + r0 + rr] = sum;
+      }
+    };
+    int red_t = -1;   // direct: a shared tile this wave completed last, summed after the next issue
     for (int base = 0; base < nu; base += PREF) {
 #pragma unroll
       for (int d = 0; d < PREF; ++d) {
@@ -1150,6 +1189,17 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) yacc[r] = 0.f;
             yb = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (DIRECT && !sole) {
+              // count this wave's units of the shared tile in (its slot written first); the
+              // wave that brings the count to the tile's ns units is the last to arrive
+              const uint32_t cnt = (uint32_t)(min(ub, (ct + 1) * ns) - max(ua, ct * ns));
+              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+              uint32_t before = 0;
+              if (lane == 0)
+                before = __hip_atomic_fetch_add(reinterpret_cast<uint32_t*>(ytile) + ct * (MAXM * 16), cnt,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              if (__builtin_amdgcn_readfirstlane(before) + cnt == (uint32_t)ns) red_t = ct;
+            }
             cs = 0;
             ++ct;
           }
@@ -1160,7 +1210,25 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
         // its registers in place instead of on copies.
         if (base + d + PREF < nu) issue(ring[d]);
         else ring[d] = Unit<FMT, SBI>{};
+        if (DIRECT && red_t >= 0) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+          reduce_store(red_t);
+          red_t = -1;
+        }
       }
+    }
+    if constexpr (DIRECT) {
+      // the tiles this wave holds alone, read back from its own accumulator writes
+      for (int t = ua_t; nu > 0 && t * ns < ub; ++t) {
+        if (ua > t * ns || ub < (t + 1) * ns) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1 && M <= 4) break;
+          const int e = lane + 64 * h, m = e >> 4, rr = 16 * t + (e & 15);
+          if (m < M && rr < r1 - r0) A.y[(size_t)m * A.N + r0 + rr] = ytile[t * (MAXM * 16) + e];
+        }
+      }
+      return;
     }
     lds_barrier();
 
@@ -1572,15 +1640,15 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
 }
 
 // The kernel names carry the variant name, so a trace shows which variant ran.
-template <int FMT, int XT, int PREF, bool EARLY, bool SBI>
+template <int FMT, int XT, int PREF, bool EARLY, bool SBI, bool DIRECT>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_q(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY, SBI>(A, smem);
+  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY, SBI, DIRECT>(A, smem);
 }
-template <int FMT, int XT, int PREF, bool AMASK, bool EARLY, bool SBI>
+template <int FMT, int XT, int PREF, bool AMASK, bool EARLY, bool SBI, bool DIRECT>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY, SBI>(A, smem);
+  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY, SBI, DIRECT>(A, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1641,6 +1709,7 @@ static bool finish_plan(int fmt, int M, int K, int N, int rg, int ks, const Devi
   if (rows_max > (1 << 18)) return false;   // the output store maps elements to rows by a float reciprocal
   p->tiles_max = (rows_max + 15) / 16 + 1;
   if (p->tiles_max > 32767) return false;   // the split-tile records hold 15-bit tile indices
+  if (K >= (1 << 26)) return false;   // lane offsets are 24-bit products of a row and a row's bytes
   // the kernels divide by ks with a multiply-high, exact for n * ks < 2^32 (n <= S * ks)
   if ((uint64_t)(K / KSTEP) * (uint64_t)ks * (uint64_t)ks >= (1ull << 31)) return false;
   const int s_wg = (S + ks - 1) / ks;
@@ -1649,6 +1718,8 @@ static bool finish_plan(int fmt, int M, int K, int N, int rg, int ks, const Devi
   // one for the 2-bit formats, long streams included (a second unit in flight measured
   // slower on every 2-bit shape, the 243 MB output head too).
   p->pref = fmt_one_bit(fmt) ? 2 : 1;
+  // the fewest units any wave gets: the smallest workgroup's tiles times the K-steps, over NW
+  p->direct = ks == 1 && p->win_steps >= S && (N / rg + 15) / 16 * S >= NW * p->pref;
   return p->win_steps > 0;
 }
 
@@ -1719,15 +1790,20 @@ static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t 
   // one more LDS pass per read than the 32 of the drafted rows; the masking costs three
   // scalar instructions per read group, which pays at 8 rows only (measured on MI355X).
   constexpr bool MASKABLE = MODE == VAR_MFMA_H && fmt_one_bit(FMT);
+  // The instance whose waves store their tiles without a barrier after the loop (the plan's
+  // direct case, a plain verify); every wave of it carries at least PREF units, so its first
+  // loads are issued unconditionally.
+  const bool direct = p.direct && p.pref == PREF && !A.idx && !A.route;
   void (*kern)(MfmaArgs) =
-      MODE == VAR_MFMA_Q ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI> : vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI>;
-  static std::atomic<uint64_t> attr_done{0};
-  static std::atomic<uint64_t> attr_done_mask{0};
-  std::atomic<uint64_t>* done = &attr_done;
+      MODE == VAR_MFMA_Q ? (direct ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true> : vg_mfma_q<FMT, XT, PREF, EARLY, SBI, false>)
+                         : (direct ? vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, true>
+                                   : vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, false>);
+  static std::atomic<uint64_t> attr_done[2][2];
+  std::atomic<uint64_t>* done = &attr_done[0][direct];
   if constexpr (MASKABLE) {
     if (A.M == 8) {
-      kern = vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI>;
-      done = &attr_done_mask;
+      kern = direct ? vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI, true> : vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI, false>;
+      done = &attr_done[1][direct];
     }
   }
   const hipError_t e = allow_lds(kern, *done, dev);
@@ -1828,6 +1904,7 @@ bool plan_gemv(int fmt, int M, int K, int N, const DeviceInfo& dev, MfmaPlan* p)
   p->tiles_max = 0;
   p->pref = 3;
   p->lds = lds;
+  p->direct = false;
   return true;
 }
 

@@ -64,6 +64,10 @@ struct MfmaPlan {
   int tiles_max;   // 16-row tiles per workgroup, upper bound
   int pref;        // units in flight per wave
   size_t lds;      // dynamic LDS bytes
+  // One window over the whole K, one slice, and at least pref units for every wave of every
+  // workgroup: a plain verify's waves store their tiles with no barrier after the loop (the
+  // fused argmax and grouped jobs keep the barrier and the reduction after it).
+  bool direct;
 };
 
 // Plans an MFMA call; force_ks > 0 imposes that many K slices (capped at K/1024).

@@ -322,6 +322,26 @@ int vg_plan_ksplit(int format, int x_dtype, int M, int N, int K);
 vg_status vg_force_ksplit(int ksplit);
 
 /*
+ * How a plain verify call (vg_plan_variant's MFMA variants, no argmax) finishes its output
+ * tiles: 1 when each 16-row tile goes to y from the wave that completes it, with no
+ * workgroup barrier after the main loop -- a tile that waves share is added up, in wave
+ * order, by the last of them to arrive -- and 0 when the waves meet at a barrier and the
+ * shared tiles are added up after it (the dot2 and VALU kernels, calls that split K or
+ * stage K in more than one window, and workgroups whose waves could get fewer units than
+ * they load ahead).  The sum is the same in both, so the outputs are bit-identical.  -1 for
+ * arguments no call accepts.  The dispatch is the one the calls make (forced variant and K
+ * slices included).
+ */
+int vg_plan_direct(int format, int x_dtype, int M, int N, int K);
+
+/*
+ * Force later MFMA calls in this process to finish every tile after the workgroup barrier
+ * (1), as the calls with an argmax do, or restore the dispatch (0): tests compare the two
+ * finishes bit for bit.  VG_ERR_ARG for other values.
+ */
+vg_status vg_force_barrier_tail(int on);
+
+/*
  * Measurement aid: a plain streaming read of `bytes` (a positive multiple of 16) from the
  * 16-byte aligned device buffer `buf`, every byte read once with 16-byte non-temporal
  * loads.  Not part of the method: timed at the byte count of a verify call, it shows the

@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
                "vg_plan_ksplit", "vg_force_ksplit", "verify_accept_greedy", "verify_gemm_affine1",
                "verify_gemm_had2_signed", "hadamard_rotate_signed", "verify_gemm_experts",
                "verify_gemm_argmax", "vg_debug_unpack", "vg_release_stream_workspace", "vg_stream_read_config",
-               "vg_pack_scale_bias"):
+               "vg_pack_scale_bias", "vg_plan_direct", "vg_force_barrier_tail"):
         assert fn in names, fn
 
 
@@ -165,6 +165,16 @@ def test_force_ksplit_validation():
         vgm.force_ksplit(65)
     vgm.force_ksplit(0)
     assert vgm.plan_ksplit("sign1", "f16", 0, 16, 1024) == -1
+
+
+def test_force_barrier_tail_validation():
+    L = B.lib()
+    assert L.vg_force_barrier_tail(2) == B.VG_ERR_ARG
+    assert L.vg_force_barrier_tail(-1) == B.VG_ERR_ARG
+    vgm.force_barrier_tail(True)
+    vgm.force_barrier_tail(False)
+    assert vgm.plan_direct("sign1", "f16", 0, 16, 1024) == -1   # M = 0: no call takes it
+    assert vgm.plan_direct("affine2", "f16", 1, 16, 100) == -1  # K not a multiple of the group
 
 
 def test_accept_greedy_validation():

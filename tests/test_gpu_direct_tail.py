@@ -1,0 +1,101 @@
+"""GPU: the two ways an MFMA workgroup finishes its output tiles give the same bits.
+
+A plain verify whose K fits one LDS staging window, in one K slice, with at least as many
+units for every wave as it loads ahead, stores each 16-row tile from the wave that completes
+it: a tile that waves share is added up, in wave order, by the last of them to arrive (a
+counter in LDS), and no barrier follows the main loop.  Every other call, and every call
+under vg_force_barrier_tail, meets at a workgroup barrier and adds the shared tiles after
+it.  The two are the same sums in the same order, so the outputs must be bit-identical.
+The shapes make every kind of tile occur: K = 1024 (one K-step, so every unit is a whole
+tile held by one wave), K = 2048 (tiles held by one wave beside shared ones), K = 5120
+(every tile shared by two or three waves), ragged last tiles (N not a multiple of 16), in
+both MFMA row-block modes, every format, both layouts of the affine scales and biases.
+Outputs start as NaN, so an element neither finish writes fails the comparison, and one
+shape per format is also held to the fp64 oracle's bounds.
+"""
+import numpy as np
+import pytest
+
+from synthetic import draw_case
+from synthetic.torch_io import case_tensors
+from tests.test_gpu_parity import check, reference
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+Q, H = 0, 1
+SHAPES = [(1024, 40000), (2048, 40003), (5120, 17411), (3072, 9000)]
+ORACLE_SHAPE = (2048, 40003)
+
+
+@pytest.fixture(scope="module")
+def vg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import few_row_quantized_verify_amd as m
+    m.lib()  # fails loudly if the library is missing
+    m.force_variant(-1)
+    m.force_ksplit(0)
+    m.force_barrier_tail(False)
+    yield m
+    m.force_variant(-1)
+    m.force_ksplit(0)
+    m.force_barrier_tail(False)
+
+
+def run(vg, fmt, x, w, s, b, M, N):
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    vg.verify_gemm(fmt, x, w, s, b, y=y)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("fmt", ["sign1", "affine2", "had2", "affine1"])
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+def test_direct_and_barrier_tails_agree(vg, fmt, x_dtype):
+    direct_runs = {Q: 0, H: 0}
+    try:
+        for K, N in SHAPES:
+            case = draw_case(fmt, K, N, x_dtype, seed=K + N)
+            ref = reference(case, 8) if (K, N) == ORACLE_SHAPE and x_dtype == "f16" else None
+            for v in (Q, H):
+                vg.force_variant(v)
+                for M in range(1, 9):
+                    if vg.plan_variant(fmt, x_dtype, M, N, K) != v:
+                        continue
+                    direct = vg.plan_direct(fmt, x_dtype, M, N, K)
+                    assert direct in (0, 1), (K, N, v, M)
+                    direct_runs[v] += direct
+                    x, w, s, b = case_tensors(case, M)
+                    layouts = [(s, b)] + ([(vg.pack_scale_bias(s, b), None)] if b is not None else [])
+                    for s_, b_ in layouts:
+                        y_dir = run(vg, fmt, x, w, s_, b_, M, N)
+                        vg.force_barrier_tail(True)
+                        try:
+                            assert vg.plan_direct(fmt, x_dtype, M, N, K) == 0
+                            y_bar = run(vg, fmt, x, w, s_, b_, M, N)
+                        finally:
+                            vg.force_barrier_tail(False)
+                        assert not torch.isnan(y_bar).any(), (K, N, v, M)
+                        assert torch.equal(y_dir, y_bar), (fmt, x_dtype, K, N, vg.variant_name(v), M, direct)
+                    if ref is not None:
+                        check(case, M, y_dir.cpu().numpy().astype(np.float64), ref=ref,
+                              label=f"direct[{vg.variant_name(v)}]")
+    finally:
+        vg.force_variant(-1)
+    # the shapes must reach the direct finish in both row-block modes
+    assert direct_runs[Q] > 0 and direct_runs[H] > 0, direct_runs
+
+
+def test_argmax_and_split_k_take_the_barrier(vg):
+    """The plan's own bounds: a K split, or a K longer than one window, never finishes
+    directly (their tiles are summed across slices or windows after the barrier)."""
+    try:
+        vg.force_ksplit(2)
+        assert vg.plan_direct("affine2", "f16", 8, 17408, 5120) == 0
+        vg.force_ksplit(1)
+        assert vg.plan_direct("affine2", "f16", 8, 300, 16384) == 0
+    finally:
+        vg.force_ksplit(0)
+    assert vg.plan_direct("affine2", "f32", 4, 17408, 5120) == 0    # the VALU kernel
+    assert vg.plan_direct("affine2", "f16", 8, 17408, 5120) == 1    # the 2-bit MLP up-projection
