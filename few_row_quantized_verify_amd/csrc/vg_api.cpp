@@ -99,17 +99,23 @@ int kstep_of(int fmt) { (void)fmt; return 1024; }   // K per MFMA-kernel unit, b
 // 5120 x 17408 projections it finishes first (its set-up before the first weight load is
 // shorter), while on the 151936-row output head, where that set-up no longer matters, its
 // stream is slower, as it is for the sign format and the rotated format at every size
-// timed.  A call that also wants the rows' argmax stays on mode Q, whose epilogue fuses
-// the argmax: the dot2 kernel and the argmax kernel after it measured slower there.
-// Shapes the MFMA kernels cannot stage fall back to the VALU kernel.
+// timed.  The exception is the 1-bit affine format where mode Q finishes its tiles without
+// the barrier after its loop (MfmaPlan::direct): mode Q is then ahead by 0.03-0.2 us on the
+// 5120 x 17408 projection, in every one of four alternating repeats on MI355X.  A call
+// that also wants the rows' argmax stays on mode Q, whose epilogue fuses the argmax: the
+// dot2 kernel and the argmax kernel after it measured slower there.  Shapes the MFMA
+// kernels cannot stage fall back to the VALU kernel.
 constexpr double kGemvMaxCodeBytes = 64.0 * 1024 * 1024;
 int plan(int fmt, int xt, int M, int N, int K, const vg::DeviceInfo& dev, bool argmax = false) {
   if (xt == VG_F32) return vg::VAR_VALU;
   if (K % kstep_of(fmt) != 0) return vg::VAR_VALU;
   if (!argmax && M == 1 && (fmt == vg::AFFINE2 || fmt == vg::AFFINE1) &&
       (double)N * K / (fmt == vg::AFFINE2 ? 4.0 : 8.0) <= kGemvMaxCodeBytes) {
+    vg::MfmaPlan q;
+    const bool q_direct = fmt == vg::AFFINE1 && vg::plan_mfma(fmt, vg::VAR_MFMA_Q, M, K, N, dev, g_forced_ks, &q) &&
+                          q.direct;
     vg::MfmaPlan g;
-    if (vg::plan_gemv(fmt, M, K, N, dev, &g)) return vg::VAR_GEMV;
+    if (!q_direct && vg::plan_gemv(fmt, M, K, N, dev, &g)) return vg::VAR_GEMV;
   }
   const int var = M <= 4 ? vg::VAR_MFMA_Q : vg::VAR_MFMA_H;
   vg::MfmaPlan p;

@@ -87,7 +87,7 @@ def test_direct_and_barrier_tails_agree(vg, fmt, x_dtype):
     assert direct_runs[Q] > 0 and direct_runs[H] > 0, direct_runs
 
 
-def test_argmax_and_split_k_take_the_barrier(vg):
+def test_split_k_and_long_k_take_the_barrier(vg):
     """The plan's own bounds: a K split, or a K longer than one window, never finishes
     directly (their tiles are summed across slices or windows after the barrier)."""
     try:
@@ -99,3 +99,25 @@ def test_argmax_and_split_k_take_the_barrier(vg):
         vg.force_ksplit(0)
     assert vg.plan_direct("affine2", "f32", 4, 17408, 5120) == 0    # the VALU kernel
     assert vg.plan_direct("affine2", "f16", 8, 17408, 5120) == 1    # the 2-bit MLP up-projection
+
+
+def test_one_row_affine1_takes_mode_q_when_it_finishes_directly(vg):
+    """The dispatch at one row of the 1-bit affine format: mode Q where its tiles finish
+    without the barrier, the dot2 kernel elsewhere (as for the 2-bit format everywhere)."""
+    Qname, G = "vg_mfma_q", "vg_gemv"
+    for K, N in ((5120, 17408), (2048, 5000), (1024, 333)):
+        direct = vg.plan_direct("affine1", "bf16", 1, N, K)
+        vg.force_variant(Q)
+        try:
+            q_direct = vg.plan_direct("affine1", "bf16", 1, N, K)
+        finally:
+            vg.force_variant(-1)
+        assert vg.variant_name(vg.plan_variant("affine1", "bf16", 1, N, K)) == (Qname if q_direct else G), (K, N)
+        assert direct == q_direct, (K, N)
+        assert vg.variant_name(vg.plan_variant("affine2", "f16", 1, N, K)) == G, (K, N)
+    vg.force_variant(Q)
+    try:
+        assert vg.plan_direct("affine1", "bf16", 1, 17408, 5120) == 1
+        assert vg.plan_direct("affine1", "bf16", 1, 333, 1024) == 0
+    finally:
+        vg.force_variant(-1)
