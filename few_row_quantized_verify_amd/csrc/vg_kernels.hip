@@ -267,12 +267,20 @@ __device__ __forceinline__ void load_x32_f32(const void* x, int K, int m, int k0
 // weight prefetch: loads enter the memory pipeline in order, and staged behind the weight
 // burst they would delay every workgroup's first MFMA by that whole burst.
 constexpr int MAXT = 3;   // activation chunks (32 K of one row) per thread and window
+// Thread tid's chunk in staging round j (MAXT * NTHREADS when it has none).  The chunks go
+// to all NTHREADS threads in turn, or with SIX to the first six waves only (the launch
+// takes SIX for at most NTHREADS chunks, which MAXT rounds of six waves cover).
+template <bool SIX>
+__device__ __forceinline__ int stage_task(int tid, int j) {
+  if constexpr (SIX) return tid < 6 * 64 ? tid + j * (6 * 64) : MAXT * NTHREADS;
+  else return tid + j * NTHREADS;
+}
 struct XStage {
   u32x4 d[MAXT][4];       // raw fp16/bf16 bits of 32 consecutive activations
   int m[MAXT], c[MAXT];   // the chunk's row and its index within the row's window
 };
 
-template <int XT>
+template <int XT, bool SIX>
 // xmap: the x row of each row (grouped expert verify), or null for x rows 0..M-1.
 __device__ __forceinline__ void stage_load(const MfmaArgs& A, int M, const int* xmap, int k0, int WK, XStage& xs) {
   const int nchunks = WK / 32, ntask = M * nchunks;
@@ -282,7 +290,7 @@ __device__ __forceinline__ void stage_load(const MfmaArgs& A, int M, const int* 
   const float inv_steps = 1.0f / (float)(WK / KSTEP);
 #pragma unroll
   for (int j = 0; j < MAXT; ++j) {
-    const int t = threadIdx.x + j * NTHREADS;
+    const int t = stage_task<SIX>((int)threadIdx.x, j);
     const int m = (int)(((float)(t >> 5) + 0.5f) * inv_steps), c = t - m * nchunks;
     xs.m[j] = m;
     xs.c[j] = c;
@@ -317,7 +325,7 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
   return XT == XBF16 ? bf16_to_f32(h) : f16_to_f32(h);
 }
 
-template <int FMT, int XT>
+template <int FMT, int XT, bool SIX>
 __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLayout& L, int k0, int WK,
                               const XStage& xs) {
   using F = Fmt<FMT>;
@@ -336,7 +344,7 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
-      const int t = tid + j * NTHREADS;
+      const int t = stage_task<SIX>(tid, j);
       if (t < ntask) {
         // magnitudes of one 16-bit float type order like their bit patterns with the sign
         // cleared: two per packed integer max
@@ -369,8 +377,8 @@ __device__ void stage_compute(const MfmaArgs& A, int M, char* smem, const LdsLay
 
 #pragma unroll
   for (int j = 0; j < MAXT; ++j) {
-    const int t = tid + j * NTHREADS;
-    if (t >= ntask) continue;   // whole blocks of 8 lanes skip together (32 | ntask, 64 | NTHREADS)
+    const int t = stage_task<SIX>(tid, j);
+    if (t >= ntask) continue;   // whole blocks of 8 lanes skip together (32 | ntask, 64 | 6 * 64)
     const int m = xs.m[j], c = xs.c[j];
     uint32_t hv[32];  // rotated and rescaled fp16 bits, natural K order (rotated format only)
     float scale = 1.0f;
@@ -932,7 +940,7 @@ __device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, 
   if (A.accepted) A.accepted[0] = agreed;
 }
 
-template <int FMT, int MODE, int XT, int PREF, bool AMASK, bool EARLY, bool SBI, bool DIRECT>
+template <int FMT, int MODE, int XT, int PREF, bool AMASK, bool EARLY, bool SBI, bool DIRECT, bool SIX>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, GPS = 4 * GL;
@@ -1091,7 +1099,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
     // own activation data has landed, so their latency overlaps the staging arithmetic and
     // the barrier after it; without, after the staging.
     XStage xs;
-    stage_load<XT>(A, M, xmap, ws0 * KSTEP, ns * KSTEP, xs);
+    stage_load<XT, SIX>(A, M, xmap, ws0 * KSTEP, ns * KSTEP, xs);
     Unit<FMT, SBI> ring[PREF];
     lds_barrier();  // previous window's readers are done with the LDS
     if constexpr (EARLY) {
@@ -1130,7 +1138,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       reinterpret_cast<uint32_t*>(smem + L.red_off)[2 * lane] = rec;
       reinterpret_cast<uint32_t*>(smem + L.red_off)[2 * lane + 1] = who;
     }
-    stage_compute<FMT, XT>(A, M, smem, L, ws0 * KSTEP, ns * KSTEP, xs);
+    stage_compute<FMT, XT, SIX>(A, M, smem, L, ws0 * KSTEP, ns * KSTEP, xs);
     if constexpr (!EARLY) {
 #pragma unroll
       for (int d = 0; d < PREF; ++d)
@@ -1640,15 +1648,15 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
 }
 
 // The kernel names carry the variant name, so a trace shows which variant ran.
-template <int FMT, int XT, int PREF, bool EARLY, bool SBI, bool DIRECT>
+template <int FMT, int XT, int PREF, bool EARLY, bool SBI, bool DIRECT, bool SIX>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_q(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY, SBI, DIRECT>(A, smem);
+  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY, SBI, DIRECT, SIX>(A, smem);
 }
 template <int FMT, int XT, int PREF, bool AMASK, bool EARLY, bool SBI, bool DIRECT>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY, SBI, DIRECT>(A, smem);
+  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY, SBI, DIRECT, false>(A, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1794,16 +1802,26 @@ static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t 
   // direct case, a plain verify); every wave of it carries at least PREF units, so its first
   // loads are issued unconditionally.
   const bool direct = p.direct && p.pref == PREF && !A.idx && !A.route;
+  // Mode Q issues its first weight loads after the staging, and a wave with no staging chunk
+  // sends them out at once.  When one round of a window's chunks would keep seven or eight
+  // waves busy, six waves take them (SIX, some in two rounds), so two waves start the weight
+  // stream while the others stage: 0.4 to 0.6 us faster at three rows of the 5120-wide
+  // shapes on MI355X, where the 480 chunks otherwise occupy all eight waves.  Level or slower
+  // at every other count measured.
+  const int chunks = A.M * (p.win_steps * KSTEP / 32);
+  const bool six = MODE == VAR_MFMA_Q && !A.route && chunks > 6 * 64 && chunks <= NTHREADS;
   void (*kern)(MfmaArgs) =
-      MODE == VAR_MFMA_Q ? (direct ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true> : vg_mfma_q<FMT, XT, PREF, EARLY, SBI, false>)
-                         : (direct ? vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, true>
-                                   : vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, false>);
-  static std::atomic<uint64_t> attr_done[2][2];
-  std::atomic<uint64_t>* done = &attr_done[0][direct];
+      MODE == VAR_MFMA_Q
+          ? (direct ? (six ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true, true> : vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true, false>)
+                    : (six ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI, false, true>
+                           : vg_mfma_q<FMT, XT, PREF, EARLY, SBI, false, false>))
+          : (direct ? vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, true> : vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, false>);
+  static std::atomic<uint64_t> attr_done[2][2][2];
+  std::atomic<uint64_t>* done = &attr_done[0][direct][six];
   if constexpr (MASKABLE) {
     if (A.M == 8) {
       kern = direct ? vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI, true> : vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI, false>;
-      done = &attr_done[1][direct];
+      done = &attr_done[1][direct][0];
     }
   }
   const hipError_t e = allow_lds(kern, *done, dev);
