@@ -121,3 +121,48 @@ def test_one_row_affine1_takes_mode_q_when_it_finishes_directly(vg):
         assert vg.plan_direct("affine1", "bf16", 1, 333, 1024) == 0
     finally:
         vg.force_variant(-1)
+
+
+# Six-wave staging: a mode-Q launch whose staging window holds more than 384 and at most 512
+# chunks (32 K of one row each, M * 32 per 1024-K step) stages on the first six waves only.
+# The cases below reach it with the barrier finish: with the fused argmax (K = 5120 at three
+# rows, 480 chunks; K = 4096 at four rows, 512; N large enough that K stays in one slice,
+# which the fused argmax needs) and with K split over two slices (K = 8192, a 4-step window
+# per slice, 512 chunks at four rows; 384 at three rows, which keeps eight waves).  Every output is held to the oracle's
+# bounds; the argmax to the argmax of the call's own logits and of the oracle's.
+
+@pytest.mark.parametrize("fmt,K,N,x_dtype,M", [("affine2", 5120, 12000, "f16", 3), ("sign1", 5120, 12001, "bf16", 3),
+                                               ("affine1", 4096, 12003, "bf16", 4), ("affine2", 4096, 16384, "f16", 4)])
+def test_six_wave_staging_with_the_fused_argmax(vg, fmt, K, N, x_dtype, M):
+    case = draw_case(fmt, K, N, x_dtype, seed=K + N + M)
+    assert vg.plan_variant(fmt, x_dtype, M, N, K) == Q
+    assert vg.plan_ksplit(fmt, x_dtype, M, N, K) == 1
+    x, w, s, b = case_tensors(case, M)
+    y, idx = vg.verify_gemm_argmax(fmt, x, w, s, b)
+    torch.cuda.synchronize()
+    yn = y.cpu().numpy().astype(np.float64)
+    ref = reference(case, M)
+    check(case, M, yn, ref=ref, label="six-wave+argmax")
+    assert idx.cpu().tolist() == list(np.argmax(y.cpu().numpy(), axis=1))
+    # the oracle's argmax, wherever its top two are apart by more than the verify bar
+    y_ref = ref[0]
+    for m in range(M):
+        top2 = np.sort(y_ref[m])[-2:]
+        if top2[1] - top2[0] > 4e-3 * np.max(np.abs(y_ref[m])):
+            assert int(idx[m]) == int(np.argmax(y_ref[m])), m
+
+
+@pytest.mark.parametrize("fmt,x_dtype", [("affine2", "f16"), ("sign1", "bf16"), ("affine1", "bf16")])
+def test_six_wave_staging_with_k_split(vg, fmt, x_dtype):
+    K, N = 8192, 300
+    case = draw_case(fmt, K, N, x_dtype, seed=91)
+    try:
+        vg.force_ksplit(2)
+        for M in (3, 4):
+            assert vg.plan_variant(fmt, x_dtype, M, N, K) == Q
+            assert vg.plan_ksplit(fmt, x_dtype, M, N, K) == 2
+            x, w, s, b = case_tensors(case, M)
+            y = run(vg, fmt, x, w, s, b, M, N)
+            check(case, M, y.cpu().numpy().astype(np.float64), label=f"six-wave+ksplit M={M}")
+    finally:
+        vg.force_ksplit(0)
