@@ -152,17 +152,14 @@ struct Workspace {
 };
 std::mutex g_ws_mu;
 std::vector<Workspace> g_ws;
-// Counter area (zeroed at allocation, left zero by every call), u32 indices, each counter and
-// key on its own 128-byte line:
+// Counter area (zeroed at allocation, left zero by every call), u32 indices, each counter on
+// its own 128-byte line:
 //   [0, 24576)       split-K arrival counters, row group r at r * 32 (r < 768)
 //   [24576, 24864)   the argmax kernel's nine counters (rows 0..7, finished rows)
-//   [24864, 28960)   the fused argmax's 64-bit keys, 16 slots per row
-//   [28960, 28992)   the fused argmax's arrival counter
+// The fused argmax needs no counter: its per-workgroup keys sit in the partial area.
 constexpr int kArgmaxCounterBase = vg::MAX_SPLIT_ROW_GROUPS * vg::SPLIT_CTR_STRIDE;
-constexpr int kFusedKeyBase = kArgmaxCounterBase + 32 * (VG_MAX_ROWS + 1);   // 8-byte aligned
-constexpr int kFusedCountIndex = kFusedKeyBase + 32 * 16 * VG_MAX_ROWS;
 constexpr size_t kCounterBytes = 116736;
-static_assert((kFusedCountIndex + 32) * 4 <= (int)kCounterBytes, "counter area too small");
+static_assert((kArgmaxCounterBase + 32 * (VG_MAX_ROWS + 1)) * 4 <= (int)kCounterBytes, "counter area too small");
 
 // Whether work enqueued on `stream` now would be captured into a graph.
 bool capturing(hipStream_t stream, bool* cap) {
@@ -300,6 +297,8 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   if (split || idx) {
     size_t part_bytes = split ? vg::mfma_workspace_bytes(M, N, p) : 0;
     if (argmax_after && argmax_key_bytes(M, N) > part_bytes) part_bytes = argmax_key_bytes(M, N);
+    // the fused argmax: FUSED_KEYS 64-bit keys per workgroup
+    if (fused && (size_t)p.grid * vg::FUSED_KEYS * 8 > part_bytes) part_bytes = (size_t)p.grid * vg::FUSED_KEYS * 8;
     if (vg_status s = get_workspace(fixed, dev.id, c.stream, part_bytes, &part, &counters)) return s;
   }
   hipError_t e;
@@ -308,12 +307,15 @@ vg_status run_gemm(int fmt, const void* x, int x_dtype, int M, int K, const uint
   } else if (var == vg::VAR_GEMV) {
     e = vg::launch_gemv(c, p, dev);
   } else if (fused) {
+    // each workgroup stores its rows' largest keys, and one workgroup after the GEMM picks
+    // the winners: stream order makes the keys visible, where a count of arriving
+    // workgroups inside the GEMM would add three dependent trips past the L2 to its end
     c.idx = idx;
     c.draft = draft;
     c.accepted = accepted;
-    c.amax_key = reinterpret_cast<unsigned long long*>(counters + kFusedKeyBase);
-    c.amax_count = counters + kFusedCountIndex;
+    c.amax_key = reinterpret_cast<unsigned long long*>(part);
     e = vg::launch_mfma(c, var, p, nullptr, nullptr, dev);
+    if (e == hipSuccess) e = vg::launch_argmax_keys(c.amax_key, p.grid, M, idx, draft, accepted, c.stream);
   } else {
     e = vg::launch_mfma(c, var, p, split ? part : nullptr, split ? counters : nullptr, dev);
   }

@@ -424,6 +424,53 @@ __global__ __launch_bounds__(ARG_THREADS) void vg_argmax_kernel(const float* y, 
 
 int argmax_chunks(int N) { return (N + ARG_CHUNK - 1) / ARG_CHUNK; }
 
+// The fused argmax's last step, after the GEMM on the same stream (whose end makes its keys
+// visible): wave m folds row m's keys of all G workgroups (a key orders like (value,
+// -column)), with its lanes' loads in flight together, and writes idx[m].  With a draft, the
+// waves' verdicts meet in LDS and wave 0 counts the leading rows that agree.
+__global__ __launch_bounds__(64 * FUSED_KEYS) void vg_argmax_keys_kernel(const unsigned long long* keys, int G,
+                                                                          int M, int32_t* idx, const int32_t* draft,
+                                                                          int32_t* accepted) {
+  __shared__ int agree[FUSED_KEYS];
+  const int m = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (m < M) {
+    const int want = draft != nullptr && lane == 0 ? draft[m] : 0;   // read before the keys land
+    unsigned long long k = 0ull;
+    for (int g0 = 0; g0 < G; g0 += 4 * 64) {
+      unsigned long long v[4];
+      // lanes past the last workgroup read its key again (the maximum does not change), so
+      // the loads need no branch and all four are in flight together
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = keys[(size_t)min(g0 + 64 * j + lane, G - 1) * FUSED_KEYS + m];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) k = v[j] > k ? v[j] : k;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const unsigned long long o = __shfl_xor(k, off);
+      k = o > k ? o : k;
+    }
+    const int id = k == 0ull ? 0 : (int)~(uint32_t)k;
+    if (lane == 0) {
+      idx[m] = id;
+      agree[m] = id == want;
+    }
+  }
+  if (draft == nullptr) return;   // uniform over the workgroup
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  // the accepted prefix: the rows before the first that disagrees
+  const unsigned long long bad = __ballot(lane < M && !agree[lane < M ? lane : 0]);
+  if (lane == 0) accepted[0] = bad == 0ull ? M : __builtin_ctzll(bad);
+}
+
+hipError_t launch_argmax_keys(const unsigned long long* keys, int G, int M, int32_t* idx, const int32_t* draft,
+                              int32_t* accepted, hipStream_t s) {
+  if (M < 1 || M > FUSED_KEYS || G < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(vg_argmax_keys_kernel, dim3(1), dim3(64 * FUSED_KEYS), 0, s, keys, G, M, idx, draft, accepted);
+  return hipGetLastError();
+}
+
 hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
                          unsigned long long* pkey, uint32_t* counters, hipStream_t s) {
   hipLaunchKernelGGL(vg_argmax_kernel, dim3(argmax_chunks(N), M), dim3(ARG_THREADS), 0, s, y, M, N, idx, draft,

@@ -156,10 +156,10 @@ struct MfmaArgs {
   const int32_t* route;
   int topk, E, cap;
   long long w_estride, s_estride;
-  // Fused argmax (plain calls with ks = 1; idx null otherwise): idx [M] gets each row's
-  // argmax over the N columns, and with draft non-null accepted[0] the number of leading
-  // rows whose argmax equals draft[m].  amax_key (row m's slot s at amax_key[16 (16 m + s)],
-  // a 128-byte line each) and amax_count are zero between calls.
+  // Fused argmax (plain calls with ks = 1; idx null otherwise): the workgroup's largest key
+  // of each row goes to amax_key[FUSED_KEYS * blockIdx.x + m] (fused_argmax), and the
+  // launch after the GEMM turns them into idx [M] and, with draft non-null, accepted[0] (the
+  // number of leading rows whose argmax equals draft[m]).  amax_count is unused.
   int32_t* idx;
   const int32_t* draft;
   int32_t* accepted;
@@ -863,85 +863,41 @@ __device__ bool find_job(const MfmaArgs& A, char* smem, int& M, int& expert, int
   return true;
 }
 
-// Fused argmax of the output head (the head's verify is checked by its argmax): wave m
-// takes row m of the workgroup's columns and folds each (value, column) into one 64-bit key
-// that orders like (value, -column): larger value first, then the lower column, and NaN
-// never enters.  The keys meet in one per-row maximum across workgroups; the last
-// workgroup to arrive turns them into indices (0 for a row with no key), counts the
-// accepted prefix when a draft is given, and leaves keys and counter zero for the next
-// call.  The keys and the counter are agent-scope atomics, as in the split-K reduction.
-constexpr int AMAX_STRIDE = 16;   // u64 elements between keys: a 128-byte line each
-constexpr int AMAX_SLOTS = 16;    // key slots per row
+// Fused argmax of the output head (the head's verify is checked by its argmax): each
+// (value, column) of a row becomes one 64-bit key that orders like (value, -column) --
+// larger value first, then the lower column -- and NaN never enters.  A workgroup leaves its
+// largest key of each row in its own slot of amax_key (row m at amax_key[FUSED_KEYS *
+// blockIdx.x + m], zero for a row with no key), with plain stores: no counter and no wait,
+// and a one-workgroup kernel after the GEMM (launch_argmax_keys) picks each row's winner.
 __device__ __forceinline__ unsigned long long arg_key(float v, int n) {
   const uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);   // -0 ties with +0
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);   // orders like v
   return ((unsigned long long)o << 32) | (uint32_t)~(uint32_t)n;
 }
 
-__device__ void fused_argmax(const MfmaArgs& A, char* smem, const LdsLayout& L, const float* ytile, int M, int r0,
-                             int nr, int wid, int lane) {
-  // Workgroup b updates slot b % AMAX_SLOTS of each row's key, so no key line takes more
-  // than 1 / AMAX_SLOTS of the workgroups' maxima (a line's atomics serialize); the last
-  // workgroup to arrive reads every slot.
-  const uint32_t slot = blockIdx.x % AMAX_SLOTS;
-  if (wid < M) {
-    unsigned long long best = 0ull;
-    for (int rr = lane; rr < nr; rr += 64) {
-      const float v = ytile[(rr >> 4) * (MAXM * 16) + wid * 16 + (rr & 15)];
-      if (v == v) {
-        const unsigned long long k = arg_key(v, r0 + rr);
-        best = k > best ? k : best;
-      }
+static_assert(FUSED_KEYS == MAXM, "a workgroup keeps one key slot per row");
+// After the barrier finish: wave m takes row m of the workgroup's columns from ytile.
+__device__ void fused_argmax(const MfmaArgs& A, const float* ytile, int M, int r0, int nr, int wid, int lane) {
+  if (wid >= M) return;
+  unsigned long long best = 0ull;
+  for (int rr = lane; rr < nr; rr += 64) {
+    const float v = ytile[(rr >> 4) * (MAXM * 16) + wid * 16 + (rr & 15)];
+    if (v == v) {
+      const unsigned long long k = arg_key(v, r0 + rr);
+      best = k > best ? k : best;
     }
+  }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const unsigned long long o = __shfl_xor(best, off);
-      best = o > best ? o : best;
-    }
-    if (lane == 0 && best != 0ull)
-      __hip_atomic_fetch_max(A.amax_key + (wid * AMAX_SLOTS + slot) * AMAX_STRIDE, best, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(best, off);
+    best = o > best ? o : best;
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's key has landed
-  lds_barrier();
-  uint32_t* flag = reinterpret_cast<uint32_t*>(smem + L.flag_off);
-  if (threadIdx.x == 0)
-    flag[0] = __hip_atomic_fetch_add(A.amax_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              gridDim.x - 1u ? 1u : 0u;
-  lds_barrier();
-  if (flag[0] == 0u) return;
-  // the last workgroup: row m's winner over the slots (lane s of wave m reads slot s), then
-  // the keys and the counter cleared for the next call
-  if (wid < M) {
-    unsigned long long k = 0ull;
-    if (lane < AMAX_SLOTS) {
-      unsigned long long* kp = A.amax_key + (wid * AMAX_SLOTS + lane) * AMAX_STRIDE;
-      k = __hip_atomic_load(kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(kp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-#pragma unroll
-    for (int off = AMAX_SLOTS / 2; off >= 1; off >>= 1) {
-      const unsigned long long o = __shfl_xor(k, off);
-      k = o > k ? o : k;
-    }
-    if (lane == 0) reinterpret_cast<int*>(smem + L.slot_off)[wid] = k == 0ull ? 0 : (int)~(uint32_t)k;
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(A.amax_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  lds_barrier();
-  if (threadIdx.x != 0) return;
-  const int* ids = reinterpret_cast<const int*>(smem + L.slot_off);   // the split-tile slots are free now
-  int agreed = 0;
-  bool agree = A.draft != nullptr;
-  for (int m = 0; m < M; ++m) {
-    A.idx[m] = ids[m];
-    if (agree && ids[m] == A.draft[m]) ++agreed;
-    else agree = false;
-  }
-  if (A.accepted) A.accepted[0] = agreed;
+  if (lane == 0) A.amax_key[(size_t)blockIdx.x * FUSED_KEYS + wid] = best;
 }
 
-template <int FMT, int MODE, int XT, int PREF, bool AMASK, bool EARLY, bool SBI, bool DIRECT, bool SIX>
+template <int FMT, int MODE, int XT, int PREF, bool AMASK, bool EARLY, bool SBI, bool DIRECT, bool SIX, bool DARG>
 __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
+  static_assert(DIRECT || !DARG, "the argmax of the direct finish needs the direct finish");
   using F = Fmt<FMT>;
   constexpr int GL = F::GL, GPS = 4 * GL;
   constexpr bool NORM = x_rescaled(FMT, XT);
@@ -1027,6 +983,21 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
   // the first word of the tile's accumulator, which such a tile leaves unused.
   if constexpr (DIRECT)
     for (int t = tid; t < T; t += NTHREADS) reinterpret_cast<uint32_t*>(ytile)[t * (MAXM * 16)] = 0u;
+  // direct argmax: each row's largest key over the tiles stored so far (the split-tile
+  // records' area, unused by the direct finish), and the waves done (the flag word)
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(smem + L.red_off);
+  uint32_t* waves_done = reinterpret_cast<uint32_t*>(smem + L.flag_off);
+  if constexpr (DARG) {
+    if (tid < MAXM) keys[tid] = 0ull;
+    if (tid == 0) waves_done[0] = 0u;
+  }
+  // direct argmax: the key of element v of row m at column col (none when ok is false) joins
+  // the row's LDS maximum, each lane on its own: an LDS atomic whose result no one waits
+  // for.  A cross-lane maximum first would chain several LDS permutes per tile, and a
+  // running maximum per lane in registers measured no faster.
+  auto note_key = [&](float v, bool ok, int m, int col) {
+    if (ok && v == v) __hip_atomic_fetch_max(keys + m, arg_key(v, col), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
 
 
   const char* wbase = reinterpret_cast<const char*>(wq) + (size_t)r0 * wrow;
@@ -1179,7 +1150,9 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
         float sum = 0.0f;
 #pragma unroll
         for (int w2 = 0; w2 < NW; ++w2) sum += ((mask >> w2) & 1u) ? v[w2] : 0.0f;
-        if (m < M && rr < r1 - r0) A.y[(size_t)m * A.N + r0 + rr] = sum;
+        const bool ok = m < M && rr < r1 - r0;
+        if (ok) A.y[(size_t)m * A.N + r0 + rr] = sum;
+        if constexpr (DARG) note_key(sum, ok, m, r0 + rr);
       }
     };
     int red_t = -1;   // direct: a shared tile this wave completed last, summed after the next issue
@@ -1233,7 +1206,21 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
         for (int h = 0; h < 2; ++h) {
           if (h == 1 && M <= 4) break;
           const int e = lane + 64 * h, m = e >> 4, rr = 16 * t + (e & 15);
-          if (m < M && rr < r1 - r0) A.y[(size_t)m * A.N + r0 + rr] = ytile[t * (MAXM * 16) + e];
+          const bool ok = m < M && rr < r1 - r0;
+          const float v = ytile[t * (MAXM * 16) + e];
+          if (ok) A.y[(size_t)m * A.N + r0 + rr] = v;
+          if constexpr (DARG) note_key(v, ok, m, r0 + rr);
+        }
+      }
+      if constexpr (DARG) {
+        // the last of the workgroup's waves to finish stores the rows' keys
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        uint32_t before = 0;
+        if (lane == 0)
+          before = __hip_atomic_fetch_add(waves_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(before) == (uint32_t)(NW - 1)) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+          if (lane < M) A.amax_key[(size_t)blockIdx.x * FUSED_KEYS + lane] = keys[lane];
         }
       }
       return;
@@ -1285,7 +1272,7 @@ __device__ __forceinline__ void mfma_body(const MfmaArgs& A, char* smem) {
       const int m = row_of(e), rr = e - m * nr;
       A.y[(size_t)(xmap ? xmap[MAXM + m] : m) * A.N + r0 + rr] = ytile[(rr >> 4) * (MAXM * 16) + m * 16 + (rr & 15)];
     }
-    if (A.idx) fused_argmax(A, smem, L, ytile, M, r0, nr, wid, lane);
+    if (A.idx) fused_argmax(A, ytile, M, r0, nr, wid, lane);
     return;
   }
   // K split across workgroups: park this slice's partial, and let the last slice of the row
@@ -1648,15 +1635,15 @@ __global__ __launch_bounds__(GV_MAXS * 64) void vg_gemv(MfmaArgs A) {
 }
 
 // The kernel names carry the variant name, so a trace shows which variant ran.
-template <int FMT, int XT, int PREF, bool EARLY, bool SBI, bool DIRECT, bool SIX>
+template <int FMT, int XT, int PREF, bool EARLY, bool SBI, bool DIRECT, bool SIX, bool DARG>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_q(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY, SBI, DIRECT, SIX>(A, smem);
+  mfma_body<FMT, VAR_MFMA_Q, XT, PREF, false, EARLY, SBI, DIRECT, SIX, DARG>(A, smem);
 }
-template <int FMT, int XT, int PREF, bool AMASK, bool EARLY, bool SBI, bool DIRECT>
+template <int FMT, int XT, int PREF, bool AMASK, bool EARLY, bool SBI, bool DIRECT, bool DARG>
 __global__ __launch_bounds__(NTHREADS) void vg_mfma_h(MfmaArgs A) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY, SBI, DIRECT, false>(A, smem);
+  mfma_body<FMT, VAR_MFMA_H, XT, PREF, AMASK, EARLY, SBI, DIRECT, false, DARG>(A, smem);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1799,9 +1786,11 @@ static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t 
   // scalar instructions per read group, which pays at 8 rows only (measured on MI355X).
   constexpr bool MASKABLE = MODE == VAR_MFMA_H && fmt_one_bit(FMT);
   // The instance whose waves store their tiles without a barrier after the loop (the plan's
-  // direct case, a plain verify); every wave of it carries at least PREF units, so its first
-  // loads are issued unconditionally.
-  const bool direct = p.direct && p.pref == PREF && !A.idx && !A.route;
+  // direct case); every wave of it carries at least PREF units, so its first loads are issued
+  // unconditionally.  With the argmax its waves also fold the keys of the tiles they store
+  // (DARG).
+  const bool direct = p.direct && p.pref == PREF && !A.route;
+  const bool darg = direct && A.idx != nullptr;
   // Mode Q issues its first weight loads after the staging, and a wave with no staging chunk
   // sends them out at once.  When one round of a window's chunks would keep seven or eight
   // waves busy, six waves take them (SIX, some in two rounds), so two waves start the weight
@@ -1810,20 +1799,30 @@ static hipError_t launch_kern(const MfmaArgs& A, const MfmaPlan& p, hipStream_t 
   // at every other count measured.
   const int chunks = A.M * (p.win_steps * KSTEP / 32);
   const bool six = MODE == VAR_MFMA_Q && !A.route && chunks > 6 * 64 && chunks <= NTHREADS;
-  void (*kern)(MfmaArgs) =
-      MODE == VAR_MFMA_Q
-          ? (direct ? (six ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true, true> : vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true, false>)
-                    : (six ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI, false, true>
-                           : vg_mfma_q<FMT, XT, PREF, EARLY, SBI, false, false>))
-          : (direct ? vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, true> : vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, false>);
-  static std::atomic<uint64_t> attr_done[2][2][2];
-  std::atomic<uint64_t>* done = &attr_done[0][direct][six];
-  if constexpr (MASKABLE) {
-    if (A.M == 8) {
-      kern = direct ? vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI, true> : vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI, false>;
-      done = &attr_done[1][direct][0];
+  bool amask = false;
+  void (*kern)(MfmaArgs);
+  if constexpr (MODE == VAR_MFMA_Q) {
+    if (!direct)
+      kern = six ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI, false, true, false> : vg_mfma_q<FMT, XT, PREF, EARLY, SBI, false, false, false>;
+    else if (darg)
+      kern = six ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true, true, true> : vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true, false, true>;
+    else
+      kern = six ? vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true, true, false> : vg_mfma_q<FMT, XT, PREF, EARLY, SBI, true, false, false>;
+  } else {
+    kern = !direct ? vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, false, false>
+                   : (darg ? vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, true, true>
+                           : vg_mfma_h<FMT, XT, PREF, false, EARLY, SBI, true, false>);
+    if constexpr (MASKABLE) {
+      if (A.M == 8) {
+        amask = true;
+        kern = !direct ? vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI, false, false>
+                       : (darg ? vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI, true, true>
+                               : vg_mfma_h<FMT, XT, PREF, true, EARLY, SBI, true, false>);
+      }
     }
   }
+  static std::atomic<uint64_t> attr_done[2][2][2][2];
+  std::atomic<uint64_t>* done = &attr_done[amask][direct][six][darg];
   const hipError_t e = allow_lds(kern, *done, dev);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.grid), dim3(NTHREADS), p.lds, stream, A);

@@ -38,8 +38,9 @@ struct GemmCall {
   int topk, E, cap;
   long long w_estride, s_estride;
   // fused argmax of every row (MFMA variants with one K slice): idx [M], and with draft
-  // non-null the accepted prefix length; the per-row keys and the arrival counter sit in
-  // the library's per-stream workspace and are zero between calls
+  // non-null the accepted prefix length; each workgroup's per-row keys go to amax_key
+  // (FUSED_KEYS per workgroup, in the library's workspace), and launch_argmax_keys after the
+  // GEMM picks the winners.  amax_count is unused.
   int32_t* idx = nullptr;
   const int32_t* draft = nullptr;
   int32_t* accepted = nullptr;
@@ -101,6 +102,13 @@ int argmax_chunks(int N);
 hipError_t launch_argmax(const float* y, int M, int N, int32_t* idx, const int32_t* draft, int32_t* accepted,
                          unsigned long long* pkey, uint32_t* counters, hipStream_t s);
 constexpr int ARG_KEY_BYTES = 128;   // workspace bytes per parked key (one line each)
+// The fused argmax's second step: keys holds FUSED_KEYS 64-bit keys per workgroup of the GEMM
+// (row m's at keys[FUSED_KEYS * g + m], zero for a row with no key) for G workgroups; one
+// workgroup picks each row's largest (the lowest column among equal values), writes idx [M]
+// and, with draft non-null, the accepted prefix length.
+constexpr int FUSED_KEYS = 8;
+hipError_t launch_argmax_keys(const unsigned long long* keys, int G, int M, int32_t* idx, const int32_t* draft,
+                              int32_t* accepted, hipStream_t s);
 // Streaming read of `bytes` (a multiple of 16) from buf with loads_in_flight (1, 2, 4, 8 or
 // 16) 16-byte loads per thread and wgs_per_cu (1..32) workgroups of 256 threads per CU; one
 // word per workgroup to sink, which holds stream_read_blocks(dev) words.

@@ -23,7 +23,7 @@
  *     counters enqueued on the stream) and replaced by a larger one when a call needs
  *     more.  A replaced workspace is not freed while the process runs (enqueued work or a
  *     captured graph may still use it); vg_release_stream_workspace frees a stream's
- *     workspaces.  The kernels leave the workspace's counters and keys zero, so calls on
+ *     workspaces.  The kernels leave the workspace's counters zero, so calls on
  *     one stream share it in stream order; calls on different streams use different
  *     workspaces.  There is no limit on the number of streams.
  *   - HIP graph capture: a call whose workspace already exists at the size it needs (one
@@ -181,11 +181,12 @@ vg_status verify_argmax_rows(const float* y, int M, int N, int32_t* idx, void* s
  * computes it, and with draft non-null accepted[0] as verify_accept_greedy computes it (the
  * output head's verify is checked by its argmax: "dflash-mlx-bonsai2" README, "Verify it
  * yourself").  When the dispatch runs the MFMA kernels with K in one slice (the output-head
- * shapes), the argmax is fused into the GEMM's epilogue: each workgroup folds its columns'
- * best (value, column) per row into a per-row 64-bit maximum and the last workgroup to
- * finish writes idx, so the logits are not read back and no second kernel runs.  Otherwise
- * the argmax kernel runs after the GEMM on the same stream.  Results are identical either
- * way (the argmax rule is order-independent).
+ * shapes), the argmax is fused into the GEMM's epilogue: each workgroup stores its
+ * columns' best (value, column) per row as one 64-bit key, and one small kernel after the
+ * GEMM takes the maximum key of every row over the workgroups and writes idx (and
+ * accepted), so the logits are not read back.  Otherwise the argmax kernel runs after the
+ * GEMM on the same stream.  Results are identical either way (the argmax rule is
+ * order-independent).
  *   format  VG_FMT_SIGN1, VG_FMT_AFFINE2, VG_FMT_HAD2 (block 128, unsigned) or
  *           VG_FMT_AFFINE1; w, scales, biases as in that format's call (biases unused and
  *           may be NULL for VG_FMT_SIGN1; NULL for the interleaved layout otherwise).
@@ -210,7 +211,9 @@ vg_status verify_gemm_argmax(int format, const void* x, int x_dtype, int M, int 
  *     per-stream workspace.  A call that needs more -- 116736 bytes of counters plus the
  *     larger of (K slices) * M * N * 4 bytes of partials (vg_plan_ksplit; none when 1) and,
  *     when the argmax runs as its own kernel after the GEMM, 128 * M * ceil(N / 2048)
- *     bytes of keys -- is refused with VG_ERR_UNSUPPORTED before anything is enqueued.
+ *     bytes of keys, or for the fused argmax 64 bytes of keys per GEMM workgroup (one
+ *     workgroup per compute unit at most) -- is refused with VG_ERR_UNSUPPORTED before
+ *     anything is enqueued.
  *   - Nothing is allocated and no memset is enqueued.  The first call on a device that
  *     uses the array looks up its address and enqueues one small kernel that clears its
  *     counters; every call leaves them zero for the next.
@@ -322,22 +325,23 @@ int vg_plan_ksplit(int format, int x_dtype, int M, int N, int K);
 vg_status vg_force_ksplit(int ksplit);
 
 /*
- * How a plain verify call (vg_plan_variant's MFMA variants, no argmax) finishes its output
- * tiles: 1 when each 16-row tile goes to y from the wave that completes it, with no
- * workgroup barrier after the main loop -- a tile that waves share is added up, in wave
- * order, by the last of them to arrive -- and 0 when the waves meet at a barrier and the
- * shared tiles are added up after it (the dot2 and VALU kernels, calls that split K or
- * stage K in more than one window, and workgroups whose waves could get fewer units than
- * they load ahead).  The sum is the same in both, so the outputs are bit-identical.  -1 for
+ * How a verify call on vg_plan_variant's MFMA variants (plain, or with the fused argmax of
+ * verify_gemm_argmax) finishes its output tiles: 1 when each 16-row tile goes to y from the
+ * wave that completes it, with no workgroup barrier after the main loop -- a tile that waves
+ * share is added up, in wave order, by the last of them to arrive, and with the argmax each
+ * wave folds the keys of the tiles it stores and the workgroup's last wave stores them --
+ * and 0 when the waves meet at a barrier and the shared tiles are added up after it (the
+ * dot2 and VALU kernels, calls that split K or stage K in more than one window, and
+ * workgroups whose waves could get fewer units than they load ahead).  The sum is the same in both, so the outputs are bit-identical.  -1 for
  * arguments no call accepts.  The dispatch is the one the calls make (forced variant and K
  * slices included).
  */
 int vg_plan_direct(int format, int x_dtype, int M, int N, int K);
 
 /*
- * Force later MFMA calls in this process to finish every tile after the workgroup barrier
- * (1), as the calls with an argmax do, or restore the dispatch (0): tests compare the two
- * finishes bit for bit.  VG_ERR_ARG for other values.
+ * Force later MFMA calls in this process (plain and argmax calls) to finish every tile after
+ * the workgroup barrier (1), or restore the dispatch (0): tests compare the two finishes bit
+ * for bit.  VG_ERR_ARG for other values.
  */
 vg_status vg_force_barrier_tail(int on);
 

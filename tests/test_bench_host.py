@@ -13,7 +13,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 import bench  # noqa: E402
 
-VERIFY = "void vg::vg_mfma_h<1, 1, 1, false, true, true, true>(vg::MfmaArgs)"
+VERIFY = "void vg::vg_mfma_h<1, 1, 1, false, true, true, true, false>(vg::MfmaArgs)"
 
 
 def test_refuses_more_than_one_gpu():
@@ -97,7 +97,7 @@ def test_ingest_scales_counters_by_the_copy_calibration(tmp_path, monkeypatch):
 
 def test_ingest_refuses_a_run_with_two_verify_kernels(tmp_path, monkeypatch):
     t = str(tmp_path)
-    other = VERIFY.replace("vg_mfma_h<1, 1, 1, false, true, true, true>", "vg_mfma_q<1, 1, 1, false, true, true>")
+    other = VERIFY.replace("vg_mfma_h<1, 1, 1, false, true, true, true, false>", "vg_mfma_q<1, 1, 1, false, true, true, false, false>")
     _counter_file(f"{t}/f", [(VERIFY, "FETCH_SIZE", 1.0), (other, "FETCH_SIZE", 1.0)])
     for d in ("w", "cf", "cw"):
         _counter_file(f"{t}/{d}", [])

@@ -166,3 +166,36 @@ def test_six_wave_staging_with_k_split(vg, fmt, x_dtype):
             check(case, M, y.cpu().numpy().astype(np.float64), label=f"six-wave+ksplit M={M}")
     finally:
         vg.force_ksplit(0)
+
+
+@pytest.mark.parametrize("fmt,K,N,x_dtype", [("affine2", 5120, 12000, "f16"), ("sign1", 5120, 13001, "bf16"),
+                                             ("affine1", 2048, 40003, "bf16"), ("had2", 1024, 40000, "f16")])
+def test_argmax_direct_and_barrier_finishes_agree(vg, fmt, K, N, x_dtype):
+    """The fused argmax on the direct finish (each wave folds the keys of the tiles it stores,
+    the workgroup's last wave publishes them) against the barrier finish: logits, idx and the
+    accepted count bit for bit, with a draft that agrees on a prefix."""
+    case = draw_case(fmt, K, N, x_dtype, seed=K + N + 5)
+    ran = 0
+    for M in range(1, 9):
+        x, w, s, b = case_tensors(case, M)
+        direct = vg.plan_direct(fmt, x_dtype, M, N, K)
+        ran += direct
+        outs = []
+        for bar in (False, True):
+            vg.force_barrier_tail(bar)
+            try:
+                y, idx = vg.verify_gemm_argmax(fmt, x, w, s, b)
+                torch.cuda.synchronize()
+                draft = idx.clone()
+                if M > 1:
+                    draft[M // 2] += 1   # agrees on the first M // 2 rows only
+                _, idx2, acc = vg.verify_gemm_argmax(fmt, x, w, s, b, draft=draft)
+                torch.cuda.synchronize()
+            finally:
+                vg.force_barrier_tail(False)
+            outs.append((y.clone(), idx.clone(), idx2.clone(), int(acc[0])))
+        (y0, i0, j0, a0), (y1, i1, j1, a1) = outs
+        assert torch.equal(y0, y1) and torch.equal(i0, i1) and torch.equal(j0, i0) and a0 == a1, (M, direct)
+        assert a0 == (M if M == 1 else M // 2), (M, a0)
+        assert i0.cpu().tolist() == list(np.argmax(y0.cpu().numpy(), axis=1)), M
+    assert ran > 0   # the shapes reach the direct finish
