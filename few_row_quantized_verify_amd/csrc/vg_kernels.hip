@@ -159,12 +159,13 @@ struct MfmaArgs {
   // Fused argmax (plain calls with ks = 1; idx null otherwise): the workgroup's largest key
   // of each row goes to amax_key[FUSED_KEYS * blockIdx.x + m] (fused_argmax), and the
   // launch after the GEMM turns them into idx [M] and, with draft non-null, accepted[0] (the
-  // number of leading rows whose argmax equals draft[m]).  amax_count is unused.
+  // number of leading rows whose argmax equals draft[m]).  `reserved` is unused: it keeps the
+  // argument block at the size and layout the kernels were timed with.
   int32_t* idx;
   const int32_t* draft;
   int32_t* accepted;
   unsigned long long* amax_key;
-  uint32_t* amax_count;
+  uint32_t* reserved;
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -1833,7 +1834,7 @@ template <int FMT, int MODE, int XT, bool SBI>
 static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, uint32_t* counters,
                              const DeviceInfo& dev) {
   if (p.win_steps <= 0 || (p.ks > 1 && (part == nullptr || counters == nullptr))) return hipErrorInvalidValue;
-  MfmaArgs A;
+  MfmaArgs A{};
   A.x = c.x; A.w = c.w; A.scales = c.scales; A.biases = c.biases; A.y = c.y;
   A.M = c.M; A.K = c.K; A.N = c.N;
   A.win_steps = p.win_steps;
@@ -1858,7 +1859,6 @@ static hipError_t launch_one(const GemmCall& c, const MfmaPlan& p, float* part, 
   A.draft = c.draft;
   A.accepted = c.accepted;
   A.amax_key = c.amax_key;
-  A.amax_count = c.amax_count;
   A.had_stages = c.had_block == 64 ? 1 : (c.had_block == 256 ? 3 : 2);
   A.had_scale = c.had_block == 64 ? 0.125f : (c.had_block == 256 ? 0.0625f : 0.08838834764831845f);
   A.signs = c.signs;

@@ -40,12 +40,11 @@ struct GemmCall {
   // fused argmax of every row (MFMA variants with one K slice): idx [M], and with draft
   // non-null the accepted prefix length; each workgroup's per-row keys go to amax_key
   // (FUSED_KEYS per workgroup, in the library's workspace), and launch_argmax_keys after the
-  // GEMM picks the winners.  amax_count is unused.
+  // GEMM picks the winners.
   int32_t* idx = nullptr;
   const int32_t* draft = nullptr;
   int32_t* accepted = nullptr;
   unsigned long long* amax_key = nullptr;
-  uint32_t* amax_count = nullptr;
   // affine formats: scales holds each group's (scale, bias) pair as one word, the low half
   // the scale (one load per lane instead of one per array)
   bool sbi = false;

@@ -172,7 +172,7 @@ def test_six_wave_staging_with_k_split(vg, fmt, x_dtype):
                                              ("affine1", 2048, 40003, "bf16"), ("had2", 1024, 40000, "f16")])
 def test_argmax_direct_and_barrier_finishes_agree(vg, fmt, K, N, x_dtype):
     """The fused argmax on the direct finish (each wave folds the keys of the tiles it stores,
-    the workgroup's last wave publishes them) against the barrier finish: logits, idx and the
+    the workgroup's last wave stores them) against the barrier finish: logits, idx and the
     accepted count bit for bit, with a draft that agrees on a prefix."""
     case = draw_case(fmt, K, N, x_dtype, seed=K + N + 5)
     ran = 0
