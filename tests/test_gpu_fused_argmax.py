@@ -143,13 +143,41 @@ def test_fused_planted_winner_in_last_workgroup(vg):
 
 
 def test_fused_consecutive_calls_reset_state(vg):
-    """The per-row keys and the arrival counter are left zero for the next call: a large M
-    then a smaller one on other inputs, then the first again, on one stream."""
+    """Each call overwrites the key slots of its own workgroups and rows, and the pick reads
+    only those: a large M, then a smaller one on other inputs (the higher rows' slots keep
+    the earlier call's keys), then a shape with far fewer workgroups (the later workgroups'
+    slots keep theirs), then the first again, on one stream."""
     a = draw_case("affine2", 2048, 6000, "f16", seed=63)
     b = draw_case("affine2", 2048, 6000, "f16", seed=64)
-    for case, M in ((a, 8), (b, 3), (a, 8), (b, 8)):
+    c = draw_case("affine2", 2048, 300, "f16", seed=65)   # 19 tiles: 19 workgroups
+    for case, M in ((a, 8), (b, 3), (c, 8), (a, 8), (b, 8), (c, 2)):
         y, idx = fused(vg, case, M)
-        assert np.array_equal(idx.cpu().numpy(), np.argmax(y.cpu().numpy(), axis=1))
+        assert np.array_equal(idx.cpu().numpy(), np.argmax(y.cpu().numpy(), axis=1)), (case.N, M)
+
+
+@pytest.mark.parametrize("K,N,direct", [(2048, 300, 0), (5120, 12000, 1)])
+def test_fused_nan_rows_give_column_zero(vg, K, N, direct):
+    """A drafted row of NaN activations makes every logit of that row NaN: no workgroup has a
+    key for it and its idx is 0, while the other rows keep their own argmax; the accepted
+    count stops at the first row whose argmax differs from the draft.  Both finishes: the
+    barrier one and the direct one, whose waves fold the keys as they store."""
+    case = draw_case("affine2", K, N, "f16", seed=66)
+    M = 6
+    assert vg.plan_direct("affine2", "f16", M, N, K) == direct
+    x, w, s, b = case_tensors(case, M)
+    x[2] = float("nan")
+    y, idx = vg.verify_gemm_argmax(case.fmt, x, w, s, b)
+    torch.cuda.synchronize()
+    y_np = y.cpu().numpy()
+    assert np.all(np.isnan(y_np[2])) and not np.any(np.isnan(np.delete(y_np, 2, axis=0)))
+    want = np.argmax(np.where(np.isnan(y_np), -np.inf, y_np), axis=1)
+    want[2] = 0
+    assert np.array_equal(idx.cpu().numpy(), want)
+    draft = torch.from_numpy(want.astype(np.int32)).cuda()
+    draft[3] += 1
+    _, idx2, acc = vg.verify_gemm_argmax(case.fmt, x, w, s, b, draft=draft)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), want) and int(acc[0]) == 3
 
 
 def test_one_row_argmax_call_keeps_the_fused_kernel(vg):
